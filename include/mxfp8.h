@@ -1,0 +1,134 @@
+/*
+ * mxfp8.h — C ABI of the MI355X (gfx950) MX block-scaled linear layer
+ *
+ *     y[M, N] = dequant(x_q, s_x)[M, K] . dequant(W_q, s_w)[N, K]^T  (+ bias[N]),  y in bf16
+ *
+ * Operation sources (vLLM API pages):
+ *  - aiter_flydsl page, AiterFlyDSLMxfp8LinearKernel: weights are prepared once at load
+ *    (process_weights_after_loading), then every call quantizes the bf16 activations to MXFP8
+ *    with row-major E8M0 scales [M, K/32] (or takes them pre-quantized with the same layout,
+ *    apply_weights / input_quant_key), runs the block-scaled GEMM, writes bf16 and adds the bias.
+ *    row_major_weight gives the inverse of the load-time weight rearrangement.
+ *  - compressed_tensors_w8a8_mxfp8 page, CompressedTensorsW8A8Mxfp8.create_weights: weight
+ *    [N, K] float8_e4m3fn, weight_scale [N, K/32] uint8 (E8M0), group size 32.
+ *  - mxfp6 page, MxFp6LinearLayerConfig: MXFP6 weights, E2M3 or E3M2, group size 32.
+ *  - Mxfp8LinearKernel page: the two-phase kernel contract (prepare weights once, apply per call).
+ * The quantizer follows the OCP MX v1.0 rule: scale byte = floor(log2(amax)) - emax + 127
+ * clamped to [0, 254] (0 for an all-zero block, 0xFF for a block holding Inf/NaN), elements
+ * x / 2^(byte-127) rounded to nearest-even and saturated at the format maximum (E4M3: 448).
+ *
+ * Conventions for every call
+ *  - All data pointers are DEVICE pointers owned by the caller.  The library never allocates,
+ *    frees or synchronizes; each call validates its arguments, enqueues its kernels on `stream`
+ *    (a hipStream_t; NULL = the null stream) and returns.  Device faults surface at the
+ *    caller's next synchronization, as usual for HIP.
+ *  - Return value: MX_OK (0) or a negative MX_E* code; mxfp8_last_error() then gives a message
+ *    (thread-local, valid until the next call on the same thread).
+ *  - Argument validation runs before any HIP call, so bad arguments are reported without a GPU.
+ *  - Shapes: M >= 0 (M == 0 is a no-op returning MX_OK), K > 0 with K % 32 == 0 (the MX
+ *    block), N > 0 with N % 16 == 0 (the weight tile height).  Otherwise MX_ESHAPE.
+ *  - Alignment: pointers marked [16] must be 16-byte aligned, or MX_EALIGN.
+ *  - Concurrency: calls on different streams may overlap; each call only writes its outputs
+ *    (and its workspace, which must therefore not be shared by overlapping calls).
+ */
+#ifndef MXFP8_H
+#define MXFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element formats.  The numbers are gfx950's MFMA operand format codes. */
+typedef enum { MX_FMT_E4M3 = 0, MX_FMT_E2M3 = 2, MX_FMT_E3M2 = 3 } mx_fmt;
+
+enum {
+    MX_OK = 0,
+    MX_EINVAL = -1,     /* null pointer, bad format code, negative stride              */
+    MX_ESHAPE = -2,     /* K % 32, N % 16, a stride smaller than the row, size limits  */
+    MX_EALIGN = -3,     /* a [16] pointer or stride not 16-byte aligned               */
+    MX_EWORKSPACE = -4, /* workspace smaller than mxfp8_workspace_bytes()             */
+    MX_EARCH = -5,      /* the current device is not gfx950 (CDNA4)                   */
+    MX_EHIP = -6        /* a HIP runtime call failed (message has the HIP error)      */
+};
+
+/* 1 if HIP device `device` is a gfx950 (the only target), 0 if not, MX_EHIP if the device
+ * cannot be queried.  aiter_flydsl page, is_supported: native MX needs CDNA4. */
+int mxfp8_device_supported(int device);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* mxfp8_last_error(void);
+
+/* ---------------------------------------------------------------- quantization */
+
+/* Dynamic MXFP8 activation quantization (aiter_flydsl page, apply_weights: the call that
+ * turns x [M, K] into E4M3 data and row-major [M, K/32] E8M0 scales).
+ *   x_bf16 [16]  bf16 [M, ldx] (row stride ldx elements, ldx >= K, ldx % 8 == 0); read only
+ *   xq     [16]  out: E4M3 codes, row-major [M, K]
+ *   xs           out: E8M0 bytes, row-major [M, K/32]
+ * Bit-exact with the OCP rule above (a block with Inf/NaN: scale 0xFF, codes 0x7F). */
+int mxfp8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
+                       void* xq, void* xs, void* stream);
+
+/* The same MX quantization for weights, in any supported element format, producing the
+ * checkpoint layout that mxfp8_prepack_weight takes (compressed_tensors_w8a8_mxfp8 page,
+ * create_weights; mxfp6 page for E2M3 / E3M2):
+ *   w_bf16 [16]  bf16 [N, ldw] (ldw >= K, ldw % 8 == 0)
+ *   wq     [16]  out: E4M3 [N, K] bytes, or FP6 [N, 3K/4] bytes (four 6-bit codes per three
+ *                bytes, little-endian along K: c0 | c1<<6 | c2<<12 | c3<<18)
+ *   ws           out: E8M0 [N, K/32] */
+int mxfp8_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64_t ldw, int fmt,
+                          void* wq, void* ws, void* stream);
+
+/* ---------------------------------------------------------------- load-time weight prepack */
+
+/* Bytes of the prepacked weight for (N, K, fmt); 0 for invalid arguments. */
+int64_t mxfp8_prepacked_bytes(int64_t N, int64_t K, int fmt);
+
+/* Load-time rearrangement of a quantized weight into this library's MFMA-ready tiled layout,
+ * with its scales interleaved for direct per-lane loads (aiter_flydsl page,
+ * process_weights_after_loading: rearranged once, scales sliced to [:N, :K/32]).
+ *   wq           E4M3 [N, ldw_bytes] or FP6 [N, ldw_bytes] bytes (ldw_bytes >= K or 3K/4)
+ *   ws           E8M0, row stride ld_ws >= K/32; only the top-left [N, K/32] is read
+ *   packed [16]  out: mxfp8_prepacked_bytes(N, K, fmt) bytes, owned by the caller; its layout
+ *                is private to this library (read it back with mxfp8_unpack_weight). */
+int mxfp8_prepack_weight(const void* wq, int64_t ldw_bytes, const void* ws, int64_t ld_ws,
+                         int64_t N, int64_t K, int fmt, void* packed, void* stream);
+
+/* Exact inverse of mxfp8_prepack_weight (cf. aiter_flydsl page, row_major_weight):
+ * writes wq [N, K] (E4M3) or [N, 3K/4] (FP6) and ws [N, K/32], both row-major; packed [16]. */
+int mxfp8_unpack_weight(const void* packed, int64_t N, int64_t K, int fmt,
+                        void* wq, void* ws, void* stream);
+
+/* ---------------------------------------------------------------- the linear layer */
+
+/* Workspace bytes mxfp8_linear needs for (M, N, K, fmt) (0 when none is needed).
+ * The workspace holds the quantized activations between the quantizer and the GEMM. */
+int64_t mxfp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt);
+
+/* y = dequant(quantize(x)) . dequant(W)^T (+ bias), bf16 out (aiter_flydsl page,
+ * AiterFlyDSLMxfp8LinearKernel.apply_weights, bf16-input branch).
+ *   x_bf16    [16]  bf16 [M, K] row-major
+ *   packed    [16]  from mxfp8_prepack_weight with the same N, K, fmt
+ *   bias            bf16 [N] or NULL; added in fp32 before the single bf16 rounding
+ *   y         [16]  out: bf16 [M, N] row-major (round to nearest even)
+ *   workspace [16]  device buffer of ws_bytes >= mxfp8_workspace_bytes(M, N, K, fmt) */
+int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N,
+                 int fmt, const void* bias, void* y, void* workspace, int64_t ws_bytes,
+                 void* stream);
+
+/* The same layer from pre-quantized activations (aiter_flydsl page, apply_weights with a
+ * QuantizedActivation; the scales must be row-major [M, K/32] E8M0 exactly, as its assert
+ * requires):
+ *   xq [16] E4M3 [M, K];  xs  E8M0 [M, K/32];  other arguments as mxfp8_linear.
+ * Needs no workspace. */
+int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K,
+                          const void* packed, int64_t N, int fmt, const void* bias, void* y,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXFP8_H */

@@ -1,0 +1,223 @@
+// mx_api.cpp — the C-ABI front of libmxfp8 (declared in include/mxfp8.h).
+//
+// Every entry point validates its arguments first (no HIP call on a bad argument, so the error
+// paths are testable without a GPU), then checks once per device that it is a gfx950, then
+// enqueues its kernels on the caller's stream.  Nothing here allocates or synchronizes.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/mxfp8.h"
+#include "mx_launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = 0;
+  return MX_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool valid_fmt(int f) { return f == MX_FMT_E4M3 || f == MX_FMT_E2M3 || f == MX_FMT_E3M2; }
+
+// 32-bit index arithmetic in the GEMM kernels: keep every dimension and every operand below
+// 2^31 elements.
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+int check_mk(int64_t M, int64_t K) {
+  if (M < 0) return fail(MX_ESHAPE, "M = %lld is negative", (long long)M);
+  if (K <= 0 || K % 32 != 0) return fail(MX_ESHAPE, "K = %lld must be a positive multiple of 32 (the MX block)", (long long)K);
+  if (M > kMaxDim || K > kMaxDim || M * K >= ((int64_t)1 << 31))
+    return fail(MX_ESHAPE, "M x K = %lld x %lld exceeds the supported size", (long long)M, (long long)K);
+  return MX_OK;
+}
+
+int check_nk(int64_t N, int64_t K) {
+  if (N <= 0 || N % 16 != 0) return fail(MX_ESHAPE, "N = %lld must be a positive multiple of 16", (long long)N);
+  if (K <= 0 || K % 32 != 0) return fail(MX_ESHAPE, "K = %lld must be a positive multiple of 32 (the MX block)", (long long)K);
+  if (N > kMaxDim || K > kMaxDim || N * K >= ((int64_t)1 << 31))
+    return fail(MX_ESHAPE, "N x K = %lld x %lld exceeds the supported size", (long long)N, (long long)K);
+  return MX_OK;
+}
+
+// gfx950 check, cached per device (the first query per device is a HIP call).
+std::mutex g_arch_mu;
+int g_arch[64];
+bool g_arch_init = false;
+
+int check_arch() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MX_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  int s = mxfp8_device_supported(dev);
+  if (s < 0) return s;
+  if (s == 0) return fail(MX_EARCH, "device %d is not a gfx950 (CDNA4) GPU", dev);
+  return MX_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MX_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int64_t quant_ws_bytes(int64_t M, int64_t K) {
+  // xq [M, K] then xs [M, K/32], the latter at a 256-byte boundary
+  return ((M * K + 255) / 256) * 256 + M * (K / 32);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mxfp8_device_supported(int device) {
+  if (device < 0) return fail(MX_EINVAL, "device %d", device);
+  std::lock_guard<std::mutex> lk(g_arch_mu);
+  if (!g_arch_init) {
+    for (int& a : g_arch) a = -1;
+    g_arch_init = true;
+  }
+  if (device < 64 && g_arch[device] >= 0) return g_arch[device];
+  hipDeviceProp_t p;
+  hipError_t e = hipGetDeviceProperties(&p, device);
+  if (e != hipSuccess) return fail(MX_EHIP, "hipGetDeviceProperties(%d): %s", device, hipGetErrorString(e));
+  const int yes = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  if (device < 64) g_arch[device] = yes;
+  return yes;
+}
+
+const char* mxfp8_last_error(void) { return g_err; }
+
+int mxfp8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, void* xq, void* xs,
+                       void* stream) {
+  int rc = check_mk(M, K);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  if (!x_bf16 || !xq || !xs) return fail(MX_EINVAL, "null pointer (x, xq or xs)");
+  if (ldx < K) return fail(MX_ESHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldx % 8 != 0 || !aligned16(x_bf16) || !aligned16(xq))
+    return fail(MX_EALIGN, "x, xq must be 16-byte aligned and ldx a multiple of 8");
+  if ((rc = check_arch())) return rc;
+  return hip_status(mx::launch_quantize_act((const uint16_t*)x_bf16, M, K, ldx, (uint8_t*)xq,
+                                            (uint8_t*)xs, (hipStream_t)stream),
+                    "quantize_act launch");
+}
+
+int mxfp8_quantize_weight(const void* w_bf16, int64_t N, int64_t K, int64_t ldw, int fmt, void* wq,
+                          void* ws, void* stream) {
+  if (!valid_fmt(fmt)) return fail(MX_EINVAL, "unknown format %d", fmt);
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (!w_bf16 || !wq || !ws) return fail(MX_EINVAL, "null pointer (w, wq or ws)");
+  if (ldw < K) return fail(MX_ESHAPE, "ldw = %lld < K = %lld", (long long)ldw, (long long)K);
+  if (ldw % 8 != 0 || !aligned16(w_bf16) || !aligned16(wq))
+    return fail(MX_EALIGN, "w, wq must be 16-byte aligned and ldw a multiple of 8");
+  if ((rc = check_arch())) return rc;
+  return hip_status(mx::launch_quantize_weight((const uint16_t*)w_bf16, N, K, ldw, fmt,
+                                               (uint8_t*)wq, (uint8_t*)ws, (hipStream_t)stream),
+                    "quantize_weight launch");
+}
+
+int64_t mxfp8_prepacked_bytes(int64_t N, int64_t K, int fmt) {
+  if (!valid_fmt(fmt) || check_nk(N, K)) return 0;
+  const mx::PackGeom p = mx::pack_geom(N, K, fmt);
+  return p.wbytes + p.sbytes;
+}
+
+int mxfp8_prepack_weight(const void* wq, int64_t ldw_bytes, const void* ws, int64_t ld_ws,
+                         int64_t N, int64_t K, int fmt, void* packed, void* stream) {
+  if (!valid_fmt(fmt)) return fail(MX_EINVAL, "unknown format %d", fmt);
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (!wq || !ws || !packed) return fail(MX_EINVAL, "null pointer (wq, ws or packed)");
+  const int64_t row = fmt == MX_FMT_E4M3 ? K : K / 4 * 3;
+  if (ldw_bytes < row) return fail(MX_ESHAPE, "ldw_bytes = %lld < row bytes %lld", (long long)ldw_bytes, (long long)row);
+  if (ld_ws < K / 32) return fail(MX_ESHAPE, "ld_ws = %lld < K/32 = %lld", (long long)ld_ws, (long long)(K / 32));
+  if (!aligned16(packed)) return fail(MX_EALIGN, "packed must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  return hip_status(mx::launch_prepack((const uint8_t*)wq, ldw_bytes, (const uint8_t*)ws, ld_ws, N,
+                                       K, fmt, (uint8_t*)packed, (hipStream_t)stream),
+                    "prepack launch");
+}
+
+int mxfp8_unpack_weight(const void* packed, int64_t N, int64_t K, int fmt, void* wq, void* ws,
+                        void* stream) {
+  if (!valid_fmt(fmt)) return fail(MX_EINVAL, "unknown format %d", fmt);
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (!wq || !ws || !packed) return fail(MX_EINVAL, "null pointer (packed, wq or ws)");
+  if (!aligned16(packed)) return fail(MX_EALIGN, "packed must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  return hip_status(mx::launch_unpack((const uint8_t*)packed, N, K, fmt, (uint8_t*)wq,
+                                      (uint8_t*)ws, (hipStream_t)stream),
+                    "unpack launch");
+}
+
+int64_t mxfp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
+  if (!valid_fmt(fmt) || check_mk(M, K) || check_nk(N, K)) return 0;
+  if (M == 0) return 0;
+  return quant_ws_bytes(M, K);
+}
+
+static int check_linear_common(int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
+                               const void* y) {
+  if (!valid_fmt(fmt)) return fail(MX_EINVAL, "unknown format %d", fmt);
+  int rc = check_mk(M, K);
+  if (rc) return rc;
+  if ((rc = check_nk(N, K))) return rc;
+  if (M > 0 && (!packed || !y)) return fail(MX_EINVAL, "null pointer (packed or y)");
+  if (M > 0 && (!aligned16(packed) || !aligned16(y)))
+    return fail(MX_EALIGN, "packed, y must be 16-byte aligned");
+  if (M * N >= ((int64_t)1 << 31)) return fail(MX_ESHAPE, "M x N exceeds the supported size");
+  return MX_OK;
+}
+
+int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
+                 const void* bias, void* y, void* workspace, int64_t ws_bytes, void* stream) {
+  int rc = check_linear_common(M, K, packed, N, fmt, y);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  if (!x_bf16) return fail(MX_EINVAL, "null pointer (x)");
+  if (!aligned16(x_bf16)) return fail(MX_EALIGN, "x must be 16-byte aligned");
+  const int64_t need = quant_ws_bytes(M, K);
+  if (!workspace || ws_bytes < need)
+    return fail(MX_EWORKSPACE, "workspace of %lld bytes given, %lld needed", (long long)ws_bytes, (long long)need);
+  if (!aligned16(workspace)) return fail(MX_EALIGN, "workspace must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* xq = (uint8_t*)workspace;
+  uint8_t* xs = xq + ((M * K + 255) / 256) * 256;
+  hipError_t e = mx::launch_quantize_act((const uint16_t*)x_bf16, M, K, K, xq, xs, s);
+  if (e != hipSuccess) return hip_status(e, "quantize_act launch");
+  return hip_status(mx::launch_gemm(xq, xs, M, K, (const uint8_t*)packed, N, fmt,
+                                    (const uint16_t*)bias, (uint16_t*)y, s),
+                    "gemm launch");
+}
+
+int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K, const void* packed,
+                          int64_t N, int fmt, const void* bias, void* y, void* stream) {
+  int rc = check_linear_common(M, K, packed, N, fmt, y);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  if (!xq || !xs) return fail(MX_EINVAL, "null pointer (xq or xs)");
+  if (!aligned16(xq)) return fail(MX_EALIGN, "xq must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  return hip_status(mx::launch_gemm((const uint8_t*)xq, (const uint8_t*)xs, M, K,
+                                    (const uint8_t*)packed, N, fmt, (const uint16_t*)bias,
+                                    (uint16_t*)y, (hipStream_t)stream),
+                    "gemm launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// mx_device.h — device-side building blocks shared by the gfx950 kernels of this library.
+//
+// Hardware facts used here were measured on gfx950 with one-hot probes:
+//  * v_mfma_scale_f32_16x16x128_f8f6f4, FP8 operand: lane l (row r = l % 16, group g = l / 16)
+//    holds 32 bytes; byte t is K index 64 * (t / 16) + 16 * g + t % 16.  FP6 operand: lane l holds
+//    the 32 values of K range [32 g, 32 g + 32) as 6-bit fields packed little-endian in 24 bytes.
+//    The scale of MX block b (K range [32 b, 32 b + 32)) of row r is taken from lane r + 16 b;
+//    the op-select argument picks which byte of that lane's 32-bit scale register is used.
+//    The accumulator of lane l, element i, is C[4 * (l / 16) + i][l % 16].
+//  * v_cvt_scalef32_pk_fp8_bf16 computes RNE(x / scale) into OCP E4M3 but does not saturate:
+//    magnitudes that round above 448 become the NaN code S.1111.111.  Replacing that code by
+//    S.1111.110 gives exactly the saturating conversion (checked over every finite bf16 and
+//    every power-of-two scale).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v2s __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// OCP MX element-format parameters (emax = exponent of the largest normal).
+template <int FMT> struct Fmt;
+template <> struct Fmt<0> { static constexpr int mbits = 3, emin = -6, emax = 8, maxcode = 0x7E, signbit = 7; static constexpr float maxval = 448.f; };
+template <> struct Fmt<2> { static constexpr int mbits = 3, emin = 0, emax = 2, maxcode = 0x1F, signbit = 5; static constexpr float maxval = 7.5f; };
+template <> struct Fmt<3> { static constexpr int mbits = 2, emin = -2, emax = 4, maxcode = 0x1F, signbit = 5; static constexpr float maxval = 28.f; };
+
+// Bytes of one prepacked weight fragment (16 rows x 128 K) per element format.
+__host__ __device__ constexpr int frag_bytes(int fmt) { return fmt == 0 ? 2048 : 1536; }
+
+// E8M0 byte from the largest |bf16| bit pattern of a block (sign bit already cleared):
+// floor(log2(amax)) = E - 127 for a normal amax with exponent field E, so the byte is
+// max(E - emax, 0); zero and bf16-subnormal amax give 0 (scale 2^-127); Inf/NaN give 0xFF.
+template <int FMT>
+__device__ __forceinline__ uint32_t scale_byte_from_amax(uint32_t amax_bits) {
+  if (amax_bits >= 0x7F80u) return 0xFFu;
+  int e = (int)(amax_bits >> 7) - Fmt<FMT>::emax;
+  return (uint32_t)(e > 0 ? e : 0);
+}
+
+// 2^(byte - 127) as an fp32 bit pattern (byte 0 is the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_float(uint32_t byte) {
+  return __uint_as_float(byte ? (byte << 23) : 0x00400000u);
+}
+
+// Four E4M3 codes (bytes of the result) from four bf16 values packed in two dwords, divided
+// by `scale` (a power of two), round-to-nearest-even, saturated at +-448.
+__device__ __forceinline__ uint32_t cvt4_e4m3(uint32_t bf_lo, uint32_t bf_hi, float scale) {
+  v2bf a, b;
+  __builtin_memcpy(&a, &bf_lo, 4);
+  __builtin_memcpy(&b, &bf_hi, 4);
+  v2s r = {0, 0};
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, a, scale, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, b, scale, true);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  // bytes equal to 0x7F / 0xFF (overflow) -> 0x7E / 0xFE: add one to the low 7 bits, the
+  // carry into bit 7 appears only for 0x7F; subtract it back as a 1 in that byte.
+  uint32_t t = ((u & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+  return u - (t >> 7);
+}
+
+// Exact element encode of an fp32 value (already divided by the block scale) for any format,
+// nearest-even with saturation, sign kept.  Used by the load-time weight quantizer.
+template <int FMT>
+__device__ __forceinline__ uint32_t encode_elem(float v) {
+  using F = Fmt<FMT>;
+  const uint32_t s = __float_as_uint(v) >> 31;
+  const float a = __builtin_fabsf(v);
+  uint32_t mag;
+  if (!(a < F::maxval)) {
+    mag = F::maxcode;
+  } else {
+    int e = (int)(__float_as_uint(a) >> 23) - 127;      // floor(log2 a) for normal a
+    if (e < F::emin) e = F::emin;                        // subnormal range of the format
+    const float q = __builtin_rintf(__builtin_ldexpf(a, F::mbits - e));   // exact scaling
+    mag = (uint32_t)((e - F::emin) << F::mbits) + (uint32_t)q;
+  }
+  return (s << F::signbit) | mag;
+}
+
+__device__ __forceinline__ float bf16_to_float(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (hardware conversion).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  __bf16 a = (__bf16)lo, b = (__bf16)hi;
+  uint16_t ua, ub;
+  __builtin_memcpy(&ua, &a, 2);
+  __builtin_memcpy(&ub, &b, 2);
+  return (uint32_t)ua | ((uint32_t)ub << 16);
+}
+
+template <int AFMT, int BFMT>
+__device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AFMT, BFMT, 0, sa, 0, sb);
+}
+
+}  // namespace mx

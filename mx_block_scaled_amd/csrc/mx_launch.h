@@ -1,0 +1,32 @@
+// mx_launch.h — internal host-side launchers (implemented next to their kernels).
+// Arguments are validated by the C-ABI front (mx_api.cpp) before any of these is called;
+// each returns the hipError_t of its launch.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mx {
+
+// Size of the prepacked weight: fragments of 16 rows x 128 K (K zero-padded to a multiple of
+// 128), ordered [K step][row group]; then the scales, one 32-bit word per lane per group of
+// four K steps, ordered [K step / 4][row group][lane].
+struct PackGeom {
+  int64_t N, K, NG, KT, KT4, frag, wbytes, sbytes;
+};
+PackGeom pack_geom(int64_t N, int64_t K, int fmt);
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
+                               uint8_t* xs, hipStream_t s);
+hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int fmt,
+                                  uint8_t* wq, uint8_t* ws, hipStream_t s);
+hipError_t launch_prepack(const uint8_t* wq, int64_t ldw, const uint8_t* ws, int64_t ld_ws,
+                          int64_t N, int64_t K, int fmt, uint8_t* packed, hipStream_t s);
+hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int fmt, uint8_t* wq,
+                         uint8_t* ws, hipStream_t s);
+
+// GEMM from quantized activations xq [M, K] + xs [M, K/32] (row-major).
+hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
+                       const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
+                       uint16_t* y, hipStream_t s);
+
+}  // namespace mx

@@ -1,0 +1,140 @@
+// mx_quant.hip — MX quantizers for gfx950.
+//
+// Activations (hot path): bf16 [M, K] -> E4M3 [M, K] + E8M0 [M, K/32], both row-major, as the
+// aiter_flydsl page's apply_weights produces them before the GEMM.  HBM-bound: each thread
+// reads 16 bytes (8 bf16) and writes 8 code bytes, so a wavefront moves 1 KiB in and 512 B out
+// in single coalesced instructions; the 32-element block maximum is a 4-lane DPP reduction
+// inside a quad, and the conversion is the hardware scaled E4M3 convert with the overflow code
+// mapped to the saturated one.
+//
+// Weights (load time): any element format, one thread per 32-element block, exact float
+// arithmetic per element (speed is irrelevant there; exactness is checked against the oracle).
+#include "mx_device.h"
+#include "mx_launch.h"
+
+namespace mx {
+
+// max over the 4 lanes of a quad (lanes 4j..4j+3), unsigned.
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  // quad_perm [1,0,3,2] then [2,3,0,1]
+  uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+  return v > t ? v : t;
+}
+
+// One thread per 8 consecutive elements of a row; 4 consecutive threads form one MX block.
+// groups = M * K / 8; the quad of a block never straddles two rows because K % 32 == 0.
+__global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict__ x, int64_t K,
+                                                      int64_t ldx, int64_t groups,
+                                                      uint8_t* __restrict__ xq,
+                                                      uint8_t* __restrict__ xs) {
+  const int64_t kg = K >> 3;  // groups of 8 per row
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // every lane of a wave runs the same number of iterations (groups is a multiple of 4 and
+  // the quad reduction only needs the 4 lanes of a block to be active together)
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t - (threadIdx.x & 63) < groups;
+       t += stride) {
+    const bool live = t < groups;
+    const int64_t row = live ? t / kg : 0;
+    const int64_t c8 = live ? t - row * kg : 0;
+    v4i v = {0, 0, 0, 0};
+    if (live) v = *(const v4i*)(x + row * ldx + c8 * 8);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = (uint32_t)v[i] & 0x7FFF7FFFu;
+      const uint32_t lo = u & 0xFFFFu, hi = u >> 16;
+      m = m > lo ? m : lo;
+      m = m > hi ? m : hi;
+    }
+    m = quad_max_u32(m);
+    const uint32_t byte = scale_byte_from_amax<0>(m);
+    uint32_t q0, q1;
+    if (byte == 0xFFu) {
+      q0 = q1 = 0x7F7F7F7Fu;  // block holds Inf/NaN: NaN codes
+    } else {
+      const float sc = e8m0_to_float(byte);
+      q0 = cvt4_e4m3((uint32_t)v[0], (uint32_t)v[1], sc);
+      q1 = cvt4_e4m3((uint32_t)v[2], (uint32_t)v[3], sc);
+    }
+    if (live) {
+      v2i o = {(int)q0, (int)q1};
+      *(v2i*)(xq + row * K + c8 * 8) = o;
+      if ((c8 & 3) == 0) xs[row * (K >> 5) + (c8 >> 2)] = (uint8_t)byte;
+    }
+  }
+}
+
+hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
+                               uint8_t* xs, hipStream_t s) {
+  const int64_t groups = M * (K >> 3);
+  int64_t blocks = (groups + 255) / 256;
+  if (blocks > 256 * 16) blocks = 256 * 16;  // grid-stride beyond 16 workgroups per CU
+  hipLaunchKernelGGL(k_quantize_act, dim3((unsigned)blocks), dim3(256), 0, s, x, K, ldx, groups,
+                     xq, xs);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- weights, any format
+
+template <int FMT>
+__global__ __launch_bounds__(256) void k_quantize_weight(const uint16_t* __restrict__ w, int64_t N,
+                                                         int64_t K, int64_t ldw,
+                                                         uint8_t* __restrict__ wq,
+                                                         uint8_t* __restrict__ ws) {
+  const int64_t KB = K >> 5;
+  const int64_t nblk = N * KB;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = b / KB, kb = b - row * KB;
+    const uint16_t* src = w + row * ldw + kb * 32;
+    uint32_t m = 0;
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t u = src[j] & 0x7FFFu;
+      m = m > u ? m : u;
+    }
+    const uint32_t byte = scale_byte_from_amax<FMT>(m);
+    ws[row * KB + kb] = (uint8_t)byte;
+    uint32_t codes[32];
+    for (int j = 0; j < 32; ++j) {
+      if (byte == 0xFFu) {
+        codes[j] = FMT == 0 ? 0x7Fu : 0u;
+      } else {
+        // x / 2^(byte - 127), exact for every result that can round to a nonzero code
+        const float v = __builtin_ldexpf(bf16_to_float(src[j]), 127 - (int)byte);
+        codes[j] = encode_elem<FMT>(v);
+      }
+    }
+    if (FMT == 0) {
+      uint8_t* dst = wq + row * K + kb * 32;
+      for (int j = 0; j < 32; ++j) dst[j] = (uint8_t)codes[j];
+    } else {
+      uint8_t* dst = wq + row * (K / 4 * 3) + kb * 24;
+      for (int g = 0; g < 8; ++g) {
+        const uint32_t w24 = codes[4 * g] | codes[4 * g + 1] << 6 | codes[4 * g + 2] << 12 |
+                             codes[4 * g + 3] << 18;
+        dst[3 * g] = (uint8_t)(w24 & 0xFF);
+        dst[3 * g + 1] = (uint8_t)((w24 >> 8) & 0xFF);
+        dst[3 * g + 2] = (uint8_t)(w24 >> 16);
+      }
+    }
+  }
+}
+
+hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int fmt,
+                                  uint8_t* wq, uint8_t* ws, hipStream_t s) {
+  const int64_t nblk = N * (K >> 5);
+  int64_t blocks = (nblk + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  dim3 grid((unsigned)blocks), block(256);
+  switch (fmt) {
+    case 0: hipLaunchKernelGGL(k_quantize_weight<0>, grid, block, 0, s, w, N, K, ldw, wq, ws); break;
+    case 2: hipLaunchKernelGGL(k_quantize_weight<2>, grid, block, 0, s, w, N, K, ldw, wq, ws); break;
+    case 3: hipLaunchKernelGGL(k_quantize_weight<3>, grid, block, 0, s, w, N, K, ldw, wq, ws); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mx

@@ -1,0 +1,230 @@
+"""Python binding of libmxfp8 (the C ABI in include/mxfp8.h): argument marshalling only.
+
+Every step of the layer runs in the HIP library; PyTorch only provides device memory and the
+current stream.  If the library is not built this module raises; there is no fallback.
+
+Two-phase use (Mxfp8LinearKernel page: weights processed once after loading, then applied per
+call; aiter_flydsl page for the shapes and layouts):
+
+    packed = prepack_weight(wq, ws, fmt)          # once, at load
+    y = linear(x, packed, N, fmt, bias)           # per call, x bf16 [..., K] -> y bf16 [..., N]
+    y = linear_prequant(xq, xs, packed, N, fmt)   # pre-quantized activations, xs [M, K/32]
+"""
+import ctypes
+import os
+
+import torch  # loaded first: libmxfp8 then binds to the HIP runtime torch already loaded
+
+__all__ = [
+    "FMT", "MXError", "lib", "library_path", "device_supported", "quantize_act",
+    "quantize_weight", "prepack_weight", "unpack_weight", "prepacked_bytes", "workspace_bytes",
+    "linear", "linear_prequant", "MxLinear",
+]
+
+FMT = {"e4m3": 0, "e2m3": 2, "e3m2": 3}
+_ERR = {0: "MX_OK", -1: "MX_EINVAL", -2: "MX_ESHAPE", -3: "MX_EALIGN", -4: "MX_EWORKSPACE",
+        -5: "MX_EARCH", -6: "MX_EHIP"}
+
+library_path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp8.so")
+_lib = None
+
+
+class MXError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (%d): %s" % (_ERR.get(code, "?"), code, msg))
+        self.code = code
+
+
+def lib():
+    """The loaded library; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError("libmxfp8.so is not built (%s); run __graft_entry__.build()"
+                               % library_path)
+        L = ctypes.CDLL(library_path)
+        P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        sig = {
+            "mxfp8_device_supported": (I, [I]),
+            "mxfp8_last_error": (ctypes.c_char_p, []),
+            "mxfp8_quantize_act": (I, [P, I64, I64, I64, P, P, P]),
+            "mxfp8_quantize_weight": (I, [P, I64, I64, I64, I, P, P, P]),
+            "mxfp8_prepacked_bytes": (I64, [I64, I64, I]),
+            "mxfp8_prepack_weight": (I, [P, I64, P, I64, I64, I64, I, P, P]),
+            "mxfp8_unpack_weight": (I, [P, I64, I64, I, P, P, P]),
+            "mxfp8_workspace_bytes": (I64, [I64, I64, I64, I]),
+            "mxfp8_linear": (I, [P, I64, I64, P, I64, I, P, P, P, I64, P]),
+            "mxfp8_linear_prequant": (I, [P, P, I64, I64, P, I64, I, P, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != 0:
+        raise MXError(rc, lib().mxfp8_last_error().decode())
+
+
+def _fmt(fmt):
+    return FMT[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _u8(t, name):
+    if t.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e8m0fnu):
+        raise TypeError("%s must be uint8 / float8 bytes, got %s" % (name, t.dtype))
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous CUDA tensor" % name)
+    return t.view(torch.uint8)
+
+
+def _bf16(t, name):
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be bfloat16, got %s" % (name, t.dtype))
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous CUDA tensor" % name)
+    return t
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def device_supported(device=0):
+    return lib().mxfp8_device_supported(int(device)) == 1
+
+
+def prepacked_bytes(N, K, fmt="e4m3"):
+    return int(lib().mxfp8_prepacked_bytes(N, K, _fmt(fmt)))
+
+
+def workspace_bytes(M, N, K, fmt="e4m3"):
+    return int(lib().mxfp8_workspace_bytes(M, N, K, _fmt(fmt)))
+
+
+def quantize_act(x):
+    """bf16 x [..., K] -> (xq uint8 [M, K] E4M3, xs uint8 [M, K/32] E8M0), M = prod(lead)."""
+    x = _bf16(x, "x")
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K)
+    M = x2.shape[0]
+    xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    xs = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().mxfp8_quantize_act(x2.data_ptr(), M, K, K, xq.data_ptr(), xs.data_ptr(),
+                                    _stream(x)))
+    return xq, xs
+
+
+def quantize_weight(w, fmt="e4m3"):
+    """bf16 W [N, K] -> (wq [N, K] E4M3 or [N, 3K/4] packed FP6, ws [N, K/32] E8M0)."""
+    w = _bf16(w, "w")
+    N, K = w.shape
+    f = _fmt(fmt)
+    wq = torch.empty((N, K if f == 0 else K // 4 * 3), dtype=torch.uint8, device=w.device)
+    ws = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+    _check(lib().mxfp8_quantize_weight(w.data_ptr(), N, K, K, f, wq.data_ptr(), ws.data_ptr(),
+                                       _stream(w)))
+    return wq, ws
+
+
+def prepack_weight(wq, ws, fmt="e4m3", K=None):
+    """Quantized weight (wq [N, row bytes], ws [>=N, >=K/32]) -> prepacked uint8 buffer."""
+    f = _fmt(fmt)
+    wq = _u8(wq, "wq")
+    if ws.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not ws.is_cuda:
+        raise TypeError("ws must be uint8 / float8_e8m0fnu on the GPU")
+    ws = ws.view(torch.uint8)
+    if ws.stride(-1) != 1:
+        raise ValueError("ws rows must be contiguous")
+    N = wq.shape[0]
+    if K is None:
+        K = wq.shape[1] if f == 0 else wq.shape[1] // 3 * 4
+    out = torch.empty(prepacked_bytes(N, K, f), dtype=torch.uint8, device=wq.device)
+    _check(lib().mxfp8_prepack_weight(wq.data_ptr(), wq.stride(0), ws.data_ptr(), ws.stride(0),
+                                      N, K, f, out.data_ptr(), _stream(wq)))
+    return out
+
+
+def unpack_weight(packed, N, K, fmt="e4m3"):
+    f = _fmt(fmt)
+    packed = _u8(packed, "packed")
+    wq = torch.empty((N, K if f == 0 else K // 4 * 3), dtype=torch.uint8, device=packed.device)
+    ws = torch.empty((N, K // 32), dtype=torch.uint8, device=packed.device)
+    _check(lib().mxfp8_unpack_weight(packed.data_ptr(), N, K, f, wq.data_ptr(), ws.data_ptr(),
+                                     _stream(packed)))
+    return wq, ws
+
+
+_ws_cache = {}
+
+
+def _workspace(device, stream, nbytes):
+    key = (device, stream)
+    t = _ws_cache.get(key)
+    if t is None or t.numel() < nbytes:
+        t = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        _ws_cache[key] = t
+    return t
+
+
+def linear(x, packed, N, fmt="e4m3", bias=None, out=None, workspace=None):
+    """y = MX-quantized x [..., K] times the prepacked weight, (+ bias), bf16 [..., N]."""
+    x = _bf16(x, "x")
+    f = _fmt(fmt)
+    lead, K = x.shape[:-1], x.shape[-1]
+    x2 = x.reshape(-1, K)
+    M = x2.shape[0]
+    packed = _u8(packed, "packed")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    b = 0 if bias is None else _bf16(bias, "bias").data_ptr()
+    st = _stream(x)
+    need = workspace_bytes(M, N, K, f)
+    ws = workspace if workspace is not None else _workspace(x.device, st.value, need)
+    _check(lib().mxfp8_linear(x2.data_ptr(), M, K, packed.data_ptr(), N, f, b, y.data_ptr(),
+                              ws.data_ptr(), ws.numel(), st))
+    return y.reshape(*lead, N)
+
+
+def linear_prequant(xq, xs, packed, N, fmt="e4m3", bias=None, out=None, lead_shape=None):
+    """Same layer from pre-quantized activations: xq [M, K] E4M3, xs [M, K/32] row-major."""
+    xq = _u8(xq, "xq")
+    xs = _u8(xs, "xs")
+    f = _fmt(fmt)
+    M, K = xq.shape
+    if tuple(xs.shape) != (M, K // 32):
+        # the aiter_flydsl page asserts exactly this scale shape before its GEMM
+        raise ValueError("activation scale %s for %s: need (M, K/32) row-major"
+                         % (tuple(xs.shape), tuple(xq.shape)))
+    packed = _u8(packed, "packed")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    b = 0 if bias is None else _bf16(bias, "bias").data_ptr()
+    _check(lib().mxfp8_linear_prequant(xq.data_ptr(), xs.data_ptr(), M, K, packed.data_ptr(),
+                                       N, f, b, y.data_ptr(), _stream(xq)))
+    return y if lead_shape is None else y.reshape(*lead_shape, N)
+
+
+class MxLinear:
+    """A linear layer whose quantized weight is prepacked once (load time) and applied per call.
+
+    ``wq``/``ws`` are the checkpoint tensors (weight [N, K] E4M3 or [N, 3K/4] FP6 bytes,
+    weight_scale [N', K'/32] E8M0 with N' >= N, K' >= K, sliced to [:N, :K/32])."""
+
+    def __init__(self, wq, ws, fmt="e4m3", bias=None, K=None):
+        self.fmt = _fmt(fmt)
+        self.N = wq.shape[0]
+        self.K = K if K is not None else (wq.shape[1] if self.fmt == 0 else wq.shape[1] // 3 * 4)
+        self.packed = prepack_weight(wq, ws, self.fmt, K=self.K)
+        self.bias = bias
+
+    def __call__(self, x):
+        return linear(x, self.packed, self.N, self.fmt, self.bias)
+
+    def apply_quantized(self, xq, xs, lead_shape=None):
+        return linear_prequant(xq, xs, self.packed, self.N, self.fmt, self.bias,
+                               lead_shape=lead_shape)
+
+    def row_major_weight(self):
+        """The weight back in checkpoint layout (exact inverse of the prepack)."""
+        return unpack_weight(self.packed, self.N, self.K, self.fmt)

@@ -76,12 +76,15 @@ def outlier_x(M, K, seed):
     return bf16_bits(x), np.sort(ch), np.sort(blk)
 
 
-def make(name, seed=0, M=None):
-    """Inputs of a named workload: dict(x, w, bias (or None), M, N, K).  ``M`` overrides
-    the row count (for reduced-size parity cases of the same distribution)."""
+def make(name, seed=0, M=None, N=None, with_w=True):
+    """Inputs of a named workload: dict(x, w, bias (or None), M, N, K).  ``M`` / ``N`` override
+    the row counts (reduced-size parity cases drawn from the same distributions: the first
+    rows of the full-size tensors are not reproduced, only their distribution)."""
     cfg = dict(CONFIGS[name])
     if M is not None:
         cfg["M"] = int(M)
+    if N is not None:
+        cfg["N"] = int(N)
     Mr, N, K = cfg["M"], cfg["N"], cfg["K"]
     if cfg["act"] == "normal":
         x = normal_bf16((Mr, K), 1.0, seed, 0)
@@ -89,6 +92,6 @@ def make(name, seed=0, M=None):
         x = laplace_bf16((Mr, K), seed, 0)
     else:
         x = outlier_x(Mr, K, seed)[0]
-    w = normal_bf16((N, K), W_STD, seed, 1)
+    w = normal_bf16((N, K), W_STD, seed, 1) if with_w else None
     bias = normal_bf16((N,), BIAS_STD, seed, 2) if cfg["bias"] else None
     return dict(x=x, w=w, bias=bias, M=Mr, N=N, K=K)

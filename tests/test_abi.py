@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every entry point include/mxfp8.h declares, and rejects bad
+arguments before touching HIP (so these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mx_block_scaled_amd import mxfp8
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp8.h")
+MX_OK, MX_EINVAL, MX_ESHAPE, MX_EALIGN, MX_EWORKSPACE = 0, -1, -2, -3, -4
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxfp8_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mxfp8.library_path):
+        import __graft_entry__
+        __graft_entry__.build()
+    return mxfp8.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 10, names
+    raw = ctypes.CDLL(mxfp8.library_path)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_binding_covers_header(L):
+    # the Python binding registers a signature for each declared entry point
+    for n in _declared():
+        assert getattr(L, n).argtypes is not None or n == "mxfp8_last_error", n
+
+
+# Fake 16-byte aligned "device" addresses.  Every call below must be rejected by argument
+# validation (or be an M == 0 no-op): none may reach a kernel launch, so these tests are safe
+# on a GPU machine too.
+A = 1 << 20
+B = (1 << 20) + 4096
+
+
+def test_quantize_act_validation(L):
+    assert L.mxfp8_quantize_act(A, 4, 48, 48, B, B, None) == MX_ESHAPE       # K % 32
+    assert L.mxfp8_quantize_act(A, -1, 64, 64, B, B, None) == MX_ESHAPE
+    assert L.mxfp8_quantize_act(None, 4, 64, 64, B, B, None) == MX_EINVAL
+    assert L.mxfp8_quantize_act(A, 4, 64, 32, B, B, None) == MX_ESHAPE       # ldx < K
+    assert L.mxfp8_quantize_act(A + 2, 4, 64, 64, B, B, None) == MX_EALIGN
+    assert L.mxfp8_quantize_act(A, 4, 64, 68, B, B, None) == MX_EALIGN       # ldx % 8
+    assert L.mxfp8_quantize_act(None, 0, 64, 64, None, None, None) == MX_OK  # M == 0: no-op
+    L.mxfp8_quantize_act(A, 4, 40, 40, B, B, None)
+    assert b"multiple of 32" in L.mxfp8_last_error()
+
+
+def test_linear_validation(L):
+    ws = L.mxfp8_workspace_bytes(64, 256, 512, 0)
+    assert ws >= 64 * 512 + 64 * 16
+    assert L.mxfp8_linear(A, 64, 512, B, 256, 0, None, B, B, ws - 1, None) == MX_EWORKSPACE
+    assert L.mxfp8_linear(A, 64, 512, B, 256, 0, None, B, None, ws, None) == MX_EWORKSPACE
+    assert L.mxfp8_linear(A, 64, 512, B, 250, 0, None, B, B, ws, None) == MX_ESHAPE   # N % 16
+    assert L.mxfp8_linear(A, 64, 500, B, 256, 0, None, B, B, ws, None) == MX_ESHAPE   # K % 32
+    assert L.mxfp8_linear(A, 64, 512, B, 256, 1, None, B, B, ws, None) == MX_EINVAL   # E5M2: no
+    assert L.mxfp8_linear(A, 64, 512, B, 256, 4, None, B, B, ws, None) == MX_EINVAL
+    assert L.mxfp8_linear(A, 64, 512, None, 256, 0, None, B, B, ws, None) == MX_EINVAL
+    assert L.mxfp8_linear(A, 64, 512, B, 256, 0, None, B + 8, B, ws, None) == MX_EALIGN
+    assert L.mxfp8_linear(None, 0, 512, B, 256, 0, None, B, None, 0, None) == MX_OK
+    assert L.mxfp8_linear_prequant(A, B, 64, 512, B, 256, 0, None, None, None) == MX_EINVAL
+    assert L.mxfp8_linear_prequant(A, None, 64, 512, B, 256, 0, None, B, None) == MX_EINVAL
+    assert L.mxfp8_linear_prequant(A + 1, B, 64, 512, B, 256, 0, None, B, None) == MX_EALIGN
+    assert L.mxfp8_linear_prequant(A, B, 0, 512, B, 256, 0, None, B, None) == MX_OK
+
+
+def test_weight_validation(L):
+    assert L.mxfp8_prepack_weight(A, 500, B, 16, 256, 512, 0, B, None) == MX_ESHAPE   # ldw < K
+    assert L.mxfp8_prepack_weight(A, 512, B, 8, 256, 512, 0, B, None) == MX_ESHAPE    # ld_ws
+    assert L.mxfp8_prepack_weight(A, 520, B, 16, 256, 512, 0, B + 8, None) == MX_EALIGN  # packed
+    # an FP6 row of 3K/4 = 384 bytes passes the shape check (then fails on the odd pointer)
+    assert L.mxfp8_prepack_weight(A, 384, B, 16, 256, 512, 2, B + 1, None) == MX_EALIGN
+    assert L.mxfp8_prepack_weight(A, 383, B, 16, 256, 512, 2, B, None) == MX_ESHAPE
+    assert L.mxfp8_prepack_weight(A, 512, B, 16, 256, 512, 7, B, None) == MX_EINVAL
+    assert L.mxfp8_unpack_weight(None, 256, 512, 0, B, B, None) == MX_EINVAL
+    assert L.mxfp8_quantize_weight(A, 256, 512, 512, 5, B, B, None) == MX_EINVAL
+    assert L.mxfp8_quantize_weight(A, 255, 512, 512, 0, B, B, None) == MX_ESHAPE
+
+
+def test_sizes(L):
+    # prepacked: K padded to 128 per 16-row fragment (2048 B E4M3, 1536 B FP6) + scale words
+    assert L.mxfp8_prepacked_bytes(256, 512, 0) == 4 * 16 * 2048 + 1 * 16 * 256
+    assert L.mxfp8_prepacked_bytes(256, 544, 0) == 5 * 16 * 2048 + 2 * 16 * 256
+    assert L.mxfp8_prepacked_bytes(8192, 8192, 2) == 64 * 512 * 1536 + 16 * 512 * 256
+    assert L.mxfp8_prepacked_bytes(250, 512, 0) == 0
+    assert L.mxfp8_prepacked_bytes(256, 512, 9) == 0
+    assert L.mxfp8_workspace_bytes(0, 256, 512, 0) == 0
+    assert L.mxfp8_device_supported(-1) == MX_EINVAL
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    import importlib
+    m = importlib.reload(mxfp8)
+    monkeypatch.setattr(m, "library_path", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(m, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        m.lib()
+    importlib.reload(mxfp8)

@@ -1,0 +1,177 @@
+"""GPU parity of the MX linear layer against the fp64 CPU oracle.
+
+Acceptance (tests/tolerance.py): per element |y - ref| <= 2 ulp_bf16(|ref|) + 1e-3 rms(ref) and
+relative Frobenius error <= 5e-3.  Weights are quantized by the oracle (as the workloads say),
+uploaded and prepacked on the GPU; activations go through the GPU quantizer (bf16 entry) or are
+pre-quantized by the oracle (pre-quantized entry).  Full-size workloads are checked on sampled
+outputs (plus whole rows and columns) that the oracle computes one by one; reduced sizes that
+span several tiles and ragged tails are checked element by element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from mx_block_scaled_amd import mxfp8, synth
+from tests import tolerance
+from tests.gpu_helpers import DEV, banner, bf16_dev, host_bf16_bits, host_u8, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+FMTS = {0: "e4m3", 2: "e2m3", 3: "e3m2"}
+
+
+def _layer(w_bits, fmt, bias_bits=None):
+    wq, ws = orc.quantize(w_bits, fmt)
+    wstore = wq if fmt == 0 else orc.fp6_pack(wq)
+    layer = mxfp8.MxLinear(u8_dev(wstore), u8_dev(ws), fmt,
+                           bias=None if bias_bits is None else bf16_dev(bias_bits))
+    return layer, wq, ws
+
+
+def _full_check(x_bits, w_bits, fmt, bias_bits=None, name=""):
+    layer, wq, ws = _layer(w_bits, fmt, bias_bits)
+    y = layer(bf16_dev(x_bits))
+    ref, _, _ = orc.linear_ref(x_bits, wq, ws, fmt, bias_bits)
+    ok, rep = tolerance.check(host_bf16_bits(y), ref, name=name)
+    assert ok, rep
+    return y, layer
+
+
+def _sampled_check(y, xq, xs, wq, ws, fmt, bias_bits, M, N, n_samples=3000, seed=0, name=""):
+    g = np.random.default_rng(seed)
+    rows = [g.integers(0, M, n_samples), np.array([0, 0, M - 1, M - 1])]
+    cols = [g.integers(0, N, n_samples), np.array([0, N - 1, 0, N - 1])]
+    # one whole output row and one whole output column
+    rows += [np.full(N, g.integers(0, M)), np.arange(M)]
+    cols += [np.arange(N), np.full(M, g.integers(0, N))]
+    r, c = np.concatenate(rows), np.concatenate(cols)
+    bias = None if bias_bits is None else tolerance.bf16_to_f64(bias_bits)
+    ref = orc.linear_entries(xq, xs, wq, ws, r, c, wfmt=fmt, bias=bias)
+    yb = host_bf16_bits(y)[r, c]
+    ok, rep = tolerance.check(yb, ref, name=name)
+    assert ok, rep
+
+
+def test_tiny_full():
+    d = synth.make("tiny")
+    banner("linear tiny")
+    _full_check(d["x"], d["w"], 0, name="tiny")
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_decode_full(M):
+    d = synth.make("decode%d" % M)
+    banner("linear decode", M)
+    _full_check(d["x"], d["w"], 0, d["bias"], name="decode%d" % M)
+
+
+def test_prefill_full_size_sampled():
+    d = synth.make("prefill")
+    banner("linear prefill 4096x14336x4096")
+    layer, wq, ws = _layer(d["w"], 0)
+    y = layer(bf16_dev(d["x"]))
+    xq, xs = orc.quantize(d["x"], orc.E4M3)
+    _sampled_check(y, xq, xs, wq, ws, 0, None, d["M"], d["N"], name="prefill")
+
+
+def test_outlier_prequant_full_size_sampled():
+    d = synth.make("outlier")
+    banner("linear_prequant outlier 2048x6144x4096")
+    xq, xs = orc.quantize(d["x"], orc.E4M3)          # quantized once, by the oracle
+    assert (xs == 0).sum() >= 262                     # the zeroed blocks
+    layer, wq, ws = _layer(d["w"], 0)
+    y = layer.apply_quantized(u8_dev(xq), u8_dev(xs))
+    _sampled_check(y, xq, xs, wq, ws, 0, None, d["M"], d["N"], name="outlier")
+
+
+def test_outlier_prequant_reduced_full():
+    d = synth.make("outlier", N=512)
+    xq, xs = orc.quantize(d["x"][:256], orc.E4M3)
+    layer, wq, ws = _layer(d["w"], 0)
+    y = layer.apply_quantized(u8_dev(xq), u8_dev(xs))
+    ref = orc.matmul_nt(orc.dequantize(xq, xs), orc.dequantize(wq, ws))
+    ok, rep = tolerance.check(host_bf16_bits(y), ref, name="outlier-256x512")
+    assert ok, rep
+
+
+@pytest.mark.parametrize("fmt", [2, 3])
+def test_mxfp6_full_size_sampled(fmt):
+    d = synth.make("mxfp6")
+    banner("linear mxfp6", FMTS[fmt], "512x8192x8192")
+    layer, wq, ws = _layer(d["w"], fmt)
+    y = layer(bf16_dev(d["x"]))
+    xq, xs = orc.quantize(d["x"], orc.E4M3)
+    _sampled_check(y, xq, xs, wq, ws, fmt, None, d["M"], d["N"], name="mxfp6-%d" % fmt)
+
+
+@pytest.mark.parametrize("fmt", [2, 3])
+def test_mxfp6_reduced_full(fmt):
+    d = synth.make("mxfp6", M=64, N=512)
+    _full_check(d["x"], d["w"], fmt, name="mxfp6-small-%d" % fmt)
+
+
+RAGGED = [(1, 16, 32), (3, 48, 96), (17, 272, 160), (33, 64, 544), (100, 80, 1056), (65, 16, 4096)]
+
+
+@pytest.mark.parametrize("fmt", [0, 2, 3])
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_ragged_shapes(M, N, K, fmt):
+    g = np.random.default_rng(M * 7 + N + K)
+    x = synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    w = synth.bf16_bits((g.standard_normal((N, K)) * 0.05).astype(np.float32))
+    b = synth.bf16_bits((g.standard_normal(N) * 0.1).astype(np.float32))
+    banner("linear ragged", M, N, K, FMTS[fmt])
+    _full_check(x, w, fmt, b, name="ragged-%d-%d-%d-%d" % (M, N, K, fmt))
+
+
+def test_gpu_weight_quantizer_path_matches_oracle_path():
+    d = synth.make("decode8", N=1024)
+    wq, ws = mxfp8.quantize_weight(bf16_dev(d["w"]), 0)
+    p1 = mxfp8.prepack_weight(wq, ws, 0)
+    layer, _, _ = _layer(d["w"], 0)
+    x = bf16_dev(d["x"])
+    y1 = mxfp8.linear(x, p1, d["N"], 0)
+    y2 = layer(x)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+def test_zero_rows_and_bias_none():
+    d = synth.make("tiny")
+    layer, _, _ = _layer(d["w"], 0)
+    y = layer(bf16_dev(d["x"][:0]))
+    assert y.shape == (0, 256)
+
+
+def test_deterministic_and_no_out_of_bounds_writes():
+    d = synth.make("decode32", N=512)
+    layer, wq, ws = _layer(d["w"], 0, d["bias"][:512])
+    x = bf16_dev(d["x"])
+    M, N = 32, 512
+    guard = 4096
+    big = torch.full((2 * guard + M * N,), -7777.0, dtype=torch.bfloat16, device=DEV)
+    out = big[guard:guard + M * N].view(M, N)
+    y1 = mxfp8.linear(x, layer.packed, N, 0, layer.bias, out=out).clone()
+    y2 = mxfp8.linear(x, layer.packed, N, 0, layer.bias)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert bool((big[:guard] == -7777.0).all()) and bool((big[guard + M * N:] == -7777.0).all())
+
+
+def test_leading_dims():
+    d = synth.make("tiny")
+    layer, wq, ws = _layer(d["w"], 0)
+    x3 = d["x"].reshape(2, 8, 512)
+    y = layer(bf16_dev(x3))
+    assert y.shape == (2, 8, 256)
+    ref, _, _ = orc.linear_ref(d["x"], wq, ws)
+    ok, rep = tolerance.check(host_bf16_bits(y).reshape(16, 256), ref)
+    assert ok, rep
+
+
+def test_prequant_rejects_wrong_scale_shape():
+    d = synth.make("tiny")
+    layer, _, _ = _layer(d["w"], 0)
+    xq, xs = mxfp8.quantize_act(bf16_dev(d["x"]))
+    with pytest.raises(ValueError):
+        layer.apply_quantized(xq, xs[:, :8].contiguous())

@@ -1,0 +1,42 @@
+"""GPU: the load-time weight prepack has an exact inverse (aiter_flydsl page, row_major_weight:
+the rearranged weight can always be read back as row-major [N, K]), for every format, ragged K,
+and weight-scale tensors larger than [N, K/32] (process_weights_after_loading slices them)."""
+import numpy as np
+import pytest
+import torch
+
+from mx_block_scaled_amd import mxfp8
+from tests.gpu_helpers import DEV, banner, host_u8, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("fmt", [0, 2, 3])
+@pytest.mark.parametrize("N,K", [(16, 32), (48, 160), (256, 544), (4096, 4096), (128, 8192)])
+def test_roundtrip(fmt, N, K):
+    g = np.random.default_rng(N + K + fmt)
+    row = K if fmt == 0 else K // 4 * 3
+    wq = g.integers(0, 256, (N, row)).astype(np.uint8)
+    ws = g.integers(0, 255, (N, K // 32)).astype(np.uint8)
+    banner("prepack roundtrip", fmt, N, K)
+    p = mxfp8.prepack_weight(u8_dev(wq), u8_dev(ws), fmt, K=K)
+    assert p.numel() == mxfp8.prepacked_bytes(N, K, fmt)
+    wq2, ws2 = mxfp8.unpack_weight(p, N, K, fmt)
+    assert np.array_equal(host_u8(wq2), wq)
+    assert np.array_equal(host_u8(ws2), ws)
+
+
+def test_strided_sources():
+    g = np.random.default_rng(9)
+    N, K = 64, 256
+    wq_big = g.integers(0, 256, (N, K + 32)).astype(np.uint8)     # row stride > K
+    ws_big = g.integers(0, 255, (N + 16, K // 32 + 3)).astype(np.uint8)   # padded scale tensor
+    t = u8_dev(wq_big)
+    s = u8_dev(ws_big)
+    p = torch.empty(mxfp8.prepacked_bytes(N, K, 0), dtype=torch.uint8, device=DEV)
+    rc = mxfp8.lib().mxfp8_prepack_weight(t.data_ptr(), K + 32, s.data_ptr(), K // 32 + 3, N, K, 0,
+                                          p.data_ptr(), None)
+    assert rc == 0
+    wq2, ws2 = mxfp8.unpack_weight(p, N, K, 0)
+    assert np.array_equal(host_u8(wq2), wq_big[:, :K])
+    assert np.array_equal(host_u8(ws2), ws_big[:N, :K // 32])

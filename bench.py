@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""bench.py — throughput of the MXFP8 linear layer (activation quantization + block-scaled GEMM)
+on one MI355X.
+
+A step is one call of the layer on the prefill workload: x bf16 [4096, 4096] ~ N(0,1), weight
+[14336, 4096] (MLP up-projection shape) quantized to E4M3 + E8M0 from N(0, 0.02), no bias, bf16
+out, through mxfp8_linear (quantizer kernel + GEMM kernel).  value = 2*M*N*K / step time, in
+TFLOP/s, with activation quantization inside the timed step.  Inputs are resident in HBM before
+the clock starts; R copies of the inputs/weights/outputs are rotated so the working set exceeds
+the 256 MiB Infinity Cache.
+
+Also measured and printed in the same JSON line:
+  roofline      the GEMM kernel alone (pre-quantized entry), timed with HIP events on the
+                stream it runs on: achieved TFLOP/s against the 5.0 PFLOP/s dense FP8 peak;
+                traffic from the committed rocprofv3 counter summary while the kernel source
+                still matches it, else null;
+  decode        the decode workload (x [M, 4096], M in {1, 8, 32}, weight [4096, 4096], bias),
+                one fused call each, replayed from a HIP graph over 32 rotated weight copies:
+                time per call, algorithmic bytes / time against 8 TB/s;
+  cpu_baseline  the CPU oracle on a bounded sample of the prefill workload (host cores),
+                run in a separate process (oracle/cpu_bench.py).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+import argparse
+import hashlib
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+MALL_BYTES = 256 << 20
+
+
+def _gemm_source_hash():
+    h = hashlib.sha256()
+    for f in ("mx_gemm.hip", "mx_device.h"):
+        h.update(open(os.path.join(ROOT, "mx_block_scaled_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, n_launch_units=1):
+    """HBM bytes per launch from profiles/traffic.json, if the kernel source is unchanged."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        t = json.load(open(p))[kernel_key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha") != _gemm_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from mx_block_scaled_amd import mxfp8, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ------------------------------------------------------------ prefill workload
+    M, N, K = 4096, 14336, 4096
+    d = synth.make("prefill")
+    x0 = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    w0 = torch.from_numpy(d["w"].view(np.int16)).view(torch.bfloat16).to(dev)
+    wq, ws = mxfp8.quantize_weight(w0, "e4m3")
+    packed0 = mxfp8.prepack_weight(wq, ws, "e4m3")
+    del w0, wq, ws
+    set_bytes = x0.numel() * 2 + packed0.numel() + M * N * 2
+    R = max(2, -(-2 * MALL_BYTES // set_bytes))
+    xs_ = [x0] + [x0.clone() for _ in range(R - 1)]
+    ps_ = [packed0] + [packed0.clone() for _ in range(R - 1)]
+    ys_ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
+    wsb = torch.empty(mxfp8.workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        j = i % R
+        mxfp8.linear(xs_[j], ps_[j], N, "e4m3", out=ys_[j], workspace=wsb)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    flop = 2.0 * M * N * K
+    value = flop / (ms_per_step * 1e-3) / 1e12
+
+    # ------------------------------------------------------------ GEMM kernel alone (roofline)
+    xq_, xsc_ = [], []
+    for j in range(R):
+        q, s = mxfp8.quantize_act(xs_[j])
+        xq_.append(q)
+        xsc_.append(s)
+    stream = torch.cuda.current_stream(dev)
+    n_gemm = max(args.steps, 50)
+    for j in range(5):
+        mxfp8.linear_prequant(xq_[j % R], xsc_[j % R], ps_[j % R], N, "e4m3", out=ys_[j % R])
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n_gemm):
+        j = i % R
+        mxfp8.linear_prequant(xq_[j], xsc_[j], ps_[j], N, "e4m3", out=ys_[j])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    gemm_us = e0.elapsed_time(e1) * 1e3 / n_gemm
+    achieved = flop / (gemm_us * 1e-6) / 1e12
+    # quantizer alone
+    e0.record(stream)
+    for i in range(n_gemm):
+        j = i % R
+        mxfp8.quantize_act(xs_[j])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    quant_us = e0.elapsed_time(e1) * 1e3 / n_gemm
+    roofline = {
+        "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
+        "traffic": _traffic("gemm_prefill"),
+        "kernel": "k_gemm (pre-quantized entry), %dx%dx%d" % (M, N, K),
+        "kernel_us": round(gemm_us, 2),
+        "algorithmic_flop_per_launch": flop,
+    }
+    quant_bytes = M * K * 2 + M * K + M * K // 32
+    del xq_, xsc_
+
+    # ------------------------------------------------------------ decode (HBM-bound)
+    decode = None
+    if not args.no_decode:
+        del xs_, ps_, ys_, wsb
+        torch.cuda.empty_cache()
+        decode = {}
+        dd = synth.make("decode32")
+        Nd = Kd = 4096
+        w0 = torch.from_numpy(dd["w"].view(np.int16)).view(torch.bfloat16).to(dev)
+        wq, ws = mxfp8.quantize_weight(w0, "e4m3")
+        pk = mxfp8.prepack_weight(wq, ws, "e4m3")
+        bias = torch.from_numpy(dd["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
+        RD = 32
+        pks = [pk] + [pk.clone() for _ in range(RD - 1)]
+        for Md in (1, 8, 32):
+            xd = torch.from_numpy(dd["x"][:Md].view(np.int16)).view(torch.bfloat16).to(dev)
+            yd = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
+            wsd = torch.empty(max(1, mxfp8.workspace_bytes(Md, Nd, Kd)), dtype=torch.uint8, device=dev)
+            s = torch.cuda.Stream(dev)
+            s.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(s):
+                for j in range(RD):                     # eager warm-up on the capture stream
+                    mxfp8.linear(xd, pks[j], Nd, "e4m3", bias, out=yd, workspace=wsd)
+            torch.cuda.current_stream(dev).wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for j in range(RD):
+                    mxfp8.linear(xd, pks[j], Nd, "e4m3", bias, out=yd, workspace=wsd)
+            reps = max(4, args.steps // 8)
+            g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) * 1e6 / (reps * RD)
+            bytes_alg = Md * Kd * 2 + (pk.numel()) + Md * Nd * 2 + Nd * 2
+            gbs = bytes_alg / (us * 1e-6) / 1e9
+            decode["M%d" % Md] = {
+                "us_per_call": round(us, 3), "TFLOP/s": round(2.0 * Md * Nd * Kd / (us * 1e-6) / 1e12, 3),
+                "algorithmic_bytes": bytes_alg, "GB/s": round(gbs, 1),
+                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+            del g
+        del pks, pk
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
+        env = dict(os.environ)
+        env.pop("CUDA_VISIBLE_DEVICES", None)
+        r = subprocess.run([sys.executable, "-m", "oracle.cpu_bench", "--workload", "prefill",
+                            "--seconds", str(args.cpu_seconds)],
+                           cwd=ROOT, capture_output=True, text=True, env=env)
+        if r.returncode == 0:
+            c = json.loads(r.stdout.strip().splitlines()[-1])
+            cpu = {"value": c["value"], "unit": c["unit"], "cores": c["cores"],
+                   "kind": "oracle", "sample": c["sample"]}
+        else:
+            cpu = {"error": r.stderr[-500:]}
+
+    out = {
+        "metric": "MXFP8 linear TFLOP/s (incl. act quant) and % MFMA/HBM roofline, prefill & decode",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8-e4m3 (mxfp8) -> fp32 acc -> bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantized on the GPU)",
+        "config": {"workload": "prefill MLP up-proj: x bf16 [4096,4096] x W mxfp8 [14336,4096] "
+                               "-> y bf16 [4096,14336], act quant included",
+                   "M": M, "N": N, "K": K, "rotated_sets": R},
+        "roofline": roofline,
+        "quantizer": {"us": round(quant_us, 2), "GB/s": round(quant_bytes / (quant_us * 1e-6) / 1e9, 1),
+                      "hbm_frac": round(quant_bytes / (quant_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -128,6 +128,14 @@ int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K,
                           const void* packed, int64_t N, int fmt, const void* bias, void* y,
                           void* stream);
 
+/* ---------------------------------------------------------------- tuning */
+
+/* Tuning / testing hook: force the tile of the LDS-tiled GEMM used for large M (fn, fm =
+ * 16-row weight fragments and 16-row activation groups per wave; the workgroup tile is
+ * 32 fn x 32 fm).  Compiled choices: (7,8) (8,7) (6,8) (4,8) (4,4); (0,0) restores the automatic
+ * choice.  Process-wide; not for use while other threads are launching.  MX_EINVAL otherwise. */
+int mxfp8_set_tile_config(int fn, int fm);
+
 #ifdef __cplusplus
 }
 #endif

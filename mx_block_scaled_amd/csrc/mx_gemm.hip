@@ -7,6 +7,9 @@
 //
 // The weight is the MFMA's A operand (rows = n) and the activations the B operand (columns =
 // m): each lane then owns 4 consecutive n of one output row m, i.e. one 8-byte bf16 store.
+#include <atomic>
+#include <type_traits>
+
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -83,11 +86,300 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const uint8_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- LDS-tiled kernel (large M)
+// Workgroup tile: 256 weight rows (n) x 256 activation rows (m), K step 128, 4 waves, each wave a
+// 128 x 128 quadrant = 8 x 8 MFMA tiles (256 fp32 accumulators per lane).  Both operand tiles
+// are copied global -> LDS with the 16-byte direct-to-LDS load (lane i of an instruction lands
+// at LDS base + 16 i), double buffered:
+//   A (weight): 16 prepacked fragments of one K step are contiguous in global memory, so the
+//     LDS image is a plain copy and each lane's MFMA operand is one (or two) lane-contiguous
+//     16-byte LDS reads — conflict-free.
+//   B (activations, row-major [M, K]): 128-byte row slices; the 16-byte chunk c of row r is kept
+//     in slot c ^ swz(r), so one DMA instruction covers 8 whole rows (coalesced global reads) and
+//     the MFMA-order reads (16 rows, same chunk) hit 16 distinct bank groups.
+// Scales: the weight's come prepacked per lane (one 32-bit word per 4 K steps); the
+// activations' are gathered per lane from row-major [M, K/32] into the same form; the MFMA's
+// op-select picks the byte of the current K step.
+// Requires K % 128 == 0 (no K tail) and a 4-byte aligned xs; rows/columns past M/N are clamped
+// on load and skipped on store.
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ ((row & 1) << 2)) & 7; }
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_dst, 16, 0, 0);
+}
+
+// scaled MFMA with the scale byte chosen by op-select; q is a constant after loop unrolling
+template <int WFMT>
+__device__ __forceinline__ v4f mfma_opsel(int q, const v8i& a, const v8i& b, v4f c, uint32_t sa,
+                                          uint32_t sb) {
+  switch (q) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, WFMT, 0, 0, (int)sa, 0, (int)sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, WFMT, 0, 1, (int)sa, 1, (int)sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, WFMT, 0, 2, (int)sa, 2, (int)sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, WFMT, 0, 3, (int)sa, 3, (int)sb);
+  }
+}
+
+// Tile geometry: each of the 4 waves (2 x 2) owns FN weight fragments (16 rows each) and FM
+// activation groups (16 rows each); workgroup tile = 32 FN weight rows x 32 FM activation rows.
+template <int WFMT, int FN, int FM>
+struct TileCfg {
+  static constexpr int FB = frag_bytes(WFMT);
+  static constexpr int BN = 32 * FN, BM = 32 * FM;
+  static constexpr int A_BYTES = 2 * FN * FB;      // BN weight rows x one K step
+  static constexpr int B_BYTES = BM * 128;         // BM activation rows x 128 bytes
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_CHUNKS = A_BYTES / 1024;  // 1 KiB DMA instructions per stage
+  static constexpr int A_PER_WAVE = (A_CHUNKS + 3) / 4;
+  static constexpr int B_PER_WAVE = B_BYTES / 4096;
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 4096 == 0, "tile must split into 1 KiB chunks");
+  static_assert(2 * STAGE <= 160 * 1024, "two stages must fit the 160 KiB LDS");
+};
+
+template <int WFMT, int FN, int FM>
+__global__ __launch_bounds__(256, 1) void k_gemm_tile(const uint8_t* __restrict__ xq,
+                                                      const uint8_t* __restrict__ xs, int M, int K,
+                                                      const uint8_t* __restrict__ packed, int N,
+                                                      const uint16_t* __restrict__ bias,
+                                                      uint16_t* __restrict__ y, int tiles_m,
+                                                      int tiles_n, int group_m) {
+  using C = TileCfg<WFMT, FN, FM>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+  const int r = lane & 15, g = lane >> 4;
+
+  // ---- tile of this workgroup: workgroups go round-robin to the 8 XCDs; give each XCD a
+  // contiguous range of tiles, ordered in groups of group_m activation-row tiles so the tiles
+  // running together on one XCD share operand panels in its L2.
+  const int T = tiles_m * tiles_n;
+  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const int t = xcd * (T >> 3) + (xcd < (T & 7) ? xcd : (T & 7)) + slot;
+  const int gsz = group_m * tiles_n;
+  const int first_m = (t / gsz) * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int tm = first_m + (t % gsz) % gm;
+  const int tn = (t % gsz) / gm;
+  const int n0 = tn * C::BN, m0 = tm * C::BM;
+
+  const int NG = N >> 4, KT = K >> 7, KB = K >> 5;
+  const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * C::FB);
+
+  // ---- per-lane DMA sources, as 32-bit offsets from uniform bases (every operand < 2^31 B)
+  // A: wave w copies 1 KiB chunks w, w+4, ... of the stage's A block (fragments clamped to NG)
+  uint32_t a_off[C::A_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::A_PER_WAVE; ++i) {
+    const int off = min(wave + 4 * i, C::A_CHUNKS - 1) * 1024 + lane * 16;
+    const int f = off / C::FB;
+    const int ng = min((n0 >> 4) + f, NG - 1);
+    a_off[i] = (uint32_t)(ng * C::FB + (off - f * C::FB));
+  }
+  // B: wave w copies rows 8 c .. 8 c + 7 for c = w, w+4, ..., lane -> (row, slot)
+  uint32_t b_off[C::B_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::B_PER_WAVE; ++i) {
+    const int row = 8 * (wave + 4 * i) + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    b_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + chunk * 16);
+  }
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    uint8_t* base = lds + stage * C::STAGE;
+    const uint8_t* ab = packed + (int64_t)kt * NG * C::FB;
+    const uint8_t* bb = xq + kt * 128;
+#pragma unroll
+    for (int i = 0; i < C::A_PER_WAVE; ++i)
+      if (C::A_CHUNKS % 4 == 0 || wave + 4 * i < C::A_CHUNKS)   // wave-uniform
+        dma16(ab + a_off[i], base + (wave + 4 * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < C::B_PER_WAVE; ++i)
+      dma16(bb + b_off[i], base + C::A_BYTES + (wave + 4 * i) * 1024);
+  };
+
+  // ---- per-lane scale sources
+  uint32_t a_soff[FN];
+#pragma unroll
+  for (int i = 0; i < FN; ++i) a_soff[i] = (uint32_t)(min((n0 >> 4) + wn * FN + i, NG - 1) * 64 + lane);
+  uint32_t b_soff[FM];
+#pragma unroll
+  for (int j = 0; j < FM; ++j) b_soff[j] = (uint32_t)(min(m0 + wm * 16 * FM + 16 * j + r, M - 1) * KB);
+  const uint32_t psel = (uint32_t)g | ((uint32_t)(4 + g) << 8) | ((uint32_t)g << 16) | ((uint32_t)(4 + g) << 24);
+  // scale words of K steps 4 kt4 .. 4 kt4 + 3 (kt4 clamped to the last group by the caller);
+  // words of steps past K read an in-row address and are replaced by 127 (1.0) — branch-free,
+  // so the K-step group below stays one basic block
+  auto load_scales = [&](int kt4, uint32_t* sa, uint32_t* sb) __attribute__((always_inline)) {
+    const uint32_t* ws4 = wsc + (int64_t)kt4 * NG * 64;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) sa[i] = ws4[a_soff[i]];
+    const int left = KB - 16 * kt4;   // scale bytes of a row left from this group on (>= 4)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      uint32_t d[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool in = 4 * q < left;
+        const uint32_t v = *(const uint32_t*)(xs + b_soff[j] + (in ? 16 * kt4 + 4 * q : 0));
+        d[q] = in ? v : 0x7F7F7F7Fu;
+      }
+      const uint32_t t01 = __builtin_amdgcn_perm(d[1], d[0], psel);
+      const uint32_t t23 = __builtin_amdgcn_perm(d[3], d[2], psel);
+      sb[j] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    }
+  };
+
+  v4f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  // one K step from LDS stage kt & 1; Q >= 0: op-select Q on 4-step scale words, Q < 0: the
+  // step's scale byte is shifted down and op-select 0 is used (remainder steps)
+  auto kstep = [&](int kt, auto qc, const uint32_t* sa, const uint32_t* sb) __attribute__((always_inline)) {
+    constexpr int Q = decltype(qc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // the next step's tiles go to the other stage; past the last step the last step is simply
+    // fetched again (unused), which keeps this code free of branches
+    issue(min(kt + 1, KT - 1), (kt + 1) & 1);
+    const uint8_t* base = lds + (kt & 1) * C::STAGE;
+    const uint8_t* bl = base + C::A_BYTES;
+    const int sh = 8 * (kt & 3);
+    v8i b[FM];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int row = wm * 16 * FM + 16 * j + r;
+      const v4i lo = *(const v4i*)(bl + row * 128 + ((g ^ swz(row)) << 4));
+      const v4i hi = *(const v4i*)(bl + row * 128 + (((4 + g) ^ swz(row)) << 4));
+      b[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const uint8_t* fa = base + (wn * FN + i) * C::FB;
+      v8i a;
+      if (WFMT == 0) {
+        const v4i lo = *(const v4i*)(fa + lane * 16);
+        const v4i hi = *(const v4i*)(fa + 1024 + lane * 16);
+        a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const v4i lo = *(const v4i*)(fa + lane * 16);
+        const v2i hi = *(const v2i*)(fa + 1024 + lane * 8);
+        a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+      }
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        if (Q >= 0)
+          acc[i][j] = mfma_opsel<WFMT>(Q, a, b[j], acc[i][j], sa[i], sb[j]);
+        else
+          acc[i][j] = mfma_opsel<WFMT>(0, a, b[j], acc[i][j], sa[i] >> sh, sb[j] >> sh);
+      }
+    }
+  };
+
+  uint32_t sa[FN], sb[FM], sa_n[FN], sb_n[FM];
+  const int KT4 = (KT + 3) >> 2;
+  const int KT4f = KT >> 2;               // groups of four whole K steps
+  load_scales(0, sa, sb);
+  issue(0, 0);
+  for (int kt4 = 0; kt4 < KT4f; ++kt4) {
+    load_scales(min(kt4 + 1, KT4 - 1), sa_n, sb_n);
+    kstep(4 * kt4 + 0, std::integral_constant<int, 0>(), sa, sb);
+    kstep(4 * kt4 + 1, std::integral_constant<int, 1>(), sa, sb);
+    kstep(4 * kt4 + 2, std::integral_constant<int, 2>(), sa, sb);
+    kstep(4 * kt4 + 3, std::integral_constant<int, 3>(), sa, sb);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) sa[i] = sa_n[i];
+#pragma unroll
+    for (int j = 0; j < FM; ++j) sb[j] = sb_n[j];
+  }
+  for (int kt = 4 * KT4f; kt < KT; ++kt) kstep(kt, std::integral_constant<int, -1>(), sa, sb);
+  // no LDS write may still be in flight when the workgroup's LDS is released
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: lane holds n = n_tile + 16 i + 4 g + (0..3) of activation row m
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    const int n = n0 + wn * 16 * FN + 16 * i + 4 * g;
+    if (n >= N) continue;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[e] = bf16_to_float(bias[n + e]);
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int m = m0 + wm * 16 * FM + 16 * j + r;
+      if (m >= M) continue;
+      const v2i o = {(int)pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]),
+                     (int)pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3])};
+      *(v2i*)(y + (int64_t)m * N + n) = o;
+    }
+  }
+}
+
+template <int WFMT, int FN, int FM>
+static void launch_tile(const uint8_t* xq, const uint8_t* xs, int M, int K, const uint8_t* packed,
+                        int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s) {
+  using C = TileCfg<WFMT, FN, FM>;
+  const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
+  hipLaunchKernelGGL((k_gemm_tile<WFMT, FN, FM>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, xq,
+                     xs, M, K, packed, N, bias, y, tm, tn, group_m);
+}
+
+// Tile choice: the configurations below are compiled; pick the one whose tile count fills the
+// 256 CUs in the fewest (and fullest) waves, preferring larger tiles on ties.
+struct TileChoice { int fn, fm; };
+static std::atomic<int> g_force_tile{0};   // fn * 16 + fm, 0 = automatic
+void force_tile(int fn, int fm) { g_force_tile.store(fn * 16 + fm); }
+static TileChoice choose_tile(int M, int N) {
+  const int f = g_force_tile.load(std::memory_order_relaxed);
+  if (f) return TileChoice{f / 16, f % 16};
+  static const TileChoice opts[] = {{7, 8}, {8, 7}, {6, 8}, {4, 8}, {4, 4}};
+  double best = 1e30;
+  TileChoice pick = opts[0];
+  for (const TileChoice& o : opts) {
+    const int bn = 32 * o.fn, bm = 32 * o.fm;
+    const long tiles = (long)((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+    const long waves = (tiles + 255) / 256;
+    // time ~ waves x per-tile work, per-tile work ~ bn * bm (+ a fixed operand-load cost)
+    const double cost = (double)waves * ((double)bn * bm + 64.0 * (bn + bm));
+    if (cost < best * 0.999) { best = cost; pick = o; }
+  }
+  return pick;
+}
+
+template <int WFMT>
+static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int K,
+                               const uint8_t* packed, int N, const uint16_t* bias, uint16_t* y,
+                               hipStream_t s) {
+  const TileChoice c = choose_tile(M, N);
+  const int group_m = 4;
+  if (c.fn == 7 && c.fm == 8) launch_tile<WFMT, 7, 8>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  else if (c.fn == 8 && c.fm == 7) launch_tile<WFMT, 8, 7>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  else if (c.fn == 6 && c.fm == 8) launch_tile<WFMT, 6, 8>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  else if (c.fn == 4 && c.fm == 8) launch_tile<WFMT, 4, 8>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  else launch_tile<WFMT, 4, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
                        uint16_t* y, hipStream_t s) {
-  dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)((M + 31) / 32)), block(256);
   const int m = (int)M, k = (int)K, n = (int)N;
+  const bool tiled = (K % 128 == 0) && (((uintptr_t)xs & 3) == 0) && M >= 64 && N >= 128;
+  if (tiled) {
+    switch (fmt) {
+      case 0: return launch_tiled<0>(xq, xs, m, k, packed, n, bias, y, s);
+      case 2: return launch_tiled<2>(xq, xs, m, k, packed, n, bias, y, s);
+      case 3: return launch_tiled<3>(xq, xs, m, k, packed, n, bias, y, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)((M + 31) / 32)), block(256);
   switch (fmt) {
     case 0: hipLaunchKernelGGL(k_gemm_generic<0>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y); break;
     case 2: hipLaunchKernelGGL(k_gemm_generic<2>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y); break;

@@ -24,6 +24,9 @@ hipError_t launch_prepack(const uint8_t* wq, int64_t ldw, const uint8_t* ws, int
 hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int fmt, uint8_t* wq,
                          uint8_t* ws, hipStream_t s);
 
+// Force the tiled GEMM's tile (fragments per wave along n and m); (0, 0) = automatic.
+void force_tile(int fn, int fm);
+
 // GEMM from quantized activations xq [M, K] + xs [M, K/32] (row-major).
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,

@@ -18,7 +18,7 @@ import torch  # loaded first: libmxfp8 then binds to the HIP runtime torch alrea
 __all__ = [
     "FMT", "MXError", "lib", "library_path", "device_supported", "quantize_act",
     "quantize_weight", "prepack_weight", "unpack_weight", "prepacked_bytes", "workspace_bytes",
-    "linear", "linear_prequant", "MxLinear",
+    "linear", "linear_prequant", "MxLinear", "set_tile_config",
 ]
 
 FMT = {"e4m3": 0, "e2m3": 2, "e3m2": 3}
@@ -55,6 +55,7 @@ def lib():
             "mxfp8_workspace_bytes": (I64, [I64, I64, I64, I]),
             "mxfp8_linear": (I, [P, I64, I64, P, I64, I, P, P, P, I64, P]),
             "mxfp8_linear_prequant": (I, [P, P, I64, I64, P, I64, I, P, P, P]),
+            "mxfp8_set_tile_config": (I, [I, I]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -90,6 +91,11 @@ def _bf16(t, name):
 
 def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def set_tile_config(fn=0, fm=0):
+    """Force the tiled GEMM's tile (tuning/testing); (0, 0) = automatic."""
+    _check(lib().mxfp8_set_tile_config(int(fn), int(fm)))
 
 
 def device_supported(device=0):

@@ -110,3 +110,8 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     with pytest.raises(RuntimeError, match="not built"):
         m.lib()
     importlib.reload(mxfp8)
+
+
+def test_tile_config_hook(L):
+    assert L.mxfp8_set_tile_config(3, 3) == MX_EINVAL
+    assert L.mxfp8_set_tile_config(0, 0) == MX_OK

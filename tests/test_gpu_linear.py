@@ -175,3 +175,24 @@ def test_prequant_rejects_wrong_scale_shape():
     xq, xs = mxfp8.quantize_act(bf16_dev(d["x"]))
     with pytest.raises(ValueError):
         layer.apply_quantized(xq, xs[:, :8].contiguous())
+
+
+TILES = [(7, 8), (8, 7), (6, 8), (4, 8), (4, 4)]
+
+
+@pytest.mark.parametrize("fmt", [0, 2, 3])
+@pytest.mark.parametrize("fn,fm", TILES)
+def test_tiled_kernel_every_tile(fn, fm, fmt):
+    """Each compiled tile of the LDS-tiled kernel, on a shape with ragged M and N tails and a K
+    that is not a multiple of 512 (remainder K steps), against the oracle element by element."""
+    g = np.random.default_rng(fn * 10 + fm + fmt)
+    M, N, K = 300, 592, 640
+    x = synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    w = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    b = synth.bf16_bits((g.standard_normal(N) * 0.01).astype(np.float32))
+    banner("tiled", fn, fm, FMTS[fmt], M, N, K)
+    mxfp8.set_tile_config(fn, fm)
+    try:
+        _full_check(x, w, fmt, b, name="tile-%d-%d-%d" % (fn, fm, fmt))
+    finally:
+        mxfp8.set_tile_config(0, 0)

@@ -131,8 +131,9 @@ int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K,
 /* ---------------------------------------------------------------- tuning */
 
 /* Tuning / testing hook: force the tile of the LDS-tiled GEMM used for large M (fn, fm =
- * 16-row weight fragments and 16-row activation groups per wave; the workgroup tile is
- * 32 fn x 32 fm).  Compiled choices: (7,8) (8,7) (6,8) (4,8) (4,4); (0,0) restores the automatic
+ * 16-row weight fragments and 16-row activation groups per wave; the workgroup of 8 waves
+ * covers 32 fn weight rows x 64 fm activation rows).  Compiled choices: (8,4) (7,4) (6,4)
+ * (4,4) (4,2); (0,0) restores the automatic
  * choice.  Process-wide; not for use while other threads are launching.  MX_EINVAL otherwise. */
 int mxfp8_set_tile_config(int fn, int fm);
 

@@ -221,7 +221,7 @@ int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K, 
 }
 
 int mxfp8_set_tile_config(int fn, int fm) {
-  static const int ok_cfg[][2] = {{0, 0}, {7, 8}, {8, 7}, {6, 8}, {4, 8}, {4, 4}};
+  static const int ok_cfg[][2] = {{0, 0}, {8, 4}, {7, 4}, {6, 4}, {4, 4}, {4, 2}};
   for (const auto& c : ok_cfg)
     if (c[0] == fn && c[1] == fm) {
       mx::force_tile(fn, fm);

@@ -110,6 +110,11 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
 }
 
 // scaled MFMA with the scale byte chosen by op-select; q is a constant after loop unrolling
+__device__ __forceinline__ void dma4(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
+                                   (void __attribute__((address_space(3)))*)lds_dst, 4, 0, 0);
+}
+
 template <int WFMT>
 __device__ __forceinline__ v4f mfma_opsel(int q, const v8i& a, const v8i& b, v4f c, uint32_t sa,
                                           uint32_t sb) {
@@ -121,31 +126,67 @@ __device__ __forceinline__ v4f mfma_opsel(int q, const v8i& a, const v8i& b, v4f
   }
 }
 
-// Tile geometry: each of the 4 waves (2 x 2) owns FN weight fragments (16 rows each) and FM
-// activation groups (16 rows each); workgroup tile = 32 FN weight rows x 32 FM activation rows.
-template <int WFMT, int FN, int FM>
+// Tile geometry: 8 waves (2 per SIMD) in a 2 (n) x 4 (m) grid; each wave owns FN weight
+// fragments (16 rows each) and FM activation groups (16 rows each).  Workgroup tile =
+// 32 FN weight rows x 64 FM activation rows; S LDS stages (the K step being computed plus
+// S - 1 prefetched).  Two waves per SIMD: while one waits on LDS or the barrier, the other
+// keeps the matrix pipe busy, and together they draw about twice the LDS read bandwidth of one.
+template <int WFMT, int FN, int FM, int S>
 struct TileCfg {
+  static constexpr int NW = 8, WGN = 2, WGM = 4;
   static constexpr int FB = frag_bytes(WFMT);
-  static constexpr int BN = 32 * FN, BM = 32 * FM;
-  static constexpr int A_BYTES = 2 * FN * FB;      // BN weight rows x one K step
+  static constexpr int BN = 16 * FN * WGN, BM = 16 * FM * WGM;
+  static constexpr int A_BYTES = (BN / 16) * FB;   // BN weight rows x one K step
   static constexpr int B_BYTES = BM * 128;         // BM activation rows x 128 bytes
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int A_CHUNKS = A_BYTES / 1024;  // 1 KiB DMA instructions per stage
-  static constexpr int A_PER_WAVE = (A_CHUNKS + 3) / 4;
-  static constexpr int B_PER_WAVE = B_BYTES / 4096;
-  static_assert(A_BYTES % 1024 == 0 && B_BYTES % 4096 == 0, "tile must split into 1 KiB chunks");
-  static_assert(2 * STAGE <= 160 * 1024, "two stages must fit the 160 KiB LDS");
+  static constexpr int A_CHUNKS = A_BYTES / 1024;  // 1 KiB DMA instructions
+  static constexpr int A_PER_WAVE = (A_CHUNKS + NW - 1) / NW;   // surplus slots -> scratch
+  static constexpr int B_PER_WAVE = B_BYTES / 1024 / NW;
+  static constexpr int D = A_PER_WAVE + B_PER_WAVE;   // vector-memory ops per wave per step
+  // scales of 4 K steps ("group"), staged in LDS with 4-byte DMA (256 B per instruction): the
+  // weight's BN/16 fragments x 64 lane words, the activations' BM rows x 16 B
+  static constexpr int SA_PIECES = BN / 16, SB_PIECES = BM / 16;
+  static constexpr int SA_PER_WAVE = (SA_PIECES + NW - 1) / NW;
+  static constexpr int SB_PER_WAVE = (SB_PIECES + NW - 1) / NW;
+  static constexpr int SA_BYTES = SA_PIECES * 256, SB_BYTES = SB_PIECES * 256;
+  static constexpr int SCALE_BYTES = SA_BYTES + SB_BYTES;
+  static constexpr int SL = SA_PER_WAVE + SB_PER_WAVE;  // scale DMAs per wave per group
+  static constexpr int SCRATCH = 1024;                  // target of surplus DMA slots
+  // epilogue: bf16 tile [BM][BN]; a row pitch of 16 (mod 256) bytes puts the 8-byte writes of
+  // a wave (16 rows x 4 column groups) on distinct bank pairs
+  static constexpr int OUT_PITCH = (BN * 2 - 16 + 255) / 256 * 256 + 16;
+  static constexpr int LDS_MAIN = S * STAGE + 2 * SCALE_BYTES + SCRATCH;
+  static constexpr int LDS_BYTES = LDS_MAIN > BM * OUT_PITCH ? LDS_MAIN : BM * OUT_PITCH;
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % (1024 * NW) == 0, "1 KiB DMA chunks");
+  static_assert(S >= 2 && LDS_BYTES <= 160 * 1024, "must fit the 160 KiB LDS");
+  // vector-memory ops issued after the DMA of step kt when step kt starts (q = kt % 4): the
+  // DMAs of the next S - 2 steps, plus one group of scale DMAs if one was issued in between
+  // (scale DMAs go out right after the DMA of each group's first step).
+  static constexpr int vm_after(int q) { return (S - 2) * D + ((q >= 1 && q <= S - 1) ? SL : 0); }
+  static_assert(vm_after(1) <= 63, "vmcnt is a 6-bit counter");
+  static_assert(S <= 4, "the scale DMAs of a group must retire before the group's first step");
 };
 
-template <int WFMT, int FN, int FM>
-__global__ __launch_bounds__(256, 1) void k_gemm_tile(const uint8_t* __restrict__ xq,
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt not waited), then the workgroup barrier.  A plain
+// barrier is used instead of __syncthreads(), whose fence would wait for every DMA in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | ((N >> 4) << 14));
+  __builtin_amdgcn_s_barrier();
+}
+
+template <int WFMT, int FN, int FM, int S>
+__global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict__ xq,
                                                       const uint8_t* __restrict__ xs, int M, int K,
                                                       const uint8_t* __restrict__ packed, int N,
                                                       const uint16_t* __restrict__ bias,
                                                       uint16_t* __restrict__ y, int tiles_m,
                                                       int tiles_n, int group_m) {
-  using C = TileCfg<WFMT, FN, FM>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * C::STAGE];
+  using C = TileCfg<WFMT, FN, FM, S>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
+  uint8_t* const slds = lds + S * C::STAGE;                  // two group-scale buffers
+  uint8_t* const scratch = slds + 2 * C::SCALE_BYTES;        // surplus DMA slots land here
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -169,20 +210,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tile(const uint8_t* __restrict_
   const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * C::FB);
 
   // ---- per-lane DMA sources, as 32-bit offsets from uniform bases (every operand < 2^31 B)
-  // A: wave w copies 1 KiB chunks w, w+4, ... of the stage's A block (fragments clamped to NG)
+  // A: wave w copies 1 KiB chunks w, w + 8, ... of the stage's A block (fragments clamped to
+  // NG); chunk indices past the block are surplus slots aimed at the scratch area
   uint32_t a_off[C::A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::A_PER_WAVE; ++i) {
-    const int off = min(wave + 4 * i, C::A_CHUNKS - 1) * 1024 + lane * 16;
+    const int off = min(wave + C::NW * i, C::A_CHUNKS - 1) * 1024 + lane * 16;
     const int f = off / C::FB;
     const int ng = min((n0 >> 4) + f, NG - 1);
     a_off[i] = (uint32_t)(ng * C::FB + (off - f * C::FB));
   }
-  // B: wave w copies rows 8 c .. 8 c + 7 for c = w, w+4, ..., lane -> (row, slot)
+  // B: wave w copies rows 8 c .. 8 c + 7 for c = w, w + 8, ..., lane -> (row, slot)
   uint32_t b_off[C::B_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::B_PER_WAVE; ++i) {
-    const int row = 8 * (wave + 4 * i) + (lane >> 3);
+    const int row = 8 * (wave + C::NW * i) + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(row);
     b_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + chunk * 16);
   }
@@ -191,39 +233,60 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tile(const uint8_t* __restrict_
     const uint8_t* ab = packed + (int64_t)kt * NG * C::FB;
     const uint8_t* bb = xq + kt * 128;
 #pragma unroll
-    for (int i = 0; i < C::A_PER_WAVE; ++i)
-      if (C::A_CHUNKS % 4 == 0 || wave + 4 * i < C::A_CHUNKS)   // wave-uniform
-        dma16(ab + a_off[i], base + (wave + 4 * i) * 1024);
+    for (int i = 0; i < C::A_PER_WAVE; ++i) {
+      const int c = wave + C::NW * i;     // wave-uniform
+      dma16(ab + a_off[i], c < C::A_CHUNKS ? base + c * 1024 : scratch);
+    }
 #pragma unroll
     for (int i = 0; i < C::B_PER_WAVE; ++i)
-      dma16(bb + b_off[i], base + C::A_BYTES + (wave + 4 * i) * 1024);
+      dma16(bb + b_off[i], base + C::A_BYTES + (wave + C::NW * i) * 1024);
   };
 
-  // ---- per-lane scale sources
-  uint32_t a_soff[FN];
+  // ---- per-lane scale DMA sources (4-byte DMA: one instruction moves 64 lanes x 4 B = 256 B)
+  // weight: piece c moves fragment n0/16 + c's 64 lane words
+  uint32_t sa_src[C::SA_PER_WAVE];
 #pragma unroll
-  for (int i = 0; i < FN; ++i) a_soff[i] = (uint32_t)(min((n0 >> 4) + wn * FN + i, NG - 1) * 64 + lane);
-  uint32_t b_soff[FM];
+  for (int i = 0; i < C::SA_PER_WAVE; ++i) {
+    const int c = min(wave + C::NW * i, C::SA_PIECES - 1);
+    sa_src[i] = (uint32_t)(min((n0 >> 4) + c, NG - 1) * 256 + lane * 4);
+  }
+  // activations: piece c moves rows 16 c .. 16 c + 15, 4 words (16 B) each; lane l takes row
+  // 16 c + l / 4, word l % 4 (columns clamped inside the row at issue time)
+  uint32_t sb_src[C::SB_PER_WAVE];
 #pragma unroll
-  for (int j = 0; j < FM; ++j) b_soff[j] = (uint32_t)(min(m0 + wm * 16 * FM + 16 * j + r, M - 1) * KB);
+  for (int i = 0; i < C::SB_PER_WAVE; ++i) {
+    const int c = min(wave + C::NW * i, C::SB_PIECES - 1);
+    sb_src[i] = (uint32_t)(min(m0 + 16 * c + (lane >> 2), M - 1) * KB);
+  }
+  const int q4 = (lane & 3) * 4;
+  auto issue_scales = [&](int kt4, int sbuf) __attribute__((always_inline)) {
+    uint8_t* base = slds + sbuf * C::SCALE_BYTES;
+    const uint8_t* wsg = (const uint8_t*)wsc + (int64_t)kt4 * NG * 256;
+#pragma unroll
+    for (int i = 0; i < C::SA_PER_WAVE; ++i) {
+      const int c = wave + C::NW * i;
+      dma4(wsg + sa_src[i], c < C::SA_PIECES ? base + c * 256 : scratch);
+    }
+    const int col = min(16 * kt4 + q4, KB - 4);
+#pragma unroll
+    for (int i = 0; i < C::SB_PER_WAVE; ++i) {
+      const int c = wave + C::NW * i;
+      dma4(xs + sb_src[i] + col, c < C::SB_PIECES ? base + C::SA_BYTES + c * 256 : scratch);
+    }
+  };
   const uint32_t psel = (uint32_t)g | ((uint32_t)(4 + g) << 8) | ((uint32_t)g << 16) | ((uint32_t)(4 + g) << 24);
-  // scale words of K steps 4 kt4 .. 4 kt4 + 3 (kt4 clamped to the last group by the caller);
-  // words of steps past K read an in-row address and are replaced by 127 (1.0) — branch-free,
-  // so the K-step group below stays one basic block
-  auto load_scales = [&](int kt4, uint32_t* sa, uint32_t* sb) __attribute__((always_inline)) {
-    const uint32_t* ws4 = wsc + (int64_t)kt4 * NG * 64;
+  // this lane's op-select scale words of group kt4 from buffer sbuf
+  auto read_scales = [&](int kt4, int sbuf, uint32_t* sa, uint32_t* sb) __attribute__((always_inline)) {
+    const uint8_t* base = slds + sbuf * C::SCALE_BYTES;
 #pragma unroll
-    for (int i = 0; i < FN; ++i) sa[i] = ws4[a_soff[i]];
-    const int left = KB - 16 * kt4;   // scale bytes of a row left from this group on (>= 4)
+    for (int i = 0; i < FN; ++i) sa[i] = *(const uint32_t*)(base + (wn * FN + i) * 256 + lane * 4);
+    const int left = KB - 16 * kt4;   // scale bytes of a row from this group on
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
+      const v4i w = *(const v4i*)(base + C::SA_BYTES + (wm * 16 * FM + 16 * j + r) * 16);
       uint32_t d[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const bool in = 4 * q < left;
-        const uint32_t v = *(const uint32_t*)(xs + b_soff[j] + (in ? 16 * kt4 + 4 * q : 0));
-        d[q] = in ? v : 0x7F7F7F7Fu;
-      }
+      for (int q = 0; q < 4; ++q) d[q] = (4 * q < left) ? (uint32_t)w[q] : 0x7F7F7F7Fu;
       const uint32_t t01 = __builtin_amdgcn_perm(d[1], d[0], psel);
       const uint32_t t23 = __builtin_amdgcn_perm(d[3], d[2], psel);
       sb[j] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
@@ -236,19 +299,26 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tile(const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-  // one K step from LDS stage kt & 1; Q >= 0: op-select Q on 4-step scale words, Q < 0: the
-  // step's scale byte is shifted down and op-select 0 is used (remainder steps)
-  auto kstep = [&](int kt, auto qc, const uint32_t* sa, const uint32_t* sb) __attribute__((always_inline)) {
+  auto load_a = [&](const uint8_t* base, int i) __attribute__((always_inline)) {
+    const uint8_t* fa = base + (wn * FN + i) * C::FB;
+    if (WFMT == 0) {
+      const v4i lo = *(const v4i*)(fa + lane * 16);
+      const v4i hi = *(const v4i*)(fa + 1024 + lane * 16);
+      return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {
+      const v4i lo = *(const v4i*)(fa + lane * 16);
+      const v2i hi = *(const v2i*)(fa + 1024 + lane * 8);
+      return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+    }
+  };
+  // One K step's MFMAs from LDS stage `stage`.  LDS reads run one weight fragment ahead of the
+  // MFMAs (fragment 0 first, then the activation fragments, then fragment i + 1 before the
+  // MFMAs of fragment i), pinned with scheduling-group barriers.
+  auto compute = [&](int stage, auto qc, const uint32_t* sa, const uint32_t* sb, int sh) __attribute__((always_inline)) {
     constexpr int Q = decltype(qc)::value;
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // the next step's tiles go to the other stage; past the last step the last step is simply
-    // fetched again (unused), which keeps this code free of branches
-    issue(min(kt + 1, KT - 1), (kt + 1) & 1);
-    const uint8_t* base = lds + (kt & 1) * C::STAGE;
+    const uint8_t* base = lds + stage * C::STAGE;
     const uint8_t* bl = base + C::A_BYTES;
-    const int sh = 8 * (kt & 3);
+    v8i a = load_a(base, 0);
     v8i b[FM];
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
@@ -257,18 +327,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tile(const uint8_t* __restrict_
       const v4i hi = *(const v4i*)(bl + row * 128 + (((4 + g) ^ swz(row)) << 4));
       b[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * FM, 0);   // DS reads: A0, all B
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      const uint8_t* fa = base + (wn * FN + i) * C::FB;
-      v8i a;
-      if (WFMT == 0) {
-        const v4i lo = *(const v4i*)(fa + lane * 16);
-        const v4i hi = *(const v4i*)(fa + 1024 + lane * 16);
-        a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      } else {
-        const v4i lo = *(const v4i*)(fa + lane * 16);
-        const v2i hi = *(const v2i*)(fa + 1024 + lane * 8);
-        a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+      v8i an = a;
+      if (i + 1 < FN) {
+        an = load_a(base, i + 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // DS reads: A(i+1)
       }
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
@@ -277,72 +342,103 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tile(const uint8_t* __restrict_
         else
           acc[i][j] = mfma_opsel<WFMT>(0, a, b[j], acc[i][j], sa[i] >> sh, sb[j] >> sh);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);           // MFMAs of fragment i
+      a = an;
     }
   };
 
-  uint32_t sa[FN], sb[FM], sa_n[FN], sb_n[FM];
+  uint32_t sa[FN], sb[FM];
   const int KT4 = (KT + 3) >> 2;
   const int KT4f = KT >> 2;               // groups of four whole K steps
-  load_scales(0, sa, sb);
-  issue(0, 0);
-  for (int kt4 = 0; kt4 < KT4f; ++kt4) {
-    load_scales(min(kt4 + 1, KT4 - 1), sa_n, sb_n);
-    kstep(4 * kt4 + 0, std::integral_constant<int, 0>(), sa, sb);
-    kstep(4 * kt4 + 1, std::integral_constant<int, 1>(), sa, sb);
-    kstep(4 * kt4 + 2, std::integral_constant<int, 2>(), sa, sb);
-    kstep(4 * kt4 + 3, std::integral_constant<int, 3>(), sa, sb);
+  // prologue: scales of group 0 (waited for and read), then the DMAs of steps 0 .. S-2
+  issue_scales(0, 0);
+  wait_vm_barrier<0>();
+  read_scales(0, 0, sa, sb);
 #pragma unroll
-    for (int i = 0; i < FN; ++i) sa[i] = sa_n[i];
-#pragma unroll
-    for (int j = 0; j < FM; ++j) sb[j] = sb_n[j];
-  }
-  for (int kt = 4 * KT4f; kt < KT; ++kt) kstep(kt, std::integral_constant<int, -1>(), sa, sb);
-  // no LDS write may still be in flight when the workgroup's LDS is released
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  for (int st = 0; st < S - 1; ++st) issue(min(st, KT - 1), st);
 
-  // ---- epilogue: lane holds n = n_tile + 16 i + 4 g + (0..3) of activation row m
+  // One K step of a full group.  At the top, the tiles of step kt have landed once at most
+  // vm_after(q) later memory operations are outstanding (vmcnt retires in issue order); the
+  // DMA of step kt + S - 1 then goes to the stage freed by step kt - 1 (past the last step the
+  // last step is fetched again, unused: the operation count per step never changes).  The
+  // first step of a group reads the group's scales and sends the next group's scale DMAs.
+  auto step = [&](int kt, auto qc) __attribute__((always_inline)) {
+    constexpr int Q = decltype(qc)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_barrier<C::vm_after(Q)>();
+    if (Q == 0 && kt > 0) read_scales(kt >> 2, (kt >> 2) & 1, sa, sb);
+    issue(min(kt + S - 1, KT - 1), (kt + S - 1) % S);
+    if (Q == 0) issue_scales(min((kt >> 2) + 1, KT4 - 1), ((kt >> 2) + 1) & 1);
+    compute(kt % S, qc, sa, sb, 0);
+  };
+  for (int kt4 = 0; kt4 < KT4f; ++kt4) {
+    step(4 * kt4 + 0, std::integral_constant<int, 0>());
+    step(4 * kt4 + 1, std::integral_constant<int, 1>());
+    step(4 * kt4 + 2, std::integral_constant<int, 2>());
+    step(4 * kt4 + 3, std::integral_constant<int, 3>());
+  }
+  // remainder steps (K / 128 not a multiple of 4): everything waited for, no prefetch
+  for (int kt = 4 * KT4f; kt < KT; ++kt) {
+    wait_vm_barrier<0>();
+    if (kt == 4 * KT4f && KT4f > 0) read_scales(KT4f, KT4f & 1, sa, sb);
+    if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    compute(kt % S, std::integral_constant<int, -1>(), sa, sb, 8 * (kt & 3));
+  }
+  // all DMAs landed and all waves done with the stages before LDS is reused for the output
+  wait_vm_barrier<0>();
+
+  // ---- epilogue: bias, bf16 rounding, through LDS as a row-major [BM][BN] tile (rows padded
+  // by 16 B so the 8-byte writes of a wave hit distinct banks), then 16-byte coalesced stores.
+  // Lane holds n = 16 (wn FN + i) + 4 g + (0..3) of activation row wm 16 FM + 16 j + r.
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
-    const int n = n0 + wn * 16 * FN + 16 * i + 4 * g;
-    if (n >= N) continue;
+    const int nl = wn * 16 * FN + 16 * i + 4 * g;
     float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
+    if (bias && n0 + nl < N) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) bv[e] = bf16_to_float(bias[n + e]);
+      for (int e = 0; e < 4; ++e) bv[e] = bf16_to_float(bias[n0 + nl + e]);
     }
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int m = m0 + wm * 16 * FM + 16 * j + r;
-      if (m >= M) continue;
+      const int ml = wm * 16 * FM + 16 * j + r;
       const v2i o = {(int)pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]),
                      (int)pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3])};
-      *(v2i*)(y + (int64_t)m * N + n) = o;
+      *(v2i*)(lds + ml * C::OUT_PITCH + nl * 2) = o;
     }
+  }
+  __syncthreads();
+  constexpr int ROW_PIECES = C::BN * 2 / 16;          // 16-byte pieces per tile row
+#pragma unroll 4
+  for (int p = tid; p < C::BM * ROW_PIECES; p += C::NW * 64) {
+    const int ml = p / ROW_PIECES, cp = p - ml * ROW_PIECES;
+    const int m = m0 + ml, n = n0 + cp * 8;
+    if (m < M && n < N) *(v4i*)(y + (int64_t)m * N + n) = *(const v4i*)(lds + ml * C::OUT_PITCH + cp * 16);
   }
 }
 
-template <int WFMT, int FN, int FM>
+template <int WFMT, int FN, int FM, int S>
 static void launch_tile(const uint8_t* xq, const uint8_t* xs, int M, int K, const uint8_t* packed,
                         int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s) {
-  using C = TileCfg<WFMT, FN, FM>;
+  using C = TileCfg<WFMT, FN, FM, S>;
   const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((k_gemm_tile<WFMT, FN, FM>), dim3((unsigned)(tm * tn)), dim3(256), 0, s, xq,
-                     xs, M, K, packed, N, bias, y, tm, tn, group_m);
+  hipLaunchKernelGGL((k_gemm_tile<WFMT, FN, FM, S>), dim3((unsigned)(tm * tn)), dim3(512), 0, s,
+                     xq, xs, M, K, packed, N, bias, y, tm, tn, group_m);
 }
 
 // Tile choice: the configurations below are compiled; pick the one whose tile count fills the
 // 256 CUs in the fewest (and fullest) waves, preferring larger tiles on ties.
 struct TileChoice { int fn, fm; };
+// compiled tiles (fn, fm) -> workgroup tile 32 fn x 64 fm, two LDS stages
 static std::atomic<int> g_force_tile{0};   // fn * 16 + fm, 0 = automatic
 void force_tile(int fn, int fm) { g_force_tile.store(fn * 16 + fm); }
 static TileChoice choose_tile(int M, int N) {
   const int f = g_force_tile.load(std::memory_order_relaxed);
   if (f) return TileChoice{f / 16, f % 16};
-  static const TileChoice opts[] = {{7, 8}, {8, 7}, {6, 8}, {4, 8}, {4, 4}};
+  static const TileChoice opts[] = {{8, 4}, {7, 4}, {6, 4}, {4, 4}, {4, 2}};
   double best = 1e30;
   TileChoice pick = opts[0];
   for (const TileChoice& o : opts) {
-    const int bn = 32 * o.fn, bm = 32 * o.fm;
+    const int bn = 32 * o.fn, bm = 64 * o.fm;
     const long tiles = (long)((N + bn - 1) / bn) * ((M + bm - 1) / bm);
     const long waves = (tiles + 255) / 256;
     // time ~ waves x per-tile work, per-tile work ~ bn * bm (+ a fixed operand-load cost)
@@ -358,11 +454,11 @@ static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int 
                                hipStream_t s) {
   const TileChoice c = choose_tile(M, N);
   const int group_m = 4;
-  if (c.fn == 7 && c.fm == 8) launch_tile<WFMT, 7, 8>(xq, xs, M, K, packed, N, bias, y, group_m, s);
-  else if (c.fn == 8 && c.fm == 7) launch_tile<WFMT, 8, 7>(xq, xs, M, K, packed, N, bias, y, group_m, s);
-  else if (c.fn == 6 && c.fm == 8) launch_tile<WFMT, 6, 8>(xq, xs, M, K, packed, N, bias, y, group_m, s);
-  else if (c.fn == 4 && c.fm == 8) launch_tile<WFMT, 4, 8>(xq, xs, M, K, packed, N, bias, y, group_m, s);
-  else launch_tile<WFMT, 4, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  if (c.fn == 8 && c.fm == 4) launch_tile<WFMT, 8, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  else if (c.fn == 7 && c.fm == 4) launch_tile<WFMT, 7, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  else if (c.fn == 6 && c.fm == 4) launch_tile<WFMT, 6, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  else if (c.fn == 4 && c.fm == 4) launch_tile<WFMT, 4, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  else launch_tile<WFMT, 4, 2, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
   return hipGetLastError();
 }
 

@@ -126,6 +126,43 @@ __device__ __forceinline__ v4f mfma_opsel(int q, const v8i& a, const v8i& b, v4f
   }
 }
 
+// In-place scaled MFMA (D == C) as inline assembly: the builtin often gets a separate
+// destination from the register allocator, which costs a spare accumulator quad per MFMA in
+// flight.  Q = op-select byte of both scale registers; CBSZ = A-operand format (weight).
+#define MX_MFMA_OPSEL_0 "op_sel_hi:[0,0,0]"
+#define MX_MFMA_OPSEL_1 "op_sel:[1,1,0] op_sel_hi:[0,0,0]"
+#define MX_MFMA_OPSEL_2 "op_sel_hi:[1,1,0]"
+#define MX_MFMA_OPSEL_3 "op_sel:[1,1,0] op_sel_hi:[1,1,0]"
+#define MX_MFMA_ASM(OPSEL, FMT)                                                                 \
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 " OPSEL FMT           \
+               : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb))
+// A-operand register image of one weight fragment: 32 bytes for E4M3, 24 for FP6
+template <int WFMT> struct AReg { typedef v8i type; };
+template <> struct AReg<2> { typedef v6i type; };
+template <> struct AReg<3> { typedef v6i type; };
+
+template <int WFMT, int Q>
+__device__ __forceinline__ void mfma_inplace(v4f& acc, const typename AReg<WFMT>::type& a,
+                                             const v8i& b, uint32_t sa, uint32_t sb) {
+  static_assert(Q >= 0 && Q < 4, "op-select byte");
+  if constexpr (WFMT == 0) {
+    if constexpr (Q == 0) MX_MFMA_ASM(MX_MFMA_OPSEL_0, "");
+    else if constexpr (Q == 1) MX_MFMA_ASM(MX_MFMA_OPSEL_1, "");
+    else if constexpr (Q == 2) MX_MFMA_ASM(MX_MFMA_OPSEL_2, "");
+    else MX_MFMA_ASM(MX_MFMA_OPSEL_3, "");
+  } else if constexpr (WFMT == 2) {
+    if constexpr (Q == 0) MX_MFMA_ASM(MX_MFMA_OPSEL_0, " cbsz:2");
+    else if constexpr (Q == 1) MX_MFMA_ASM(MX_MFMA_OPSEL_1, " cbsz:2");
+    else if constexpr (Q == 2) MX_MFMA_ASM(MX_MFMA_OPSEL_2, " cbsz:2");
+    else MX_MFMA_ASM(MX_MFMA_OPSEL_3, " cbsz:2");
+  } else {
+    if constexpr (Q == 0) MX_MFMA_ASM(MX_MFMA_OPSEL_0, " cbsz:3");
+    else if constexpr (Q == 1) MX_MFMA_ASM(MX_MFMA_OPSEL_1, " cbsz:3");
+    else if constexpr (Q == 2) MX_MFMA_ASM(MX_MFMA_OPSEL_2, " cbsz:3");
+    else MX_MFMA_ASM(MX_MFMA_OPSEL_3, " cbsz:3");
+  }
+}
+
 // Tile geometry: 8 waves (2 per SIMD) in a 2 (n) x 4 (m) grid; each wave owns FN weight
 // fragments (16 rows each) and FM activation groups (16 rows each).  Workgroup tile =
 // 32 FN weight rows x 64 FM activation rows; S LDS stages (the K step being computed plus
@@ -212,14 +249,22 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   // ---- per-lane DMA sources, as 32-bit offsets from uniform bases (every operand < 2^31 B)
   // A: wave w copies 1 KiB chunks w, w + 8, ... of the stage's A block (fragments clamped to
   // NG); chunk indices past the block are surplus slots aimed at the scratch area
+  // (E4M3 fragments are 2 KiB, so a chunk lies in one fragment and the offset is uniform +
+  // lane * 16; FP6 fragments are 1.5 KiB and a chunk may straddle two, so the offset is per lane)
   uint32_t a_off[C::A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::A_PER_WAVE; ++i) {
-    const int off = min(wave + C::NW * i, C::A_CHUNKS - 1) * 1024 + lane * 16;
-    const int f = off / C::FB;
-    const int ng = min((n0 >> 4) + f, NG - 1);
-    a_off[i] = (uint32_t)(ng * C::FB + (off - f * C::FB));
+    const int c = min(wave + C::NW * i, C::A_CHUNKS - 1);
+    if (C::FB % 1024 == 0) {
+      const int f = c * 1024 / C::FB;
+      a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (c * 1024 - f * C::FB));
+    } else {
+      const int off = c * 1024 + lane * 16;
+      const int f = off / C::FB;
+      a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (off - f * C::FB));
+    }
   }
+  const uint32_t a_lane = C::FB % 1024 == 0 ? (uint32_t)lane * 16 : 0u;
   // B: wave w copies rows 8 c .. 8 c + 7 for c = w, w + 8, ..., lane -> (row, slot)
   uint32_t b_off[C::B_PER_WAVE];
 #pragma unroll
@@ -228,18 +273,21 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     const int chunk = (lane & 7) ^ swz(row);
     b_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + chunk * 16);
   }
-  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+  // the p-th tile DMA of a step (p < D: weight chunks first, then activation rows)
+  auto issue_one = [&](int kt, int stage, int p) __attribute__((always_inline)) {
     uint8_t* base = lds + stage * C::STAGE;
-    const uint8_t* ab = packed + (int64_t)kt * NG * C::FB;
-    const uint8_t* bb = xq + kt * 128;
-#pragma unroll
-    for (int i = 0; i < C::A_PER_WAVE; ++i) {
-      const int c = wave + C::NW * i;     // wave-uniform
-      dma16(ab + a_off[i], c < C::A_CHUNKS ? base + c * 1024 : scratch);
+    if (p < C::A_PER_WAVE) {
+      const int c = wave + C::NW * p;     // wave-uniform
+      dma16(packed + (int64_t)kt * NG * C::FB + a_off[p] + a_lane,
+            c < C::A_CHUNKS ? base + c * 1024 : scratch);
+    } else {
+      const int i = p - C::A_PER_WAVE;
+      dma16(xq + kt * 128 + b_off[i], base + C::A_BYTES + (wave + C::NW * i) * 1024);
     }
+  };
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < C::B_PER_WAVE; ++i)
-      dma16(bb + b_off[i], base + C::A_BYTES + (wave + C::NW * i) * 1024);
+    for (int p = 0; p < C::D; ++p) issue_one(kt, stage, p);
   };
 
   // ---- per-lane scale DMA sources (4-byte DMA: one instruction moves 64 lanes x 4 B = 256 B)
@@ -291,6 +339,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
       const uint32_t t23 = __builtin_amdgcn_perm(d[3], d[2], psel);
       sb[j] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
     }
+    asm volatile("s_nop 2" ::: "memory");   // VALU-written scale words before MFMA reads
   };
 
   v4f acc[FN][FM];
@@ -299,50 +348,57 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
 #pragma unroll
     for (int j = 0; j < FM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
+  typedef typename AReg<WFMT>::type AR;
   auto load_a = [&](const uint8_t* base, int i) __attribute__((always_inline)) {
     const uint8_t* fa = base + (wn * FN + i) * C::FB;
-    if (WFMT == 0) {
-      const v4i lo = *(const v4i*)(fa + lane * 16);
+    const v4i lo = *(const v4i*)(fa + lane * 16);
+    if constexpr (WFMT == 0) {
       const v4i hi = *(const v4i*)(fa + 1024 + lane * 16);
-      return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      return (AR){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     } else {
-      const v4i lo = *(const v4i*)(fa + lane * 16);
       const v2i hi = *(const v2i*)(fa + 1024 + lane * 8);
-      return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+      return (AR){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1]};
     }
   };
   // One K step's MFMAs from LDS stage `stage`.  LDS reads run one weight fragment ahead of the
   // MFMAs (fragment 0 first, then the activation fragments, then fragment i + 1 before the
   // MFMAs of fragment i), pinned with scheduling-group barriers.
-  auto compute = [&](int stage, auto qc, const uint32_t* sa, const uint32_t* sb, int sh) __attribute__((always_inline)) {
+  // activation rows of this lane are wm 16 FM + 16 j + r: all share row & 15 == r and so the
+  // swizzle, leaving one address per half and a constant 2 KiB step per j
+  const uint32_t b_lo = (uint32_t)((wm * 16 * FM + r) * 128 + ((g ^ swz(r)) << 4));
+  const uint32_t b_hi = (uint32_t)((wm * 16 * FM + r) * 128 + (((4 + g) ^ swz(r)) << 4));
+  auto compute = [&](int stage, auto qc, const uint32_t* sa_in, const uint32_t* sb_in, int sh, auto&& side) __attribute__((always_inline)) {
     constexpr int Q = decltype(qc)::value;
+    // remainder steps: the step's scale byte shifted into byte 0 (op-select 0); the nops keep
+    // two wait states between these VALU writes and the MFMAs that read them
+    uint32_t sa[FN], sb[FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i) sa[i] = Q >= 0 ? sa_in[i] : sa_in[i] >> sh;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) sb[j] = Q >= 0 ? sb_in[j] : sb_in[j] >> sh;
+    if constexpr (Q < 0) asm volatile("s_nop 2" ::: "memory");
     const uint8_t* base = lds + stage * C::STAGE;
     const uint8_t* bl = base + C::A_BYTES;
-    v8i a = load_a(base, 0);
+    AR a = load_a(base, 0);
     v8i b[FM];
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int row = wm * 16 * FM + 16 * j + r;
-      const v4i lo = *(const v4i*)(bl + row * 128 + ((g ^ swz(row)) << 4));
-      const v4i hi = *(const v4i*)(bl + row * 128 + (((4 + g) ^ swz(row)) << 4));
+      const v4i lo = *(const v4i*)(bl + b_lo + j * 2048);
+      const v4i hi = *(const v4i*)(bl + b_hi + j * 2048);
       b[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 + 2 * FM, 0);   // DS reads: A0, all B
 #pragma unroll
     for (int i = 0; i < FN; ++i) {
-      v8i an = a;
+      AR an = a;
       if (i + 1 < FN) {
         an = load_a(base, i + 1);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);          // DS reads: A(i+1)
       }
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        if (Q >= 0)
-          acc[i][j] = mfma_opsel<WFMT>(Q, a, b[j], acc[i][j], sa[i], sb[j]);
-        else
-          acc[i][j] = mfma_opsel<WFMT>(0, a, b[j], acc[i][j], sa[i] >> sh, sb[j] >> sh);
+        mfma_inplace<WFMT, (Q >= 0 ? Q : 0)>(acc[i][j], a, b[j], sa[i], sb[j]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, FM, 0);           // MFMAs of fragment i
+      side(i);
+      __builtin_amdgcn_sched_barrier(0);
       a = an;
     }
   };
@@ -367,9 +423,11 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     __builtin_amdgcn_sched_barrier(0);
     wait_vm_barrier<C::vm_after(Q)>();
     if (Q == 0 && kt > 0) read_scales(kt >> 2, (kt >> 2) & 1, sa, sb);
+    // this step's DMAs go out together ahead of its MFMAs: tile DMAs first, then (first step
+    // of a group) the scale DMAs
     issue(min(kt + S - 1, KT - 1), (kt + S - 1) % S);
     if (Q == 0) issue_scales(min((kt >> 2) + 1, KT4 - 1), ((kt >> 2) + 1) & 1);
-    compute(kt % S, qc, sa, sb, 0);
+    compute(kt % S, qc, sa, sb, 0, [](int) {});
   };
   for (int kt4 = 0; kt4 < KT4f; ++kt4) {
     step(4 * kt4 + 0, std::integral_constant<int, 0>());
@@ -382,10 +440,13 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     wait_vm_barrier<0>();
     if (kt == 4 * KT4f && KT4f > 0) read_scales(KT4f, KT4f & 1, sa, sb);
     if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
-    compute(kt % S, std::integral_constant<int, -1>(), sa, sb, 8 * (kt & 3));
+    compute(kt % S, std::integral_constant<int, -1>(), sa, sb, 8 * (kt & 3), [](int) {});
   }
-  // all DMAs landed and all waves done with the stages before LDS is reused for the output
+  // all DMAs landed and all waves done with the stages before LDS is reused for the output;
+  // the nops give the last MFMAs (issued as assembly, so untracked by the compiler's hazard
+  // checks) their result latency before VALU code reads the accumulators
   wait_vm_barrier<0>();
+  asm volatile("s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
 
   // ---- epilogue: bias, bf16 rounding, through LDS as a row-major [BM][BN] tile (rows padded
   // by 16 B so the 8-byte writes of a wave hit distinct banks), then 16-byte coalesced stores.

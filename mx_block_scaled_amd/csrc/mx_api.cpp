@@ -197,6 +197,11 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, i
   if (!aligned16(workspace)) return fail(MX_EALIGN, "workspace must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
   hipStream_t s = (hipStream_t)stream;
+  if (mx::small_m_fused(M, K))   // decode shapes: quantization fused into the GEMM launch
+    return hip_status(mx::launch_linear_small_m(x_bf16, nullptr, false, M, K,
+                                                (const uint8_t*)packed, N, fmt,
+                                                (const uint16_t*)bias, (uint16_t*)y, s),
+                      "linear (small M) launch");
   uint8_t* xq = (uint8_t*)workspace;
   uint8_t* xs = xq + ((M * K + 255) / 256) * 256;
   hipError_t e = mx::launch_quantize_act((const uint16_t*)x_bf16, M, K, K, xq, xs, s);

@@ -97,6 +97,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)ua | ((uint32_t)ub << 16);
 }
 
+// max over the 4 lanes of a quad (lanes 4j..4j+3), unsigned.
+__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
+  // quad_perm [1,0,3,2] then [2,3,0,1]
+  uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+  v = v > t ? v : t;
+  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+  return v > t ? v : t;
+}
+
+// largest |bf16| bit pattern (sign cleared) among the 8 values of a 16-byte piece
+__device__ __forceinline__ uint32_t amax8_bf16(const v4i& v) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t u = (uint32_t)v[i] & 0x7FFF7FFFu;
+    const uint32_t lo = u & 0xFFFFu, hi = u >> 16;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
+  return m;
+}
+
 template <int AFMT, int BFMT>
 __device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AFMT, BFMT, 0, sa, 0, sb);

@@ -526,6 +526,8 @@ static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
                        uint16_t* y, hipStream_t s) {
+  if (small_m_quantized(M, K))
+    return launch_linear_small_m(xq, xs, true, M, K, packed, N, fmt, bias, y, s);
   const int m = (int)M, k = (int)K, n = (int)N;
   const bool tiled = (K % 128 == 0) && (((uintptr_t)xs & 3) == 0) && M >= 64 && N >= 128;
   if (tiled) {

@@ -32,4 +32,13 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t 
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
                        uint16_t* y, hipStream_t s);
 
+// Small-M (decode) path: one launch, K split over the waves of a workgroup.  x is bf16 [M, K]
+// quantized inside the kernel (small_m_fused shapes) or, with quantized = true, E4M3 xq [M, K]
+// plus xs [M, K/32] (small_m_quantized shapes).
+bool small_m_fused(int64_t M, int64_t K);
+bool small_m_quantized(int64_t M, int64_t K);
+hipError_t launch_linear_small_m(const void* x, const uint8_t* xs, bool quantized, int64_t M,
+                                 int64_t K, const uint8_t* packed, int64_t N, int fmt,
+                                 const uint16_t* bias, uint16_t* y, hipStream_t s);
+
 }  // namespace mx

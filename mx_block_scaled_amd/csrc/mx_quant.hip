@@ -14,15 +14,6 @@
 
 namespace mx {
 
-// max over the 4 lanes of a quad (lanes 4j..4j+3), unsigned.
-__device__ __forceinline__ uint32_t quad_max_u32(uint32_t v) {
-  // quad_perm [1,0,3,2] then [2,3,0,1]
-  uint32_t t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
-  v = v > t ? v : t;
-  t = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
-  return v > t ? v : t;
-}
-
 // One thread per 8 consecutive elements of a row; 4 consecutive threads form one MX block.
 // groups = M * K / 8; the quad of a block never straddles two rows because K % 32 == 0.
 __global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict__ x, int64_t K,
@@ -40,15 +31,7 @@ __global__ __launch_bounds__(256) void k_quantize_act(const uint16_t* __restrict
     const int64_t c8 = live ? t - row * kg : 0;
     v4i v = {0, 0, 0, 0};
     if (live) v = *(const v4i*)(x + row * ldx + c8 * 8);
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t u = (uint32_t)v[i] & 0x7FFF7FFFu;
-      const uint32_t lo = u & 0xFFFFu, hi = u >> 16;
-      m = m > lo ? m : lo;
-      m = m > hi ? m : hi;
-    }
-    m = quad_max_u32(m);
+    const uint32_t m = quad_max_u32(amax8_bf16(v));
     const uint32_t byte = scale_byte_from_amax<0>(m);
     uint32_t q0, q1;
     if (byte == 0xFFu) {

@@ -196,3 +196,45 @@ def test_tiled_kernel_every_tile(fn, fm, fmt):
         _full_check(x, w, fmt, b, name="tile-%d-%d-%d" % (fn, fm, fmt))
     finally:
         mxfp8.set_tile_config(0, 0)
+
+
+# Small-M (decode) path: one launch with the activation quantizer fused into the GEMM and K
+# split over the 8 waves of a workgroup.  K values give idle waves (K = 384), partial 4-step
+# groups (K = 640, 1152) and a wave with two groups, the second partial (K = 4224).
+SMALL = [(1, 16, 128), (5, 48, 384), (16, 272, 640), (17, 64, 512), (31, 80, 4224),
+         (32, 32, 1152)]
+
+
+def _small_inputs(M, N, K, seed):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((M, K)).astype(np.float32)
+    x[:, g.choice(K, max(1, K // 100), replace=False)] *= 100.0      # outlier channels
+    x = x.reshape(M, K // 32, 32)
+    x[g.integers(0, M, 3), g.integers(0, K // 32, 3)] = 0.0           # all-zero blocks
+    x = synth.bf16_bits(x.reshape(M, K))
+    w = synth.bf16_bits((g.standard_normal((N, K)) * 0.05).astype(np.float32))
+    b = synth.bf16_bits((g.standard_normal(N) * 0.1).astype(np.float32))
+    return x, w, b
+
+
+@pytest.mark.parametrize("fmt", [0, 2, 3])
+@pytest.mark.parametrize("M,N,K", SMALL)
+def test_small_m_fused(M, N, K, fmt):
+    x, w, b = _small_inputs(M, N, K, M * 131 + N + K + fmt)
+    banner("linear small-M", M, N, K, FMTS[fmt])
+    y, layer = _full_check(x, w, fmt, b, name="small-%d-%d-%d-%d" % (M, N, K, fmt))
+    # the pre-quantized entry runs the same kernel with the same summation order, so feeding
+    # it the oracle's quantization of x must reproduce the fused quantizer's result bit for bit
+    xq, xs = orc.quantize(x, orc.E4M3)
+    y2 = layer.apply_quantized(u8_dev(xq), u8_dev(xs))
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_decode_prequant_matches_fused(M):
+    d = synth.make("decode%d" % M)
+    layer, wq, ws = _layer(d["w"], 0, d["bias"])
+    y = layer(bf16_dev(d["x"]))
+    xq, xs = orc.quantize(d["x"], orc.E4M3)
+    y2 = layer.apply_quantized(u8_dev(xq), u8_dev(xs))
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))

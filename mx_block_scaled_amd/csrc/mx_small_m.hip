@@ -43,8 +43,9 @@ constexpr int kRowPitch = 512 + 16;   // LDS row of quantized codes; +16 B sprea
 
 }  // namespace
 
-// MT = 16-row activation tiles (M <= 16 MT); QX = activations arrive quantized (xq, xs).
-template <int WFMT, int MT, bool QX>
+// MT = 16-row activation tiles (M <= 16 MT); QX = activations arrive quantized (xq, xs);
+// XS16 = K % 512 == 0 and every row of xs starts 16-byte aligned (scales read 16 B at a time).
+template <int WFMT, int MT, bool QX, bool XS16>
 __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__ xin,
                                                         const uint8_t* __restrict__ xs, int M,
                                                         int K, const uint8_t* __restrict__ packed,
@@ -98,7 +99,22 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
           const uint8_t* p = (const uint8_t*)xin + (int64_t)mrow[t] * K + 128 * kt + 16 * g;
           xr[j][t][0] = *(const v4i*)p;
           xr[j][t][1] = *(const v4i*)(p + 64);
-          xsb[j][t] = xs[(int64_t)mrow[t] * KB + 4 * kt + g];
+        }
+      }
+      // activation scales of the group: row bytes 16 kt4 + 4 j + g; with XS16 the row's 16
+      // bytes of the group come in one 16-byte load (whole groups only: K % 512 == 0)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        if constexpr (XS16) {
+          const v4i w = *(const v4i*)(xs + (int64_t)mrow[t] * KB + 16 * kt4);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xsb[j][t] = (uint32_t)w[j];
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int kt = min(4 * kt4 + j, KT - 1);
+            xsb[j][t] = xs[(int64_t)mrow[t] * KB + 4 * kt + g];
+          }
         }
       }
     } else {
@@ -161,7 +177,7 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
           if constexpr (QX) {
             const v4i lo = xr[j][t][0], hi = xr[j][t][1];
             b = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            sb = xsb[j][t];
+            sb = XS16 ? (xsb[j][t] >> (8 * g)) & 0xFFu : xsb[j][t];
           } else {
             const uint8_t* p = xl[wave] + mrow[t] * kRowPitch + 128 * j + 16 * g;
             const v4i lo = *(const v4i*)p, hi = *(const v4i*)(p + 64);
@@ -200,12 +216,17 @@ static void launch_small(const void* x, const uint8_t* xs, bool quantized, int M
                          const uint8_t* packed, int N, const uint16_t* bias, uint16_t* y,
                          hipStream_t s) {
   const dim3 grid((unsigned)(N / 16)), block(512);
+  const bool xs16 = ((uintptr_t)xs & 15) == 0 && K % 512 == 0;   // then K / 32 % 16 == 0 too
   if (!quantized)
-    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
+    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, false, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
+  else if (M <= 16 && xs16)
+    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, true, true>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
   else if (M <= 16)
-    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, true>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
+    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, true, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
+  else if (xs16)
+    hipLaunchKernelGGL((k_linear_small_m<WFMT, 2, true, true>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
   else
-    hipLaunchKernelGGL((k_linear_small_m<WFMT, 2, true>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
+    hipLaunchKernelGGL((k_linear_small_m<WFMT, 2, true, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
 }
 
 hipError_t launch_linear_small_m(const void* x, const uint8_t* xs, bool quantized, int64_t M,

@@ -238,3 +238,22 @@ def test_decode_prequant_matches_fused(M):
     xq, xs = orc.quantize(d["x"], orc.E4M3)
     y2 = layer.apply_quantized(u8_dev(xq), u8_dev(xs))
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("fmt", [0, 2])
+@pytest.mark.parametrize("K", [640, 1024])
+def test_tiled_kernel_persistent(K, fmt):
+    """More tiles than workgroups (289 tiles of 128 x 128 on a 256-workgroup persistent grid),
+    ragged M and N: workgroups that run a second tile, with the K pipeline running on from one
+    tile into the next (K % 512 == 0) or restarting per tile (K = 640)."""
+    g = np.random.default_rng(K + fmt)
+    M, N = 2100, 2080
+    x = synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    w = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    b = synth.bf16_bits((g.standard_normal(N) * 0.01).astype(np.float32))
+    banner("tiled persistent", M, N, K, FMTS[fmt])
+    mxfp8.set_tile_config(4, 2)
+    try:
+        _full_check(x, w, fmt, b, name="persistent-%d-%d" % (K, fmt))
+    finally:
+        mxfp8.set_tile_config(0, 0)

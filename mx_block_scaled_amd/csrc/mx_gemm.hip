@@ -189,7 +189,11 @@ struct TileCfg {
   static constexpr int SCALE_BYTES = SA_BYTES + SB_BYTES;
   static constexpr int SL = SA_PER_WAVE + SB_PER_WAVE;  // scale DMAs per wave per group
   static constexpr int SCRATCH = 1024;                  // target of surplus DMA slots
-  static constexpr int LDS_BYTES = S * STAGE + 2 * SCALE_BYTES + SCRATCH;
+  // epilogue: bf16 tile [BM][BN]; a row pitch of 16 (mod 256) bytes puts the 8-byte writes of
+  // a wave (16 rows x 4 column groups) on distinct bank pairs
+  static constexpr int OUT_PITCH = (BN * 2 - 16 + 255) / 256 * 256 + 16;
+  static constexpr int LDS_MAIN = S * STAGE + 2 * SCALE_BYTES + SCRATCH;
+  static constexpr int LDS_BYTES = LDS_MAIN > BM * OUT_PITCH ? LDS_MAIN : BM * OUT_PITCH;
   static_assert(A_BYTES % 1024 == 0 && B_BYTES % (1024 * NW) == 0, "1 KiB DMA chunks");
   static_assert(S >= 2 && LDS_BYTES <= 160 * 1024, "must fit the 160 KiB LDS");
   // vector-memory ops issued after the DMA of step kt when step kt starts (q = kt % 4): the
@@ -226,103 +230,98 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   const int wn = wave & 1, wm = wave >> 1;
   const int r = lane & 15, g = lane >> 4;
 
-  // ---- tiles: the grid is persistent (at most one workgroup per CU); workgroup b takes tiles
-  // b, b + G, b + 2G, ... (G = grid size, a multiple of 8).  Workgroups go round-robin to the 8
-  // XCDs, so tile t runs on XCD t % 8; tile t is mapped to (tm, tn) so that each XCD owns a
-  // contiguous range of the tile order, in groups of group_m activation-row tiles that share
-  // operand panels in the XCD's L2.
+  // ---- tile of this workgroup: workgroups go round-robin to the 8 XCDs; give each XCD a
+  // contiguous range of tiles, ordered in groups of group_m activation-row tiles so the tiles
+  // running together on one XCD share operand panels in its L2.
   const int T = tiles_m * tiles_n;
-  const int G = gridDim.x;
-  auto tile_origin = [&](int t, int& n0, int& m0) __attribute__((always_inline)) {
-    const int xcd = t & 7, slot = t >> 3;
-    const int u = xcd * (T >> 3) + (xcd < (T & 7) ? xcd : (T & 7)) + slot;
-    const int gsz = group_m * tiles_n;
-    const int first_m = (u / gsz) * group_m;
-    const int gm = min(tiles_m - first_m, group_m);
-    m0 = (first_m + (u % gsz) % gm) * C::BM;
-    n0 = ((u % gsz) / gm) * C::BN;
-  };
+  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const int t = xcd * (T >> 3) + (xcd < (T & 7) ? xcd : (T & 7)) + slot;
+  const int gsz = group_m * tiles_n;
+  const int first_m = (t / gsz) * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int tm = first_m + (t % gsz) % gm;
+  const int tn = (t % gsz) / gm;
+  const int n0 = tn * C::BN, m0 = tm * C::BM;
 
   const int NG = N >> 4, KT = K >> 7, KB = K >> 5;
-  const int KT4 = (KT + 3) >> 2;
-  const int KT4f = KT >> 2;               // groups of four whole K steps
-  // whole groups only: the DMA pipeline then runs on from one tile into the next
-  const bool cross = (KT & 3) == 0;
   const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * C::FB);
 
-  // ---- per-lane DMA sources of one tile, as 32-bit offsets from uniform bases (every operand
-  // is below 2^31 bytes): each DMA address is a 64-bit scalar base plus a 32-bit lane offset,
-  // the instruction's own base + offset form, so no 64-bit per-lane address stays live
+  // ---- per-lane DMA sources, as 32-bit offsets from uniform bases (every operand < 2^31 B):
+  // each DMA address is then a 64-bit scalar base plus a 32-bit lane offset, the instruction's
+  // own base + offset form, and no 64-bit per-lane address stays live
   // A: wave w copies 1 KiB chunks w, w + 8, ... of the stage's A block (fragments clamped to
   // NG); chunk indices past the block are surplus slots aimed at the scratch area
   // (E4M3 fragments are 2 KiB, so a chunk lies in one fragment and the offset is uniform +
   // lane * 16; FP6 fragments are 1.5 KiB and a chunk may straddle two, so the offset is per lane)
-  // B: wave w copies rows 8 c .. 8 c + 7 for c = w, w + 8, ..., lane -> (row, slot)
-  // weight scales: piece c moves fragment n0/16 + c's 64 lane words (4-byte DMA: one
-  // instruction moves 64 lanes x 4 B = 256 B); activation scales: piece c moves rows
-  // 16 c .. 16 c + 15, 4 words each; lane l takes row 16 c + l / 4, word l % 4
-  struct Src {
-    uint32_t a_off[C::A_PER_WAVE], b_off[C::B_PER_WAVE], sa[C::SA_PER_WAVE], sb[C::SB_PER_WAVE];
-  };
-  auto make_src = [&](int n0, int m0, Src& o) __attribute__((always_inline)) {
+  uint32_t a_off[C::A_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < C::A_PER_WAVE; ++i) {
-      const int c = min(wave + C::NW * i, C::A_CHUNKS - 1);
-      if (C::FB % 1024 == 0) {
-        const int f = c * 1024 / C::FB;
-        o.a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (c * 1024 - f * C::FB));
-      } else {
-        const int off = c * 1024 + lane * 16;
-        const int f = off / C::FB;
-        o.a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (off - f * C::FB));
-      }
+  for (int i = 0; i < C::A_PER_WAVE; ++i) {
+    const int c = min(wave + C::NW * i, C::A_CHUNKS - 1);
+    if (C::FB % 1024 == 0) {
+      const int f = c * 1024 / C::FB;
+      a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (c * 1024 - f * C::FB));
+    } else {
+      const int off = c * 1024 + lane * 16;
+      const int f = off / C::FB;
+      a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (off - f * C::FB));
     }
-#pragma unroll
-    for (int i = 0; i < C::B_PER_WAVE; ++i) {
-      const int row = 8 * (wave + C::NW * i) + (lane >> 3);
-      const int chunk = (lane & 7) ^ swz(row);
-      o.b_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + chunk * 16);
-    }
-#pragma unroll
-    for (int i = 0; i < C::SA_PER_WAVE; ++i) {
-      const int c = min(wave + C::NW * i, C::SA_PIECES - 1);
-      o.sa[i] = (uint32_t)(min((n0 >> 4) + c, NG - 1) * 256 + lane * 4);
-    }
-#pragma unroll
-    for (int i = 0; i < C::SB_PER_WAVE; ++i) {
-      const int c = min(wave + C::NW * i, C::SB_PIECES - 1);
-      o.sb[i] = (uint32_t)(min(m0 + 16 * c + (lane >> 2), M - 1) * KB);
-    }
-  };
+  }
   const uint32_t a_lane = C::FB % 1024 == 0 ? (uint32_t)lane * 16 : 0u;
-  // the tile DMAs of step kt of the tile described by `src` into stage `stage` (weight chunks
-  // first, then activation rows)
-  auto issue = [&](const Src& src, int kt, int stage) __attribute__((always_inline)) {
+  // B: wave w copies rows 8 c .. 8 c + 7 for c = w, w + 8, ..., lane -> (row, slot)
+  uint32_t b_off[C::B_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::B_PER_WAVE; ++i) {
+    const int row = 8 * (wave + C::NW * i) + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    b_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + chunk * 16);
+  }
+  // the p-th tile DMA of a step (p < D: weight chunks first, then activation rows)
+  auto issue_one = [&](int kt, int stage, int p) __attribute__((always_inline)) {
     uint8_t* base = lds + stage * C::STAGE;
-#pragma unroll
-    for (int p = 0; p < C::A_PER_WAVE; ++p) {
+    if (p < C::A_PER_WAVE) {
       const int c = wave + C::NW * p;     // wave-uniform
-      dma16(packed + (uint32_t)(kt * NG * C::FB + src.a_off[p] + a_lane),
+      dma16(packed + (uint32_t)(kt * NG * C::FB + a_off[p] + a_lane),
             c < C::A_CHUNKS ? base + c * 1024 : scratch);
+    } else {
+      const int i = p - C::A_PER_WAVE;
+      dma16(xq + (uint32_t)(kt * 128 + b_off[i]), base + C::A_BYTES + (wave + C::NW * i) * 1024);
     }
-#pragma unroll
-    for (int i = 0; i < C::B_PER_WAVE; ++i)
-      dma16(xq + (uint32_t)(kt * 128 + src.b_off[i]), base + C::A_BYTES + (wave + C::NW * i) * 1024);
   };
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < C::D; ++p) issue_one(kt, stage, p);
+  };
+
+  // ---- per-lane scale DMA sources (4-byte DMA: one instruction moves 64 lanes x 4 B = 256 B)
+  // weight: piece c moves fragment n0/16 + c's 64 lane words
+  uint32_t sa_src[C::SA_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::SA_PER_WAVE; ++i) {
+    const int c = min(wave + C::NW * i, C::SA_PIECES - 1);
+    sa_src[i] = (uint32_t)(min((n0 >> 4) + c, NG - 1) * 256 + lane * 4);
+  }
+  // activations: piece c moves rows 16 c .. 16 c + 15, 4 words (16 B) each; lane l takes row
+  // 16 c + l / 4, word l % 4 (columns clamped inside the row at issue time)
+  uint32_t sb_src[C::SB_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < C::SB_PER_WAVE; ++i) {
+    const int c = min(wave + C::NW * i, C::SB_PIECES - 1);
+    sb_src[i] = (uint32_t)(min(m0 + 16 * c + (lane >> 2), M - 1) * KB);
+  }
   const int q4 = (lane & 3) * 4;
-  auto issue_scales = [&](const Src& src, int kt4, int sbuf) __attribute__((always_inline)) {
+  auto issue_scales = [&](int kt4, int sbuf) __attribute__((always_inline)) {
     uint8_t* base = slds + sbuf * C::SCALE_BYTES;
 #pragma unroll
     for (int i = 0; i < C::SA_PER_WAVE; ++i) {
       const int c = wave + C::NW * i;
-      dma4((const uint8_t*)wsc + (uint32_t)(kt4 * NG * 256 + src.sa[i]),
+      dma4((const uint8_t*)wsc + (uint32_t)(kt4 * NG * 256 + sa_src[i]),
            c < C::SA_PIECES ? base + c * 256 : scratch);
     }
     const int col = min(16 * kt4 + q4, KB - 4);
 #pragma unroll
     for (int i = 0; i < C::SB_PER_WAVE; ++i) {
       const int c = wave + C::NW * i;
-      dma4(xs + (uint32_t)(src.sb[i] + col), c < C::SB_PIECES ? base + C::SA_BYTES + c * 256 : scratch);
+      dma4(xs + (uint32_t)(sb_src[i] + col), c < C::SB_PIECES ? base + C::SA_BYTES + c * 256 : scratch);
     }
   };
   const uint32_t psel = (uint32_t)g | ((uint32_t)(4 + g) << 8) | ((uint32_t)g << 16) | ((uint32_t)(4 + g) << 24);
@@ -349,6 +348,10 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   };
 
   v4f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   typedef typename AReg<WFMT>::type AR;
   auto load_a = [&](const uint8_t* base, int i) __attribute__((always_inline)) {
@@ -362,9 +365,9 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
       return (AR){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1]};
     }
   };
-  // One K step's MFMAs from LDS stage `stage`.  LDS reads run ahead of the MFMAs: weight
-  // fragments 0 and 1 and all activation fragments first, then fragment i + 2 before the MFMAs
-  // of fragment i, pinned with scheduling barriers.
+  // One K step's MFMAs from LDS stage `stage`.  LDS reads run one weight fragment ahead of the
+  // MFMAs (fragment 0 first, then the activation fragments, then fragment i + 1 before the
+  // MFMAs of fragment i), pinned with scheduling-group barriers.
   // activation rows of this lane are wm 16 FM + 16 j + r: all share row & 15 == r and so the
   // swizzle, leaving one address per half and a constant 2 KiB step per j
   const uint32_t b_lo = (uint32_t)((wm * 16 * FM + r) * 128 + ((g ^ swz(r)) << 4));
@@ -414,143 +417,81 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     }
   };
 
-  // ---- output through bounds-checked buffer stores: every lane issues all FN x FM stores
-  // (8 bytes: 4 consecutive n of one row), those outside [M, N] get an offset past the end of
-  // y and are dropped by the hardware, so the number of stores a wave issues is fixed
-  const __amdgpu_buffer_rsrc_t yrs =
-      __builtin_amdgcn_make_buffer_rsrc((void*)y, (short)0, (int)((int64_t)M * N * 2), 0x00020000);
-  const uint32_t y_end = (uint32_t)((int64_t)M * N * 2);
-  constexpr int NSTORE = FN * FM;
-
   uint32_t sa[FN], sb[FM];
-  int t = blockIdx.x;
-  int n0, m0;
-  tile_origin(t, n0, m0);
-  Src cur;
-  make_src(n0, m0, cur);
-  // scale buffer of group kt4 of the current tile: (gpar + kt4) & 1
-  int gpar = 0;
-  // prologue of the first tile: scales of group 0 and the DMAs of steps 0 .. S-2
-  issue_scales(cur, 0, 0);
+  const int KT4 = (KT + 3) >> 2;
+  const int KT4f = KT >> 2;               // groups of four whole K steps
+  // prologue: scales of group 0 (waited for and read), then the DMAs of steps 0 .. S-2
+  issue_scales(0, 0);
+  wait_vm_barrier<0>();
+  read_scales(0, 0, sa, sb);
 #pragma unroll
-  for (int st = 0; st < S - 1; ++st) issue(cur, min(st, KT - 1), st);
-  bool first = true;
+  for (int st = 0; st < S - 1; ++st) issue(min(st, KT - 1), st);
 
-  while (true) {
-    const int tn_ = t + G;
-    const bool has_next = tn_ < T;
-    int n0n = n0, m0n = m0;
-    if (has_next) tile_origin(tn_, n0n, m0n);
-    const bool pipe = cross && has_next;   // DMAs past this tile's last step fetch the next tile
-
-#pragma unroll
-    for (int i = 0; i < FN; ++i)
-#pragma unroll
-      for (int j = 0; j < FM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-    // One K step of a full group.  At the top, the tiles of step kt have landed once at most
-    // vm_after(q) later memory operations are outstanding (vmcnt retires in issue order) -- at
-    // the first step of a tile that follows another in the pipeline, also the previous tile's
-    // NSTORE output stores; the DMA of step kt + S - 1 then goes to the stage freed by step
-    // kt - 1.  Past the last step it fetches the next tile's first steps, or, with no next
-    // tile, this tile's last step again (unused): the operation count per step never changes.
-    // The first step of a group reads the group's scales and sends the next group's scale DMAs.
-    auto step = [&](int kt, auto qc) __attribute__((always_inline)) {
-      constexpr int Q = decltype(qc)::value;
-      __builtin_amdgcn_sched_barrier(0);
-      if (Q == 0 && kt == 0 && !first) wait_vm_barrier<C::vm_after(0) + NSTORE>();
-      else wait_vm_barrier<C::vm_after(Q)>();
-      if (Q == 0) read_scales(kt >> 2, (gpar + (kt >> 2)) & 1, sa, sb);
-      compute(kt % S, qc, sa, sb, 0, [&]() __attribute__((always_inline)) {
-        const int ka = kt + S - 1;
-        // (the next tile's sources are built only where they are used, keeping them out of
-        // the register budget of the loop)
-        if (ka < KT) {
-          issue(cur, ka, ka % S);
-        } else if (pipe) {
-          Src nx;
-          make_src(n0n, m0n, nx);
-          issue(nx, ka - KT, ka % S);
-        } else {
-          issue(cur, KT - 1, ka % S);
-        }
-        if (Q == 0) {
-          const int g1 = (kt >> 2) + 1;
-          if (g1 < KT4) {
-            issue_scales(cur, g1, (gpar + g1) & 1);
-          } else if (pipe) {
-            Src nx;
-            make_src(n0n, m0n, nx);
-            issue_scales(nx, 0, (gpar + g1) & 1);
-          } else {
-            issue_scales(cur, KT4 - 1, (gpar + g1) & 1);
-          }
-        }
-      });
-    };
-    for (int kt4 = 0; kt4 < KT4f; ++kt4) {
-      step(4 * kt4 + 0, std::integral_constant<int, 0>());
-      step(4 * kt4 + 1, std::integral_constant<int, 1>());
-      step(4 * kt4 + 2, std::integral_constant<int, 2>());
-      step(4 * kt4 + 3, std::integral_constant<int, 3>());
-    }
-    // remainder steps (K / 128 not a multiple of 4): everything waited for, no prefetch
-    for (int kt = 4 * KT4f; kt < KT; ++kt) {
-      wait_vm_barrier<0>();
-      if (kt == 4 * KT4f) read_scales(KT4f, (gpar + KT4f) & 1, sa, sb);
-      compute(kt % S, std::integral_constant<int, -1>(), sa, sb, 8 * (kt & 3), [&]() __attribute__((always_inline)) {
-        if (kt + S - 1 < KT) issue(cur, kt + S - 1, (kt + S - 1) % S);
-      });
-    }
-    if (!pipe) wait_vm_barrier<0>();   // no DMA may still be writing LDS at the tile's end
-    // the nops give the last MFMAs (issued as assembly, so untracked by the compiler's hazard
-    // checks) their result latency before VALU code reads the accumulators; the scheduling
-    // barriers keep every accumulator read below them
+  // One K step of a full group.  At the top, the tiles of step kt have landed once at most
+  // vm_after(q) later memory operations are outstanding (vmcnt retires in issue order); the
+  // DMA of step kt + S - 1 then goes to the stage freed by step kt - 1 (past the last step the
+  // last step is fetched again, unused: the operation count per step never changes).  The
+  // first step of a group reads the group's scales and sends the next group's scale DMAs.
+  auto step = [&](int kt, auto qc) __attribute__((always_inline)) {
+    constexpr int Q = decltype(qc)::value;
     __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_barrier<C::vm_after(Q)>();
+    if (Q == 0 && kt > 0) read_scales(kt >> 2, (kt >> 2) & 1, sa, sb);
+    // this step's DMAs: tile DMAs first, then (first step of a group) the scale DMAs
+    compute(kt % S, qc, sa, sb, 0, [&]() __attribute__((always_inline)) {
+      issue(min(kt + S - 1, KT - 1), (kt + S - 1) % S);
+      if (Q == 0) issue_scales(min((kt >> 2) + 1, KT4 - 1), ((kt >> 2) + 1) & 1);
+    });
+  };
+  for (int kt4 = 0; kt4 < KT4f; ++kt4) {
+    step(4 * kt4 + 0, std::integral_constant<int, 0>());
+    step(4 * kt4 + 1, std::integral_constant<int, 1>());
+    step(4 * kt4 + 2, std::integral_constant<int, 2>());
+    step(4 * kt4 + 3, std::integral_constant<int, 3>());
+  }
+  // remainder steps (K / 128 not a multiple of 4): everything waited for, no prefetch
+  for (int kt = 4 * KT4f; kt < KT; ++kt) {
+    wait_vm_barrier<0>();
+    if (kt == 4 * KT4f && KT4f > 0) read_scales(KT4f, KT4f & 1, sa, sb);
+    compute(kt % S, std::integral_constant<int, -1>(), sa, sb, 8 * (kt & 3), [&]() __attribute__((always_inline)) {
+      if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
+    });
+  }
+  // all DMAs landed and all waves done with the stages before LDS is reused for the output;
+  // the nops give the last MFMAs (issued as assembly, so untracked by the compiler's hazard
+  // checks) their result latency before VALU code reads the accumulators
+  wait_vm_barrier<0>();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 
-    // ---- epilogue: bias, one bf16 rounding, stores straight from the accumulators; the
-    // stores drain while the next tile's first steps (already in flight) are computed.
-    // Lane holds n = 16 (wn FN + i) + 4 g + (0..3) of activation row wm 16 FM + 16 j + r.
+  // ---- epilogue: bias, bf16 rounding, through LDS as a row-major [BM][BN] tile (rows padded
+  // by 16 B so the 8-byte writes of a wave hit distinct banks), then 16-byte coalesced stores.
+  // Lane holds n = 16 (wn FN + i) + 4 g + (0..3) of activation row wm 16 FM + 16 j + r.
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
-      const int n = n0 + wn * 16 * FN + 16 * i + 4 * g;   // n < N: whole fragment in range
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias && n < N) {
+  for (int i = 0; i < FN; ++i) {
+    const int nl = wn * 16 * FN + 16 * i + 4 * g;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias && n0 + nl < N) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) bv[e] = bf16_to_float(bias[n + e]);
-      }
-#pragma unroll
-      for (int j = 0; j < FM; ++j) {
-        const int m = m0 + wm * 16 * FM + 16 * j + r;
-        const v2i o = {(int)pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]),
-                       (int)pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3])};
-        const uint32_t off = (m < M && n < N) ? (uint32_t)(((int64_t)m * N + n) * 2) : y_end;
-        __builtin_amdgcn_raw_buffer_store_b64(o, yrs, (int)off, 0, 0);
-      }
+      for (int e = 0; e < 4; ++e) bv[e] = bf16_to_float(bias[n0 + nl + e]);
     }
-    if (!has_next) break;
-    // next tile: its first steps and group-0 scales are in flight already when pipelined;
-    // otherwise start them now (after every wave is done with this tile's stages)
-    t = tn_;
-    n0 = n0n;
-    m0 = m0n;
-    make_src(n0, m0, cur);
-    if (pipe) {
-      gpar = (gpar + KT4) & 1;
-      first = false;
-    } else {
-      // (every wave passed the barrier above after its last reads of this tile's stages)
-      gpar = 0;
-      first = true;   // the waits below count no stores: the prologue waits for everything
-      issue_scales(cur, 0, 0);
 #pragma unroll
-      for (int st = 0; st < S - 1; ++st) issue(cur, min(st, KT - 1), st);
+    for (int j = 0; j < FM; ++j) {
+      const int ml = wm * 16 * FM + 16 * j + r;
+      const v2i o = {(int)pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]),
+                     (int)pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3])};
+      *(v2i*)(lds + ml * C::OUT_PITCH + nl * 2) = o;
     }
   }
-  // every DMA has landed before the workgroup's LDS is released
-  wait_vm_barrier<0>();
+  __syncthreads();
+  constexpr int ROW_PIECES = C::BN * 2 / 16;          // 16-byte pieces per tile row
+#pragma unroll 4
+  for (int p = tid; p < C::BM * ROW_PIECES; p += C::NW * 64) {
+    const int ml = p / ROW_PIECES, cp = p - ml * ROW_PIECES;
+    const int m = m0 + ml, n = n0 + cp * 8;
+    if (m < M && n < N) *(v4i*)(y + (int64_t)m * N + n) = *(const v4i*)(lds + ml * C::OUT_PITCH + cp * 16);
+  }
 }
 
 template <int WFMT, int FN, int FM, int S>
@@ -558,11 +499,7 @@ static void launch_tile(const uint8_t* xq, const uint8_t* xs, int M, int K, cons
                         int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s) {
   using C = TileCfg<WFMT, FN, FM, S>;
   const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
-  // persistent grid: one workgroup per CU (the LDS footprint allows no second), a multiple of
-  // the 8 XCDs so that a workgroup's tiles all map to its own XCD
-  const int T = tm * tn;
-  const int grid = T < 256 ? T : 256;
-  hipLaunchKernelGGL((k_gemm_tile<WFMT, FN, FM, S>), dim3((unsigned)grid), dim3(512), 0, s,
+  hipLaunchKernelGGL((k_gemm_tile<WFMT, FN, FM, S>), dim3((unsigned)(tm * tn)), dim3(512), 0, s,
                      xq, xs, M, K, packed, N, bias, y, tm, tn, group_m);
 }
 

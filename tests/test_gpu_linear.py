@@ -242,18 +242,17 @@ def test_decode_prequant_matches_fused(M):
 
 @pytest.mark.parametrize("fmt", [0, 2])
 @pytest.mark.parametrize("K", [640, 1024])
-def test_tiled_kernel_persistent(K, fmt):
-    """More tiles than workgroups (289 tiles of 128 x 128 on a 256-workgroup persistent grid),
-    ragged M and N: workgroups that run a second tile, with the K pipeline running on from one
-    tile into the next (K % 512 == 0) or restarting per tile (K = 640)."""
+def test_tiled_kernel_many_tiles(K, fmt):
+    """More tiles than CUs (289 tiles of 128 x 128), ragged M and N, K with and without whole
+    groups of four K steps."""
     g = np.random.default_rng(K + fmt)
     M, N = 2100, 2080
     x = synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32))
     w = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
     b = synth.bf16_bits((g.standard_normal(N) * 0.01).astype(np.float32))
-    banner("tiled persistent", M, N, K, FMTS[fmt])
+    banner("tiled many tiles", M, N, K, FMTS[fmt])
     mxfp8.set_tile_config(4, 2)
     try:
-        _full_check(x, w, fmt, b, name="persistent-%d-%d" % (K, fmt))
+        _full_check(x, w, fmt, b, name="many-tiles-%d-%d" % (K, fmt))
     finally:
         mxfp8.set_tile_config(0, 0)

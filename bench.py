@@ -21,6 +21,8 @@ Also measured and printed in the same JSON line:
                 run in a separate process (oracle/cpu_bench.py).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --only gemm --steps K   (the GEMM alone, for rocprofv3 --pmc passes)
+       python bench.py --only copy             (1 GiB device copy x 3: counter calibration)
 """
 import argparse
 import hashlib
@@ -65,6 +67,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["all", "gemm", "copy"], default="all",
+                    help="counter runs: 'gemm' launches only the prefill GEMM (pre-quantized "
+                         "entry) --steps times; 'copy' copies a 1 GiB device buffer 3 times, the "
+                         "calibration of the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -78,6 +84,15 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    if args.only == "copy":
+        src = torch.full((1 << 30,), 3, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copied_bytes_per_launch": 1 << 30, "launches": 3}))
+        return
+
     # ------------------------------------------------------------ prefill workload
     M, N, K = 4096, 14336, 4096
     d = synth.make("prefill")
@@ -86,6 +101,14 @@ def main():
     wq, ws = mxfp8.quantize_weight(w0, "e4m3")
     packed0 = mxfp8.prepack_weight(wq, ws, "e4m3")
     del w0, wq, ws
+    if args.only == "gemm":
+        xq, xsc = mxfp8.quantize_act(x0)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        for _ in range(args.steps):
+            mxfp8.linear_prequant(xq, xsc, packed0, N, "e4m3", out=y)
+        torch.cuda.synchronize()
+        print(json.dumps({"gemm_launches": args.steps, "M": M, "N": N, "K": K}))
+        return
     set_bytes = x0.numel() * 2 + packed0.numel() + M * N * 2
     R = max(2, -(-2 * MALL_BYTES // set_bytes))
     xs_ = [x0] + [x0.clone() for _ in range(R - 1)]

@@ -536,7 +536,12 @@ static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int 
   else if (c.fn == 7 && c.fm == 4) launch_tile<WFMT, 7, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
   else if (c.fn == 6 && c.fm == 4) launch_tile<WFMT, 6, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
   else if (c.fn == 4 && c.fm == 4) launch_tile<WFMT, 4, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
-  else launch_tile<WFMT, 4, 2, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  else if ((long)((N + 127) / 128) * ((M + 127) / 128) <= 256)
+    // one tile per CU at most: each workgroup runs the whole K of its tile, where a third LDS
+    // stage (deeper prefetch) pays off
+    launch_tile<WFMT, 4, 2, 3>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  else
+    launch_tile<WFMT, 4, 2, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
   return hipGetLastError();
 }
 

@@ -198,11 +198,13 @@ def test_tiled_kernel_every_tile(fn, fm, fmt):
         mxfp8.set_tile_config(0, 0)
 
 
-# Small-M (decode) path: one launch with the activation quantizer fused into the GEMM and K
-# split over the 8 waves of a workgroup.  K values give idle waves (K = 384), partial 4-step
-# groups (K = 640, 1152) and a wave with two groups, the second partial (K = 4224).
-SMALL = [(1, 16, 128), (5, 48, 384), (16, 272, 640), (17, 64, 512), (31, 80, 4224),
-         (32, 32, 1152)]
+# Small-M (decode) paths.  M <= 16: one launch with the activation quantizer fused into the
+# GEMM and K split over the 8 waves of a workgroup; K values give idle waves (K = 384), partial
+# 4-step groups (K = 640, 1152, 3968) and a wave with two groups, the second partial (K = 4224).
+# 16 < M <= 32: the activation quantizer kernel, then the same small-M kernel on the quantized
+# activations (two 16-row tiles).
+SMALL = [(1, 16, 128), (5, 48, 384), (16, 272, 640), (15, 80, 4224), (17, 64, 512),
+         (31, 80, 3968), (32, 32, 1152), (24, 48, 4096), (32, 4096, 4096)]
 
 
 def _small_inputs(M, N, K, seed):
@@ -224,7 +226,7 @@ def test_small_m_fused(M, N, K, fmt):
     banner("linear small-M", M, N, K, FMTS[fmt])
     y, layer = _full_check(x, w, fmt, b, name="small-%d-%d-%d-%d" % (M, N, K, fmt))
     # the pre-quantized entry runs the same kernel with the same summation order, so feeding
-    # it the oracle's quantization of x must reproduce the fused quantizer's result bit for bit
+    # it the oracle's quantization of x must reproduce the bf16 entry's result bit for bit
     xq, xs = orc.quantize(x, orc.E4M3)
     y2 = layer.apply_quantized(u8_dev(xq), u8_dev(xs))
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))

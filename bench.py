@@ -17,6 +17,10 @@ Also measured and printed in the same JSON line:
   decode        the decode workload (x [M, 4096], M in {1, 8, 32}, weight [4096, 4096], bias),
                 one fused call each, replayed from a HIP graph over 32 rotated weight copies:
                 time per call, algorithmic bytes / time against 8 TB/s;
+  other_workloads  outlier activations on the pre-quantized entry (2048 x 6144 x 4096, GEMM
+                only), MXFP6 weights (E2M3 and E3M2, 512 x 8192 x 8192, activation quantization
+                included), each over enough rotated sets to exceed the Infinity Cache; and the
+                latency of one tiny call (16 x 256 x 512) from a HIP graph;
   cpu_baseline  the CPU oracle on a bounded sample of the prefill workload (host cores),
                 run in a separate process (oracle/cpu_bench.py).
 
@@ -66,6 +70,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the outlier, MXFP6 and tiny workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", choices=["all", "gemm", "copy"], default="all",
                     help="counter runs: 'gemm' launches only the prefill GEMM (pre-quantized "
@@ -216,6 +222,103 @@ def main():
             del g
         del pks, pk
 
+    # ------------------------------------------------------------ the other workloads
+    others = None
+    if not args.no_others:
+        torch.cuda.empty_cache()
+        others = {}
+
+        def bf16_dev(bits):
+            return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        def rotated(make_set, set_bytes):
+            n = max(2, -(-2 * MALL_BYTES // set_bytes))
+            return [make_set(j) for j in range(n)]
+
+        def time_calls(fn, n_sets, iters):
+            for j in range(n_sets):
+                fn(j)
+            torch.cuda.synchronize()
+            stream = torch.cuda.current_stream(dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(iters):
+                fn(i % n_sets)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / iters
+
+        # outlier activations on the pre-quantized entry (GEMM only), fused-QKV shape
+        do = synth.make("outlier")
+        Mo, No, Ko = do["M"], do["N"], do["K"]
+        xq_o, xs_o = mxfp8.quantize_act(bf16_dev(do["x"]))
+        wq, ws = mxfp8.quantize_weight(bf16_dev(do["w"]), "e4m3")
+        pk_o = mxfp8.prepack_weight(wq, ws, "e4m3")
+        del wq, ws
+        sets = rotated(lambda j: (xq_o.clone(), xs_o.clone(), pk_o.clone(),
+                                  torch.empty((Mo, No), dtype=torch.bfloat16, device=dev)),
+                       xq_o.numel() + xs_o.numel() + pk_o.numel() + Mo * No * 2)
+        us = time_calls(lambda j: mxfp8.linear_prequant(sets[j][0], sets[j][1], sets[j][2], No,
+                                                        "e4m3", out=sets[j][3]),
+                        len(sets), max(50, args.steps))
+        fl = 2.0 * Mo * No * Ko
+        others["outlier_prequant_2048x6144x4096"] = {
+            "us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
+            "mfma_frac": round(fl / us / 1e6 / PEAK_FP8_TFLOPS, 4), "rotated_sets": len(sets)}
+        del sets, xq_o, xs_o, pk_o
+        torch.cuda.empty_cache()
+
+        # MXFP6 weights (E2M3, E3M2), bf16 activations quantized to MXFP8 inside the call
+        dm = synth.make("mxfp6")
+        Mf, Nf, Kf = dm["M"], dm["N"], dm["K"]
+        xf = bf16_dev(dm["x"])
+        wf = bf16_dev(dm["w"])
+        for fname in ("e2m3", "e3m2"):
+            wq, ws = mxfp8.quantize_weight(wf, fname)
+            pk_f = mxfp8.prepack_weight(wq, ws, fname)
+            del wq, ws
+            sets = rotated(lambda j: (xf.clone(), pk_f.clone(),
+                                      torch.empty((Mf, Nf), dtype=torch.bfloat16, device=dev)),
+                           xf.numel() * 2 + pk_f.numel() + Mf * Nf * 2)
+            wsf = torch.empty(mxfp8.workspace_bytes(Mf, Nf, Kf, fname), dtype=torch.uint8, device=dev)
+            us = time_calls(lambda j: mxfp8.linear(sets[j][0], sets[j][1], Nf, fname,
+                                                   out=sets[j][2], workspace=wsf),
+                            len(sets), max(50, args.steps))
+            fl = 2.0 * Mf * Nf * Kf
+            others["mxfp6_%s_512x8192x8192" % fname] = {
+                "us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
+                "mfma_frac_fp8_rate": round(fl / us / 1e6 / PEAK_FP8_TFLOPS, 4),
+                "rotated_sets": len(sets)}
+            del sets, pk_f, wsf
+        del xf, wf
+        torch.cuda.empty_cache()
+
+        # tiny: latency of one call (HIP graph of 64 calls)
+        dt = synth.make("tiny")
+        xt = bf16_dev(dt["x"])
+        wq, ws = mxfp8.quantize_weight(bf16_dev(dt["w"]), "e4m3")
+        pk_t = mxfp8.prepack_weight(wq, ws, "e4m3")
+        yt = torch.empty((dt["M"], dt["N"]), dtype=torch.bfloat16, device=dev)
+        wst = torch.empty(max(1, mxfp8.workspace_bytes(dt["M"], dt["N"], dt["K"])), dtype=torch.uint8, device=dev)
+        st = torch.cuda.Stream(dev)
+        st.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(st):
+            mxfp8.linear(xt, pk_t, dt["N"], "e4m3", out=yt, workspace=wst)
+        torch.cuda.current_stream(dev).wait_stream(st)
+        torch.cuda.synchronize()
+        gt = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gt, stream=st):
+            for _ in range(64):
+                mxfp8.linear(xt, pk_t, dt["N"], "e4m3", out=yt, workspace=wst)
+        gt.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            gt.replay()
+        torch.cuda.synchronize()
+        others["tiny_16x256x512_us_per_call"] = round((time.perf_counter() - t0) * 1e6 / (20 * 64), 3)
+        del gt, xt, pk_t, yt, wst
+
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
@@ -244,6 +347,7 @@ def main():
         "quantizer": {"us": round(quant_us, 2), "GB/s": round(quant_bytes / (quant_us * 1e-6) / 1e9, 1),
                       "hbm_frac": round(quant_bytes / (quant_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
         "decode": decode,
+        "other_workloads": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))

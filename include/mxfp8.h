@@ -102,6 +102,21 @@ int mxfp8_prepack_weight(const void* wq, int64_t ldw_bytes, const void* ws, int6
 int mxfp8_unpack_weight(const void* packed, int64_t N, int64_t K, int fmt,
                         void* wq, void* ws, void* stream);
 
+/* Import of a weight stored in the aiter_flydsl page's (16, 16) preshuffled layout (E4M3
+ * only; aiter_flydsl page, process_weights_after_loading / row_major_weight: the logical byte
+ * array [N/16, 16, K/32, 2, 16] of W [N, K] is stored as [N/16, K/32, 2, 16, 16], i.e. byte
+ * W[16 n0 + n1][32 k0 + 16 k1 + k2] at ((((n0 K/32 + k0) 2 + k1) 16 + n1) 16 + k2)).
+ *   w16          N x K bytes in that order
+ *   ws           E8M0, row stride ld_ws >= K/32 (as for mxfp8_prepack_weight)
+ *   packed [16]  out: the same bytes mxfp8_prepack_weight writes for the row-major weight */
+int mxfp8_prepack_weight_shuffled16(const void* w16, const void* ws, int64_t ld_ws, int64_t N,
+                                    int64_t K, void* packed, void* stream);
+
+/* Export of a prepacked E4M3 weight to that preshuffled layout: w16 (N x K bytes) and
+ * ws [N, K/32] row-major.  Exact inverse of mxfp8_prepack_weight_shuffled16. */
+int mxfp8_unpack_weight_shuffled16(const void* packed, int64_t N, int64_t K, void* w16,
+                                   void* ws, void* stream);
+
 /* ---------------------------------------------------------------- the linear layer */
 
 /* Workspace bytes mxfp8_linear needs for (M, N, K, fmt) (0 when none is needed).
@@ -128,7 +143,15 @@ int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K,
                           const void* packed, int64_t N, int fmt, const void* bias, void* y,
                           void* stream);
 
-/* ---------------------------------------------------------------- tuning */
+/* ---------------------------------------------------------------- modes and tuning */
+
+/* Batch-invariant mode (aiter_flydsl page, is_supported: its split-K kernel is not batch
+ * invariant).  on != 0: every M runs on kernels that add the K steps of an output in
+ * sequence, so a row's result does not depend on how many rows the call has (the small-M
+ * kernels, which split K over waves, are not used).  on == 0 (default): fastest kernel per
+ * shape.  Process-wide; not for use while other threads are launching.  Returns MX_OK. */
+int mxfp8_set_batch_invariant(int on);
+
 
 /* Tuning / testing hook: force the tile of the LDS-tiled GEMM used for large M (fn, fm =
  * 16-row weight fragments and 16-row activation groups per wave; the workgroup of 8 waves

@@ -165,6 +165,31 @@ int mxfp8_unpack_weight(const void* packed, int64_t N, int64_t K, int fmt, void*
                     "unpack launch");
 }
 
+int mxfp8_prepack_weight_shuffled16(const void* w16, const void* ws, int64_t ld_ws, int64_t N,
+                                    int64_t K, void* packed, void* stream) {
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (!w16 || !ws || !packed) return fail(MX_EINVAL, "null pointer (w16, ws or packed)");
+  if (ld_ws < K / 32) return fail(MX_ESHAPE, "ld_ws = %lld < K/32 = %lld", (long long)ld_ws, (long long)(K / 32));
+  if (!aligned16(packed)) return fail(MX_EALIGN, "packed must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  return hip_status(mx::launch_prepack_shuffled16((const uint8_t*)w16, (const uint8_t*)ws, ld_ws,
+                                                  N, K, (uint8_t*)packed, (hipStream_t)stream),
+                    "prepack (shuffled16) launch");
+}
+
+int mxfp8_unpack_weight_shuffled16(const void* packed, int64_t N, int64_t K, void* w16, void* ws,
+                                   void* stream) {
+  int rc = check_nk(N, K);
+  if (rc) return rc;
+  if (!w16 || !ws || !packed) return fail(MX_EINVAL, "null pointer (packed, w16 or ws)");
+  if (!aligned16(packed)) return fail(MX_EALIGN, "packed must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  return hip_status(mx::launch_unpack_shuffled16((const uint8_t*)packed, N, K, (uint8_t*)w16,
+                                                 (uint8_t*)ws, (hipStream_t)stream),
+                    "unpack (shuffled16) launch");
+}
+
 int64_t mxfp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
   if (!valid_fmt(fmt) || check_mk(M, K) || check_nk(N, K)) return 0;
   if (M == 0) return 0;
@@ -197,7 +222,7 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, i
   if (!aligned16(workspace)) return fail(MX_EALIGN, "workspace must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
   hipStream_t s = (hipStream_t)stream;
-  if (mx::small_m_fused(M, K))   // decode shapes: quantization fused into the GEMM launch
+  if (!mx::batch_invariant() && mx::small_m_fused(M, K))   // decode: quantizer fused in
     return hip_status(mx::launch_linear_small_m(x_bf16, nullptr, false, M, K,
                                                 (const uint8_t*)packed, N, fmt,
                                                 (const uint16_t*)bias, (uint16_t*)y, s),
@@ -223,6 +248,11 @@ int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K, 
                                     (const uint8_t*)packed, N, fmt, (const uint16_t*)bias,
                                     (uint16_t*)y, (hipStream_t)stream),
                     "gemm launch");
+}
+
+int mxfp8_set_batch_invariant(int on) {
+  mx::set_batch_invariant(on != 0);
+  return ok();
 }
 
 int mxfp8_set_tile_config(int fn, int fm) {

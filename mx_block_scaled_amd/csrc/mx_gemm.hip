@@ -509,6 +509,9 @@ struct TileChoice { int fn, fm; };
 // compiled tiles (fn, fm) -> workgroup tile 32 fn x 64 fm, two LDS stages
 static std::atomic<int> g_force_tile{0};   // fn * 16 + fm, 0 = automatic
 void force_tile(int fn, int fm) { g_force_tile.store(fn * 16 + fm); }
+static std::atomic<bool> g_batch_invariant{false};
+void set_batch_invariant(bool on) { g_batch_invariant.store(on); }
+bool batch_invariant() { return g_batch_invariant.load(std::memory_order_relaxed); }
 static TileChoice choose_tile(int M, int N) {
   const int f = g_force_tile.load(std::memory_order_relaxed);
   if (f) return TileChoice{f / 16, f % 16};
@@ -548,7 +551,9 @@ static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
                        uint16_t* y, hipStream_t s) {
-  if (small_m_quantized(M, K))
+  // the small-M kernel splits K over waves (a different summation order); batch-invariant
+  // mode keeps every M on the kernels that add the K steps in sequence
+  if (!batch_invariant() && small_m_quantized(M, K))
     return launch_linear_small_m(xq, xs, true, M, K, packed, N, fmt, bias, y, s);
   const int m = (int)M, k = (int)K, n = (int)N;
   const bool tiled = (K % 128 == 0) && (((uintptr_t)xs & 3) == 0) && M >= 64 && N >= 128;

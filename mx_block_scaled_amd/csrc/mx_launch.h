@@ -24,8 +24,17 @@ hipError_t launch_prepack(const uint8_t* wq, int64_t ldw, const uint8_t* ws, int
 hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int fmt, uint8_t* wq,
                          uint8_t* ws, hipStream_t s);
 
+// The same rearrangement from / to the aiter_flydsl page's (16, 16) preshuffled E4M3 layout.
+hipError_t launch_prepack_shuffled16(const uint8_t* w16, const uint8_t* ws, int64_t ld_ws,
+                                     int64_t N, int64_t K, uint8_t* packed, hipStream_t s);
+hipError_t launch_unpack_shuffled16(const uint8_t* packed, int64_t N, int64_t K, uint8_t* w16,
+                                    uint8_t* ws, hipStream_t s);
+
 // Force the tiled GEMM's tile (fragments per wave along n and m); (0, 0) = automatic.
 void force_tile(int fn, int fm);
+// Batch-invariant mode: no small-M (split-K) kernels, so a row's result does not depend on M.
+void set_batch_invariant(bool on);
+bool batch_invariant();
 
 // GEMM from quantized activations xq [M, K] + xs [M, K/32] (row-major).
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,

@@ -32,8 +32,18 @@ PackGeom pack_geom(int64_t N, int64_t K, int fmt) {
   return p;
 }
 
+// Byte offset of W[row][k] in the source (PACK) or destination (unpack) weight:
+//   row-major with row stride ldw, or (SHUF) the aiter_flydsl page's (16, 16) preshuffled E4M3
+//   layout, which stores the logical [N/16, 16, K/32, 2, 16] array as [N/16, K/32, 2, 16, 16]
+//   (aiter_flydsl page, row_major_weight).
+template <bool SHUF>
+__device__ __forceinline__ int64_t w_offset(int64_t row, int64_t k, int64_t ldw, int64_t KB) {
+  if (!SHUF) return row * ldw + k;
+  return ((((row >> 4) * KB + (k >> 5)) * 2 + ((k >> 4) & 1)) * 16 + (row & 15)) * 16 + (k & 15);
+}
+
 // one thread per (fragment, lane); byte-granular copies (load-time only, any stride)
-template <int FMT, bool PACK>
+template <int FMT, bool PACK, bool SHUF = false>
 __global__ __launch_bounds__(256) void k_pack(uint8_t* __restrict__ wq, int64_t ldw,
                                               uint8_t* __restrict__ ws, int64_t ld_ws, int64_t N,
                                               int64_t K, uint8_t* __restrict__ packed) {
@@ -53,8 +63,8 @@ __global__ __launch_bounds__(256) void k_pack(uint8_t* __restrict__ wq, int64_t 
         const int64_t k = 128 * kt + 64 * h + 16 * g;
         uint8_t* d = fr + h * 1024 + l * 16;
         for (int j = 0; j < 16; ++j) {
-          if (PACK) d[j] = (k + j < K) ? wq[row * ldw + k + j] : 0;
-          else if (k + j < K) wq[row * ldw + k + j] = d[j];
+          if (PACK) d[j] = (k + j < K) ? wq[w_offset<SHUF>(row, k + j, ldw, KB)] : 0;
+          else if (k + j < K) wq[w_offset<SHUF>(row, k + j, ldw, KB)] = d[j];
         }
       }
     } else {
@@ -83,7 +93,7 @@ __global__ void k_pack_scale_tail(uint8_t* __restrict__ sreg, int64_t NG, int64_
   }
 }
 
-template <bool PACK>
+template <bool PACK, bool SHUF = false>
 static hipError_t launch_pack(const uint8_t* wq, int64_t ldw, const uint8_t* ws, int64_t ld_ws,
                               int64_t N, int64_t K, int fmt, uint8_t* packed, hipStream_t s) {
   const PackGeom p = pack_geom(N, K, fmt);
@@ -93,11 +103,16 @@ static hipError_t launch_pack(const uint8_t* wq, int64_t ldw, const uint8_t* ws,
   dim3 grid((unsigned)blocks), block(256);
   uint8_t* w = const_cast<uint8_t*>(wq);
   uint8_t* sc = const_cast<uint8_t*>(ws);
-  switch (fmt) {
-    case 0: hipLaunchKernelGGL((k_pack<0, PACK>), grid, block, 0, s, w, ldw, sc, ld_ws, N, K, packed); break;
-    case 2: hipLaunchKernelGGL((k_pack<2, PACK>), grid, block, 0, s, w, ldw, sc, ld_ws, N, K, packed); break;
-    case 3: hipLaunchKernelGGL((k_pack<3, PACK>), grid, block, 0, s, w, ldw, sc, ld_ws, N, K, packed); break;
-    default: return hipErrorInvalidValue;
+  if (SHUF) {   // the preshuffled layout is defined for 1-byte (E4M3) elements only
+    if (fmt != 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_pack<0, PACK, true>), grid, block, 0, s, w, ldw, sc, ld_ws, N, K, packed);
+  } else {
+    switch (fmt) {
+      case 0: hipLaunchKernelGGL((k_pack<0, PACK>), grid, block, 0, s, w, ldw, sc, ld_ws, N, K, packed); break;
+      case 2: hipLaunchKernelGGL((k_pack<2, PACK>), grid, block, 0, s, w, ldw, sc, ld_ws, N, K, packed); break;
+      case 3: hipLaunchKernelGGL((k_pack<3, PACK>), grid, block, 0, s, w, ldw, sc, ld_ws, N, K, packed); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -120,6 +135,16 @@ hipError_t launch_unpack(const uint8_t* packed, int64_t N, int64_t K, int fmt, u
                          uint8_t* ws, hipStream_t s) {
   const int64_t ldw = fmt == 0 ? K : K / 4 * 3;
   return launch_pack<false>(wq, ldw, ws, K / 32, N, K, fmt, const_cast<uint8_t*>(packed), s);
+}
+
+hipError_t launch_prepack_shuffled16(const uint8_t* w16, const uint8_t* ws, int64_t ld_ws,
+                                     int64_t N, int64_t K, uint8_t* packed, hipStream_t s) {
+  return launch_pack<true, true>(w16, K, ws, ld_ws, N, K, 0, packed, s);
+}
+
+hipError_t launch_unpack_shuffled16(const uint8_t* packed, int64_t N, int64_t K, uint8_t* w16,
+                                    uint8_t* ws, hipStream_t s) {
+  return launch_pack<false, true>(w16, K, ws, K / 32, N, K, 0, const_cast<uint8_t*>(packed), s);
 }
 
 }  // namespace mx

@@ -18,7 +18,8 @@ import torch  # loaded first: libmxfp8 then binds to the HIP runtime torch alrea
 __all__ = [
     "FMT", "MXError", "lib", "library_path", "device_supported", "quantize_act",
     "quantize_weight", "prepack_weight", "unpack_weight", "prepacked_bytes", "workspace_bytes",
-    "linear", "linear_prequant", "MxLinear", "set_tile_config",
+    "linear", "linear_prequant", "MxLinear", "set_tile_config", "set_batch_invariant",
+    "prepack_weight_shuffled16", "unpack_weight_shuffled16",
 ]
 
 FMT = {"e4m3": 0, "e2m3": 2, "e3m2": 3}
@@ -56,6 +57,9 @@ def lib():
             "mxfp8_linear": (I, [P, I64, I64, P, I64, I, P, P, P, I64, P]),
             "mxfp8_linear_prequant": (I, [P, P, I64, I64, P, I64, I, P, P, P]),
             "mxfp8_set_tile_config": (I, [I, I]),
+            "mxfp8_set_batch_invariant": (I, [I]),
+            "mxfp8_prepack_weight_shuffled16": (I, [P, P, I64, I64, I64, P, P]),
+            "mxfp8_unpack_weight_shuffled16": (I, [P, I64, I64, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -96,6 +100,11 @@ def _stream(t):
 def set_tile_config(fn=0, fm=0):
     """Force the tiled GEMM's tile (tuning/testing); (0, 0) = automatic."""
     _check(lib().mxfp8_set_tile_config(int(fn), int(fm)))
+
+
+def set_batch_invariant(on=True):
+    """Batch-invariant mode: a row's result no longer depends on the number of rows M."""
+    _check(lib().mxfp8_set_batch_invariant(1 if on else 0))
 
 
 def device_supported(device=0):
@@ -151,6 +160,32 @@ def prepack_weight(wq, ws, fmt="e4m3", K=None):
     _check(lib().mxfp8_prepack_weight(wq.data_ptr(), wq.stride(0), ws.data_ptr(), ws.stride(0),
                                       N, K, f, out.data_ptr(), _stream(wq)))
     return out
+
+
+def prepack_weight_shuffled16(w16, ws, N, K):
+    """E4M3 weight in the aiter (16, 16) preshuffled order (N * K bytes) + scales -> prepacked."""
+    w16 = _u8(w16, "w16")
+    if w16.numel() != N * K:
+        raise ValueError("w16 must hold N * K = %d bytes" % (N * K))
+    if ws.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not ws.is_cuda:
+        raise TypeError("ws must be uint8 / float8_e8m0fnu on the GPU")
+    ws = ws.view(torch.uint8)
+    if ws.stride(-1) != 1:
+        raise ValueError("ws rows must be contiguous")
+    out = torch.empty(prepacked_bytes(N, K, 0), dtype=torch.uint8, device=w16.device)
+    _check(lib().mxfp8_prepack_weight_shuffled16(w16.data_ptr(), ws.data_ptr(), ws.stride(0), N, K,
+                                                 out.data_ptr(), _stream(w16)))
+    return out
+
+
+def unpack_weight_shuffled16(packed, N, K):
+    """Prepacked E4M3 weight -> (w16 uint8 [N * K] in the aiter (16, 16) order, ws [N, K/32])."""
+    packed = _u8(packed, "packed")
+    w16 = torch.empty(N * K, dtype=torch.uint8, device=packed.device)
+    ws = torch.empty((N, K // 32), dtype=torch.uint8, device=packed.device)
+    _check(lib().mxfp8_unpack_weight_shuffled16(packed.data_ptr(), N, K, w16.data_ptr(),
+                                                ws.data_ptr(), _stream(packed)))
+    return w16, ws
 
 
 def unpack_weight(packed, N, K, fmt="e4m3"):

@@ -112,6 +112,17 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     importlib.reload(mxfp8)
 
 
+def test_shuffled16_and_mode_validation(L):
+    assert L.mxfp8_prepack_weight_shuffled16(A, B, 16, 250, 512, B, None) == MX_ESHAPE   # N % 16
+    assert L.mxfp8_prepack_weight_shuffled16(A, B, 8, 256, 512, B, None) == MX_ESHAPE    # ld_ws
+    assert L.mxfp8_prepack_weight_shuffled16(None, B, 16, 256, 512, B, None) == MX_EINVAL
+    assert L.mxfp8_prepack_weight_shuffled16(A, B, 16, 256, 512, B + 4, None) == MX_EALIGN
+    assert L.mxfp8_unpack_weight_shuffled16(B, 256, 500, A, A, None) == MX_ESHAPE         # K % 32
+    assert L.mxfp8_unpack_weight_shuffled16(B + 8, 256, 512, A, A, None) == MX_EALIGN
+    assert L.mxfp8_set_batch_invariant(1) == MX_OK
+    assert L.mxfp8_set_batch_invariant(0) == MX_OK
+
+
 def test_tile_config_hook(L):
     assert L.mxfp8_set_tile_config(3, 3) == MX_EINVAL
     assert L.mxfp8_set_tile_config(0, 0) == MX_OK

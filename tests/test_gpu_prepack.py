@@ -40,3 +40,22 @@ def test_strided_sources():
     wq2, ws2 = mxfp8.unpack_weight(p, N, K, 0)
     assert np.array_equal(host_u8(wq2), wq_big[:, :K])
     assert np.array_equal(host_u8(ws2), ws_big[:N, :K // 32])
+
+
+@pytest.mark.parametrize("N,K", [(16, 32), (48, 160), (256, 544), (4096, 4096)])
+def test_shuffled16_import_export(N, K):
+    """Weights in the aiter_flydsl page's (16, 16) preshuffled order (produced here by the
+    oracle's shuffle, itself pinned to the page's row_major_weight inverse) prepack to exactly
+    the bytes of the row-major prepack, and export back to that order."""
+    import oracle as orc
+    g = np.random.default_rng(3 * N + K)
+    wq = g.integers(0, 256, (N, K)).astype(np.uint8)
+    ws = g.integers(0, 255, (N, K // 32)).astype(np.uint8)
+    w16 = orc.shuffle16(wq)
+    banner("shuffled16 import/export", N, K)
+    p_row = mxfp8.prepack_weight(u8_dev(wq), u8_dev(ws), 0)
+    p_shuf = mxfp8.prepack_weight_shuffled16(u8_dev(w16.reshape(-1)), u8_dev(ws), N, K)
+    assert torch.equal(p_row, p_shuf)
+    w16b, ws2 = mxfp8.unpack_weight_shuffled16(p_row, N, K)
+    assert np.array_equal(host_u8(w16b), w16.reshape(-1))
+    assert np.array_equal(host_u8(ws2), ws)

@@ -219,6 +219,29 @@ def main():
                 "us_per_call": round(us, 3), "TFLOP/s": round(2.0 * Md * Nd * Kd / (us * 1e-6) / 1e12, 3),
                 "algorithmic_bytes": bytes_alg, "GB/s": round(gbs, 1),
                 "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+            # the same calls in batch-invariant mode (no split-K kernels)
+            mxfp8.set_batch_invariant(True)
+            try:
+                with torch.cuda.stream(s):
+                    for j in range(RD):
+                        mxfp8.linear(xd, pks[j], Nd, "e4m3", bias, out=yd, workspace=wsd)
+                torch.cuda.current_stream(dev).wait_stream(s)
+                torch.cuda.synchronize()
+                gi = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gi, stream=s):
+                    for j in range(RD):
+                        mxfp8.linear(xd, pks[j], Nd, "e4m3", bias, out=yd, workspace=wsd)
+                gi.replay()
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                for _ in range(reps):
+                    gi.replay()
+                torch.cuda.synchronize()
+                decode["M%d" % Md]["batch_invariant_us_per_call"] = round(
+                    (time.perf_counter() - t0) * 1e6 / (reps * RD), 3)
+                del gi
+            finally:
+                mxfp8.set_batch_invariant(False)
             del g
         del pks, pk
 
@@ -318,6 +341,32 @@ def main():
         torch.cuda.synchronize()
         others["tiny_16x256x512_us_per_call"] = round((time.perf_counter() - t0) * 1e6 / (20 * 64), 3)
         del gt, xt, pk_t, yt, wst
+
+        # batched layer: 8 independent 512 x 4096 x 4096 layers in one call vs 8 calls
+        Bb, Mb, Nb, Kb = 8, 512, 4096, 4096
+        gb = torch.Generator(device=dev)
+        gb.manual_seed(0)
+        xb = torch.randn((Bb, Mb, Kb), generator=gb, device=dev).to(torch.bfloat16)
+        pks = []
+        for _ in range(Bb):
+            wq, ws = mxfp8.quantize_weight(
+                (torch.randn((Nb, Kb), generator=gb, device=dev) * 0.02).to(torch.bfloat16), "e4m3")
+            pks.append(mxfp8.prepack_weight(wq, ws, "e4m3"))
+        pkb = torch.cat(pks)
+        del pks, wq, ws
+        yb = torch.empty((Bb, Mb, Nb), dtype=torch.bfloat16, device=dev)
+        wsb2 = torch.empty(mxfp8.workspace_bytes(Bb * Mb, Nb, Kb), dtype=torch.uint8, device=dev)
+        P = mxfp8.prepacked_bytes(Nb, Kb)
+        us_b = time_calls(lambda j: mxfp8.linear_batched(xb, pkb, Nb, "e4m3", out=yb, workspace=wsb2),
+                          1, max(20, args.steps // 4))
+        us_s = time_calls(lambda j: [mxfp8.linear(xb[b], pkb[b * P:(b + 1) * P], Nb, "e4m3",
+                                                  out=yb[b], workspace=wsb2) for b in range(Bb)],
+                          1, max(20, args.steps // 4))
+        fl = 2.0 * Bb * Mb * Nb * Kb
+        others["batched_8x512x4096x4096"] = {
+            "us": round(us_b, 2), "TFLOP/s": round(fl / us_b / 1e6, 1),
+            "us_as_8_separate_calls": round(us_s, 2)}
+        del xb, pkb, yb, wsb2
 
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None

@@ -143,6 +143,27 @@ int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K,
                           const void* packed, int64_t N, int fmt, const void* bias, void* y,
                           void* stream);
 
+/* Batched layer (Mxfp8LinearKernel page, Mxfp8LinearLayerConfig.bmm_batch_size; the
+ * aiter_flydsl page's can_implement turns such layers away): for every b < B,
+ *     y[b] = dequant(quantize(x[b])) . dequant(W[b])^T (+ bias[b])
+ * with the same kernels, hence the same results, as B separate mxfp8_linear calls.
+ *   x_bf16    [16]  bf16 [B, M, K], contiguous
+ *   packed    [16]  B prepacked weights back to back, mxfp8_prepacked_bytes(N, K, fmt) each
+ *   bias            bf16 [B, N] or NULL
+ *   y         [16]  out: bf16 [B, M, N]
+ *   workspace [16]  ws_bytes >= mxfp8_workspace_bytes(B * M, N, K, fmt)
+ * 0 <= B <= 65535; B * M obeys the limits on M; B == 0 or M == 0 is a no-op. */
+int mxfp8_linear_batched(const void* x_bf16, int64_t B, int64_t M, int64_t K, const void* packed,
+                         int64_t N, int fmt, const void* bias, void* y, void* workspace,
+                         int64_t ws_bytes, void* stream);
+
+/* The batched layer from pre-quantized activations: xq [B, M, K] E4M3 [16], xs [B, M, K/32]
+ * E8M0 (row-major per batch, contiguous); other arguments as mxfp8_linear_batched.  Needs no
+ * workspace. */
+int mxfp8_linear_prequant_batched(const void* xq, const void* xs, int64_t B, int64_t M,
+                                  int64_t K, const void* packed, int64_t N, int fmt,
+                                  const void* bias, void* y, void* stream);
+
 /* ---------------------------------------------------------------- modes and tuning */
 
 /* Batch-invariant mode (aiter_flydsl page, is_supported: its split-K kernel is not batch

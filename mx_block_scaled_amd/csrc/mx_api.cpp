@@ -250,6 +250,70 @@ int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K, 
                     "gemm launch");
 }
 
+int mxfp8_linear_batched(const void* x_bf16, int64_t B, int64_t M, int64_t K, const void* packed,
+                         int64_t N, int fmt, const void* bias, void* y, void* workspace,
+                         int64_t ws_bytes, void* stream) {
+  if (B < 0) return fail(MX_ESHAPE, "B = %lld is negative", (long long)B);
+  if (B > 0 && M > 0 && B * M / B != M) return fail(MX_ESHAPE, "B x M overflows");
+  int rc = check_linear_common(B * M, K, packed, N, fmt, y);
+  if (rc) return rc;
+  if (B == 0 || M == 0) return ok();
+  if (!x_bf16) return fail(MX_EINVAL, "null pointer (x)");
+  if (!aligned16(x_bf16)) return fail(MX_EALIGN, "x must be 16-byte aligned");
+  const int64_t need = quant_ws_bytes(B * M, K);
+  if (!workspace || ws_bytes < need)
+    return fail(MX_EWORKSPACE, "workspace of %lld bytes given, %lld needed", (long long)ws_bytes, (long long)need);
+  if (!aligned16(workspace)) return fail(MX_EALIGN, "workspace must be 16-byte aligned");
+  if (B > 65535) return fail(MX_ESHAPE, "B = %lld exceeds 65535", (long long)B);
+  if ((rc = check_arch())) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t P = mxfp8_prepacked_bytes(N, K, fmt);   // a multiple of 16
+  mx::BatchStrides bs;
+  bs.w = P;
+  bs.y = M * N * 2;
+  bs.bias = bias ? N * 2 : 0;
+  if (!mx::batch_invariant() && mx::small_m_fused(M, K)) {
+    bs.x = M * K * 2;
+    return hip_status(mx::launch_linear_small_m(x_bf16, nullptr, false, M, K,
+                                                (const uint8_t*)packed, N, fmt,
+                                                (const uint16_t*)bias, (uint16_t*)y, s, (int)B, bs),
+                      "linear (batched, small M) launch");
+  }
+  uint8_t* xq = (uint8_t*)workspace;
+  uint8_t* xs = xq + ((B * M * K + 255) / 256) * 256;
+  hipError_t e = mx::launch_quantize_act((const uint16_t*)x_bf16, B * M, K, K, xq, xs, s);
+  if (e != hipSuccess) return hip_status(e, "quantize_act launch");
+  bs.x = M * K;
+  bs.xs = M * (K / 32);
+  return hip_status(mx::launch_gemm(xq, xs, M, K, (const uint8_t*)packed, N, fmt,
+                                    (const uint16_t*)bias, (uint16_t*)y, s, (int)B, bs),
+                    "gemm (batched) launch");
+}
+
+int mxfp8_linear_prequant_batched(const void* xq, const void* xs, int64_t B, int64_t M, int64_t K,
+                                  const void* packed, int64_t N, int fmt, const void* bias,
+                                  void* y, void* stream) {
+  if (B < 0) return fail(MX_ESHAPE, "B = %lld is negative", (long long)B);
+  if (B > 0 && M > 0 && B * M / B != M) return fail(MX_ESHAPE, "B x M overflows");
+  int rc = check_linear_common(B * M, K, packed, N, fmt, y);
+  if (rc) return rc;
+  if (B == 0 || M == 0) return ok();
+  if (!xq || !xs) return fail(MX_EINVAL, "null pointer (xq or xs)");
+  if (!aligned16(xq)) return fail(MX_EALIGN, "xq must be 16-byte aligned");
+  if (B > 65535) return fail(MX_ESHAPE, "B = %lld exceeds 65535", (long long)B);
+  if ((rc = check_arch())) return rc;
+  mx::BatchStrides bs;
+  bs.x = M * K;
+  bs.xs = M * (K / 32);
+  bs.w = mxfp8_prepacked_bytes(N, K, fmt);
+  bs.y = M * N * 2;
+  bs.bias = bias ? N * 2 : 0;
+  return hip_status(mx::launch_gemm((const uint8_t*)xq, (const uint8_t*)xs, M, K,
+                                    (const uint8_t*)packed, N, fmt, (const uint16_t*)bias,
+                                    (uint16_t*)y, (hipStream_t)stream, (int)B, bs),
+                    "gemm (batched) launch");
+}
+
 int mxfp8_set_batch_invariant(int on) {
   mx::set_batch_invariant(on != 0);
   return ok();

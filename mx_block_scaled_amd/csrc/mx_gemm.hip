@@ -19,13 +19,26 @@ namespace mx {
 // Any M, K % 32 == 0, N % 16 == 0.  Workgroup = 4 waves = 64 weight rows x 32 activation rows;
 // each wave owns one 16-row weight fragment and two 16-row activation tiles, streaming both
 // operands straight from global memory into registers (no LDS).
+// Offsets the operand pointers (kernel parameters) to batch b (byte strides; all zero when
+// unbatched).
+#define MX_BATCH_OFFSET(b)                                                   \
+  do {                                                                       \
+    const int64_t b_ = (b);                                                  \
+    xq += b_ * bs.x;                                                         \
+    xs += b_ * bs.xs;                                                        \
+    packed += b_ * bs.w;                                                     \
+    y = (uint16_t*)((uint8_t*)y + b_ * bs.y);                                \
+    if (bias) bias = (const uint16_t*)((const uint8_t*)bias + b_ * bs.bias); \
+  } while (0)
+
 template <int WFMT>
 __global__ __launch_bounds__(256) void k_gemm_generic(const uint8_t* __restrict__ xq,
                                                       const uint8_t* __restrict__ xs, int M, int K,
                                                       const uint8_t* __restrict__ packed, int N,
                                                       const uint16_t* __restrict__ bias,
-                                                      uint16_t* __restrict__ y) {
+                                                      uint16_t* __restrict__ y, BatchStrides bs) {
   constexpr int FB = frag_bytes(WFMT);
+  MX_BATCH_OFFSET(blockIdx.z);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int NG = N >> 4, KT = (K + 127) >> 7, KB = K >> 5;
@@ -219,8 +232,9 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
                                                       const uint8_t* __restrict__ packed, int N,
                                                       const uint16_t* __restrict__ bias,
                                                       uint16_t* __restrict__ y, int tiles_m,
-                                                      int tiles_n, int group_m) {
+                                                      int tiles_n, int group_m, BatchStrides bs) {
   using C = TileCfg<WFMT, FN, FM, S>;
+  MX_BATCH_OFFSET(blockIdx.y);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
   uint8_t* const slds = lds + S * C::STAGE;                  // two group-scale buffers
   uint8_t* const scratch = slds + 2 * C::SCALE_BYTES;        // surplus DMA slots land here
@@ -496,11 +510,12 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
 
 template <int WFMT, int FN, int FM, int S>
 static void launch_tile(const uint8_t* xq, const uint8_t* xs, int M, int K, const uint8_t* packed,
-                        int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s) {
+                        int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s,
+                        int batch, const BatchStrides& bs) {
   using C = TileCfg<WFMT, FN, FM, S>;
   const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((k_gemm_tile<WFMT, FN, FM, S>), dim3((unsigned)(tm * tn)), dim3(512), 0, s,
-                     xq, xs, M, K, packed, N, bias, y, tm, tn, group_m);
+  hipLaunchKernelGGL((k_gemm_tile<WFMT, FN, FM, S>), dim3((unsigned)(tm * tn), (unsigned)batch),
+                     dim3(512), 0, s, xq, xs, M, K, packed, N, bias, y, tm, tn, group_m, bs);
 }
 
 // Tile choice: the configurations below are compiled; pick the one whose tile count fills the
@@ -532,44 +547,44 @@ static TileChoice choose_tile(int M, int N) {
 template <int WFMT>
 static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int K,
                                const uint8_t* packed, int N, const uint16_t* bias, uint16_t* y,
-                               hipStream_t s) {
+                               hipStream_t s, int batch, const BatchStrides& bs) {
   const TileChoice c = choose_tile(M, N);
   const int group_m = 4;
-  if (c.fn == 8 && c.fm == 4) launch_tile<WFMT, 8, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
-  else if (c.fn == 7 && c.fm == 4) launch_tile<WFMT, 7, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
-  else if (c.fn == 6 && c.fm == 4) launch_tile<WFMT, 6, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
-  else if (c.fn == 4 && c.fm == 4) launch_tile<WFMT, 4, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+  if (c.fn == 8 && c.fm == 4) launch_tile<WFMT, 8, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+  else if (c.fn == 7 && c.fm == 4) launch_tile<WFMT, 7, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+  else if (c.fn == 6 && c.fm == 4) launch_tile<WFMT, 6, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+  else if (c.fn == 4 && c.fm == 4) launch_tile<WFMT, 4, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else if ((long)((N + 127) / 128) * ((M + 127) / 128) <= 256)
     // one tile per CU at most: each workgroup runs the whole K of its tile, where a third LDS
     // stage (deeper prefetch) pays off
-    launch_tile<WFMT, 4, 2, 3>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+    launch_tile<WFMT, 4, 2, 3>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else
-    launch_tile<WFMT, 4, 2, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s);
+    launch_tile<WFMT, 4, 2, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
-                       uint16_t* y, hipStream_t s) {
+                       uint16_t* y, hipStream_t s, int batch, BatchStrides bs) {
   // the small-M kernel splits K over waves (a different summation order); batch-invariant
   // mode keeps every M on the kernels that add the K steps in sequence
   if (!batch_invariant() && small_m_quantized(M, K))
-    return launch_linear_small_m(xq, xs, true, M, K, packed, N, fmt, bias, y, s);
+    return launch_linear_small_m(xq, xs, true, M, K, packed, N, fmt, bias, y, s, batch, bs);
   const int m = (int)M, k = (int)K, n = (int)N;
   const bool tiled = (K % 128 == 0) && (((uintptr_t)xs & 3) == 0) && M >= 64 && N >= 128;
   if (tiled) {
     switch (fmt) {
-      case 0: return launch_tiled<0>(xq, xs, m, k, packed, n, bias, y, s);
-      case 2: return launch_tiled<2>(xq, xs, m, k, packed, n, bias, y, s);
-      case 3: return launch_tiled<3>(xq, xs, m, k, packed, n, bias, y, s);
+      case 0: return launch_tiled<0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
+      case 2: return launch_tiled<2>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
+      case 3: return launch_tiled<3>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
       default: return hipErrorInvalidValue;
     }
   }
-  dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)((M + 31) / 32)), block(256);
+  dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)((M + 31) / 32), (unsigned)batch), block(256);
   switch (fmt) {
-    case 0: hipLaunchKernelGGL(k_gemm_generic<0>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y); break;
-    case 2: hipLaunchKernelGGL(k_gemm_generic<2>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y); break;
-    case 3: hipLaunchKernelGGL(k_gemm_generic<3>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y); break;
+    case 0: hipLaunchKernelGGL(k_gemm_generic<0>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y, bs); break;
+    case 2: hipLaunchKernelGGL(k_gemm_generic<2>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y, bs); break;
+    case 3: hipLaunchKernelGGL(k_gemm_generic<3>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y, bs); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -15,6 +15,13 @@ struct PackGeom {
 };
 PackGeom pack_geom(int64_t N, int64_t K, int fmt);
 
+// Batched calls (grid dimension = batch index b): per-batch byte strides of the activations
+// (bf16 or E4M3), their scales, the prepacked weight, the output and the bias.  All zero for an
+// unbatched call.
+struct BatchStrides {
+  int64_t x = 0, xs = 0, w = 0, y = 0, bias = 0;
+};
+
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
                                uint8_t* xs, hipStream_t s);
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int fmt,
@@ -39,7 +46,7 @@ bool batch_invariant();
 // GEMM from quantized activations xq [M, K] + xs [M, K/32] (row-major).
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
-                       uint16_t* y, hipStream_t s);
+                       uint16_t* y, hipStream_t s, int batch = 1, BatchStrides bs = {});
 
 // Small-M (decode) path: one launch, K split over the waves of a workgroup.  x is bf16 [M, K]
 // quantized inside the kernel (small_m_fused shapes) or, with quantized = true, E4M3 xq [M, K]
@@ -48,6 +55,7 @@ bool small_m_fused(int64_t M, int64_t K);
 bool small_m_quantized(int64_t M, int64_t K);
 hipError_t launch_linear_small_m(const void* x, const uint8_t* xs, bool quantized, int64_t M,
                                  int64_t K, const uint8_t* packed, int64_t N, int fmt,
-                                 const uint16_t* bias, uint16_t* y, hipStream_t s);
+                                 const uint16_t* bias, uint16_t* y, hipStream_t s,
+                                 int batch = 1, BatchStrides bs = {});
 
 }  // namespace mx

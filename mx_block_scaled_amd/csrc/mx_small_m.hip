@@ -50,8 +50,16 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
                                                         const uint8_t* __restrict__ xs, int M,
                                                         int K, const uint8_t* __restrict__ packed,
                                                         int N, const uint16_t* __restrict__ bias,
-                                                        uint16_t* __restrict__ y) {
+                                                        uint16_t* __restrict__ y, BatchStrides bs) {
   static_assert(QX || MT == 1, "the fused quantizer covers one 16-row tile");
+  {  // batch blockIdx.y (byte strides; all zero when unbatched)
+    const int64_t b = blockIdx.y;
+    xin = (const uint8_t*)xin + b * bs.x;
+    xs += b * bs.xs;
+    packed += b * bs.w;
+    y = (uint16_t*)((uint8_t*)y + b * bs.y);
+    if (bias) bias = (const uint16_t*)((const uint8_t*)bias + b * bs.bias);
+  }
   constexpr int FB = frag_bytes(WFMT);
   constexpr int XL = QX ? 16 : 16 * kRowPitch;   // wave-private codes [16 rows][kRowPitch]
   constexpr int SL = QX ? 16 : 16 * 16;          // wave-private scales [16 rows][16 blocks]
@@ -214,30 +222,31 @@ bool small_m_quantized(int64_t M, int64_t K) { return M >= 1 && M <= 32 && K % 1
 template <int WFMT>
 static void launch_small(const void* x, const uint8_t* xs, bool quantized, int M, int K,
                          const uint8_t* packed, int N, const uint16_t* bias, uint16_t* y,
-                         hipStream_t s) {
-  const dim3 grid((unsigned)(N / 16)), block(512);
+                         hipStream_t s, int batch, const BatchStrides& bs) {
+  const dim3 grid((unsigned)(N / 16), (unsigned)batch), block(512);
   const bool xs16 = ((uintptr_t)xs & 15) == 0 && K % 512 == 0;   // then K / 32 % 16 == 0 too
   if (!quantized)
-    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, false, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
+    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, false, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y, bs);
   else if (M <= 16 && xs16)
-    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, true, true>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
+    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, true, true>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y, bs);
   else if (M <= 16)
-    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, true, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
+    hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, true, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y, bs);
   else if (xs16)
-    hipLaunchKernelGGL((k_linear_small_m<WFMT, 2, true, true>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
+    hipLaunchKernelGGL((k_linear_small_m<WFMT, 2, true, true>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y, bs);
   else
-    hipLaunchKernelGGL((k_linear_small_m<WFMT, 2, true, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y);
+    hipLaunchKernelGGL((k_linear_small_m<WFMT, 2, true, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y, bs);
 }
 
 hipError_t launch_linear_small_m(const void* x, const uint8_t* xs, bool quantized, int64_t M,
                                  int64_t K, const uint8_t* packed, int64_t N, int fmt,
-                                 const uint16_t* bias, uint16_t* y, hipStream_t s) {
+                                 const uint16_t* bias, uint16_t* y, hipStream_t s, int batch,
+                                 BatchStrides bs) {
   if (quantized ? !small_m_quantized(M, K) : !small_m_fused(M, K)) return hipErrorInvalidValue;
   const int m = (int)M, k = (int)K, n = (int)N;
   switch (fmt) {
-    case 0: launch_small<0>(x, xs, quantized, m, k, packed, n, bias, y, s); break;
-    case 2: launch_small<2>(x, xs, quantized, m, k, packed, n, bias, y, s); break;
-    case 3: launch_small<3>(x, xs, quantized, m, k, packed, n, bias, y, s); break;
+    case 0: launch_small<0>(x, xs, quantized, m, k, packed, n, bias, y, s, batch, bs); break;
+    case 2: launch_small<2>(x, xs, quantized, m, k, packed, n, bias, y, s, batch, bs); break;
+    case 3: launch_small<3>(x, xs, quantized, m, k, packed, n, bias, y, s, batch, bs); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -19,7 +19,8 @@ __all__ = [
     "FMT", "MXError", "lib", "library_path", "device_supported", "quantize_act",
     "quantize_weight", "prepack_weight", "unpack_weight", "prepacked_bytes", "workspace_bytes",
     "linear", "linear_prequant", "MxLinear", "set_tile_config", "set_batch_invariant",
-    "prepack_weight_shuffled16", "unpack_weight_shuffled16",
+    "prepack_weight_shuffled16", "unpack_weight_shuffled16", "linear_batched",
+    "linear_prequant_batched",
 ]
 
 FMT = {"e4m3": 0, "e2m3": 2, "e3m2": 3}
@@ -58,6 +59,8 @@ def lib():
             "mxfp8_linear_prequant": (I, [P, P, I64, I64, P, I64, I, P, P, P]),
             "mxfp8_set_tile_config": (I, [I, I]),
             "mxfp8_set_batch_invariant": (I, [I]),
+            "mxfp8_linear_batched": (I, [P, I64, I64, I64, P, I64, I, P, P, P, I64, P]),
+            "mxfp8_linear_prequant_batched": (I, [P, P, I64, I64, I64, P, I64, I, P, P, P]),
             "mxfp8_prepack_weight_shuffled16": (I, [P, P, I64, I64, I64, P, P]),
             "mxfp8_unpack_weight_shuffled16": (I, [P, I64, I64, P, P, P]),
         }
@@ -244,6 +247,55 @@ def linear_prequant(xq, xs, packed, N, fmt="e4m3", bias=None, out=None, lead_sha
     _check(lib().mxfp8_linear_prequant(xq.data_ptr(), xs.data_ptr(), M, K, packed.data_ptr(),
                                        N, f, b, y.data_ptr(), _stream(xq)))
     return y if lead_shape is None else y.reshape(*lead_shape, N)
+
+
+def linear_batched(x, packed, N, fmt="e4m3", bias=None, out=None, workspace=None):
+    """x bf16 [B, M, K], packed = B prepacked weights back to back (torch.cat of
+    prepack_weight outputs), bias bf16 [B, N] or None -> y bf16 [B, M, N]."""
+    x = _bf16(x, "x")
+    f = _fmt(fmt)
+    B, M, K = x.shape
+    packed = _u8(packed, "packed")
+    if packed.numel() != B * prepacked_bytes(N, K, f):
+        raise ValueError("packed must hold B prepacked weights")
+    y = out if out is not None else torch.empty((B, M, N), dtype=torch.bfloat16, device=x.device)
+    b = 0
+    if bias is not None:
+        bias = _bf16(bias, "bias")
+        if tuple(bias.shape) != (B, N):
+            raise ValueError("bias must be [B, N]")
+        b = bias.data_ptr()
+    st = _stream(x)
+    need = workspace_bytes(B * M, N, K, f)
+    ws = workspace if workspace is not None else _workspace(x.device, st.value, need)
+    _check(lib().mxfp8_linear_batched(x.data_ptr(), B, M, K, packed.data_ptr(), N, f, b,
+                                      y.data_ptr(), ws.data_ptr(), ws.numel(), st))
+    return y
+
+
+def linear_prequant_batched(xq, xs, packed, N, fmt="e4m3", bias=None, out=None):
+    """xq E4M3 [B, M, K], xs E8M0 [B, M, K/32] -> y bf16 [B, M, N] (weights as linear_batched)."""
+    xq = _u8(xq, "xq")
+    xs = _u8(xs, "xs")
+    f = _fmt(fmt)
+    B, M, K = xq.shape
+    if tuple(xs.shape) != (B, M, K // 32):
+        raise ValueError("activation scale %s for %s: need (B, M, K/32)"
+                         % (tuple(xs.shape), tuple(xq.shape)))
+    packed = _u8(packed, "packed")
+    if packed.numel() != B * prepacked_bytes(N, K, f):
+        raise ValueError("packed must hold B prepacked weights")
+    y = out if out is not None else torch.empty((B, M, N), dtype=torch.bfloat16, device=xq.device)
+    b = 0
+    if bias is not None:
+        bias = _bf16(bias, "bias")
+        if tuple(bias.shape) != (B, N):
+            raise ValueError("bias must be [B, N]")
+        b = bias.data_ptr()
+    _check(lib().mxfp8_linear_prequant_batched(xq.data_ptr(), xs.data_ptr(), B, M, K,
+                                               packed.data_ptr(), N, f, b, y.data_ptr(),
+                                               _stream(xq)))
+    return y
 
 
 class MxLinear:

@@ -123,6 +123,18 @@ def test_shuffled16_and_mode_validation(L):
     assert L.mxfp8_set_batch_invariant(0) == MX_OK
 
 
+def test_batched_validation(L):
+    ws = L.mxfp8_workspace_bytes(3 * 64, 256, 512, 0)
+    assert L.mxfp8_linear_batched(A, -1, 64, 512, B, 256, 0, None, B, B, ws, None) == MX_ESHAPE
+    assert L.mxfp8_linear_batched(None, 3, 64, 512, B, 256, 0, None, B, B, ws, None) == MX_EINVAL
+    assert L.mxfp8_linear_batched(A, 3, 64, 512, B, 256, 0, None, B, B, ws - 1, None) == MX_EWORKSPACE
+    assert L.mxfp8_linear_batched(A, 3, 64, 500, B, 256, 0, None, B, B, ws, None) == MX_ESHAPE
+    assert L.mxfp8_linear_batched(None, 0, 64, 512, B, 256, 0, None, B, None, 0, None) == MX_OK
+    assert L.mxfp8_linear_prequant_batched(A, None, 3, 64, 512, B, 256, 0, None, B, None) == MX_EINVAL
+    assert L.mxfp8_linear_prequant_batched(A, B, 70000, 1, 512, B, 256, 0, None, B, None) == MX_ESHAPE
+    assert L.mxfp8_linear_prequant_batched(A, B, 3, 0, 512, B, 256, 0, None, B, None) == MX_OK
+
+
 def test_tile_config_hook(L):
     assert L.mxfp8_set_tile_config(3, 3) == MX_EINVAL
     assert L.mxfp8_set_tile_config(0, 0) == MX_OK

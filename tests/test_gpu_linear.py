@@ -289,3 +289,34 @@ def test_batch_invariant_mode(K):
     ref, _, _ = orc.linear_ref(x, wq, ws, 0, b)
     ok, rep = tolerance.check(host_bf16_bits(y_all), ref, name="batch-invariant-%d" % K)
     assert ok, rep
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 48, 512), (24, 64, 1024), (100, 272, 512),
+                                   (300, 592, 640), (40, 160, 544)])
+def test_batched(M, N, K):
+    """Batched layer (bmm_batch_size): every batch equals a separate call bit for bit (same
+    kernels: fused small-M, quantizer + small-M, tiled, generic), and batch 1 matches the
+    oracle; per-batch bias and the pre-quantized batched entry included."""
+    Bn = 3
+    g = np.random.default_rng(M + N + K)
+    xs_ = [synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32)) for _ in range(Bn)]
+    ws_ = [synth.bf16_bits((g.standard_normal((N, K)) * 0.03).astype(np.float32)) for _ in range(Bn)]
+    bs_ = [synth.bf16_bits((g.standard_normal(N) * 0.1).astype(np.float32)) for _ in range(Bn)]
+    banner("batched", Bn, M, N, K)
+    layers = [_layer(ws_[b], 0, bs_[b]) for b in range(Bn)]
+    packed = torch.cat([l[0].packed for l in layers])
+    bias = torch.stack([bf16_dev(bb) for bb in bs_])
+    x = torch.stack([bf16_dev(xx) for xx in xs_])
+    y = mxfp8.linear_batched(x, packed, N, 0, bias)
+    xq, xsc = mxfp8.quantize_act(x.reshape(Bn * M, K))
+    yq = mxfp8.linear_prequant_batched(xq.view(Bn, M, K), xsc.view(Bn, M, K // 32), packed, N, 0,
+                                       bias)
+    for b in range(Bn):
+        y1 = layers[b][0](x[b])
+        assert torch.equal(y[b].view(torch.int16), y1.view(torch.int16)), b
+        y1q = layers[b][0].apply_quantized(xq.view(Bn, M, K)[b].contiguous(),
+                                           xsc.view(Bn, M, K // 32)[b].contiguous())
+        assert torch.equal(yq[b].view(torch.int16), y1q.view(torch.int16)), b
+    ref, _, _ = orc.linear_ref(xs_[1], layers[1][1], layers[1][2], 0, bs_[1])
+    ok, rep = tolerance.check(host_bf16_bits(y[1]), ref, name="batched-%d-%d-%d" % (M, N, K))
+    assert ok, rep

@@ -336,25 +336,35 @@ void orc_matmul_nt(const double* xd, const double* wd, const double* bias,
 /* The same sum for a list of (m, n) output positions, straight from the quantized operands
  * (codes one per byte + row-major E8M0 scales); used to check sampled outputs of large
  * problems without materialising the dequantized matrices. */
-int orc_linear_entries(const uint8_t* xq, const uint8_t* xs, int64_t K, const uint8_t* wq,
-                       const uint8_t* ws, int wfmt, const double* bias, const int64_t* rows,
-                       const int64_t* cols, int64_t count, double* out)
+/* y[rows[i], cols[i]] from quantized operands, one code per byte.  The activation codes are
+ * in format xfmt: E4M3 for the MXFP8 layer, or E2M3 / E3M2 when the mxfp6 page's
+ * activation_quant_key names an MXFP6 activation format. */
+int orc_linear_entries_fmt(const uint8_t* xq, const uint8_t* xs, int xfmt, int64_t K,
+                           const uint8_t* wq, const uint8_t* ws, int wfmt, const double* bias,
+                           const int64_t* rows, const int64_t* cols, int64_t count, double* out)
 {
     orc_fmt f;
-    if (fmt_params(wfmt, &f) || K % 32 != 0) return -1;
+    if (fmt_params(wfmt, &f) || fmt_params(xfmt, &f) || K % 32 != 0) return -1;
     const int64_t KB = K / 32;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < count; ++i) {
         const int64_t m = rows[i], n = cols[i];
         double s = 0.0;
         for (int64_t k = 0; k < K; ++k) {
-            double a = orc_decode(xq[m * K + k], ORC_E4M3) * orc_scale_value(xs[m * KB + k / 32]);
+            double a = orc_decode(xq[m * K + k], xfmt) * orc_scale_value(xs[m * KB + k / 32]);
             double b = orc_decode(wq[n * K + k], wfmt) * orc_scale_value(ws[n * KB + k / 32]);
             s += a * b;
         }
         out[i] = s + (bias ? bias[n] : 0.0);
     }
     return 0;
+}
+
+int orc_linear_entries(const uint8_t* xq, const uint8_t* xs, int64_t K, const uint8_t* wq,
+                       const uint8_t* ws, int wfmt, const double* bias, const int64_t* rows,
+                       const int64_t* cols, int64_t count, double* out)
+{
+    return orc_linear_entries_fmt(xq, xs, ORC_E4M3, K, wq, ws, wfmt, bias, rows, cols, count, out);
 }
 
 int orc_threads(void)

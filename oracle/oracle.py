@@ -58,6 +58,7 @@ def lib():
             "orc_unshuffle16": (I, [P, I64, I64, P]),
             "orc_matmul_nt": (None, [P, P, P, I64, I64, I64, P]),
             "orc_linear_entries": (I, [P, P, I64, P, P, I, P, P, P, I64, P]),
+            "orc_linear_entries_fmt": (I, [P, P, I, I64, P, P, I, P, P, P, I64, P]),
             "orc_threads": (I, []),
         }
         for name, (res, args) in sig.items():
@@ -192,8 +193,9 @@ def matmul_nt(xd, wd, bias=None):
     return y
 
 
-def linear_entries(xq, xs, wq, ws, rows, cols, wfmt=E4M3, bias=None):
-    """Reference y[rows[i], cols[i]] straight from quantized operands (codes one per byte)."""
+def linear_entries(xq, xs, wq, ws, rows, cols, wfmt=E4M3, bias=None, xfmt=E4M3):
+    """Reference y[rows[i], cols[i]] straight from quantized operands (codes one per byte);
+    xfmt is the activation codes' format (E4M3, or E2M3 / E3M2 for MXFP6 activations)."""
     xq, xs, wq, ws = (_c(a, np.uint8) for a in (xq, xs, wq, ws))
     K = xq.shape[1]
     assert wq.shape[1] == K and xs.shape[1] == K // 32 and ws.shape[1] == K // 32
@@ -201,18 +203,19 @@ def linear_entries(xq, xs, wq, ws, rows, cols, wfmt=E4M3, bias=None):
     assert r.shape == c.shape
     b = None if bias is None else _c(bias, np.float64)
     out = np.empty(r.shape, np.float64)
-    rc = lib().orc_linear_entries(_p(xq), _p(xs), K, _p(wq), _p(ws), wfmt,
-                                  None if b is None else _p(b), _p(r), _p(c), r.size, _p(out))
+    rc = lib().orc_linear_entries_fmt(_p(xq), _p(xs), xfmt, K, _p(wq), _p(ws), wfmt,
+                                      None if b is None else _p(b), _p(r), _p(c), r.size, _p(out))
     if rc != 0:
         raise ValueError("orc_linear_entries: bad format or K")
     return out
 
 
-def linear_ref(x_bf16, wq, ws, wfmt=E4M3, bias_bf16=None):
+def linear_ref(x_bf16, wq, ws, wfmt=E4M3, bias_bf16=None, xfmt=E4M3):
     """Full fp64 reference of the linear layer from bf16 activations:
-    quantize x (E4M3, row-major scales), dequantize both operands, multiply, add bias."""
-    xq, xs = quantize(x_bf16, E4M3)
-    xd = dequantize(xq, xs, E4M3)
+    quantize x (format xfmt, E4M3 by default; row-major scales), dequantize both operands,
+    multiply, add bias.  Returns (y, x codes one per byte, x scales)."""
+    xq, xs = quantize(x_bf16, xfmt)
+    xd = dequantize(xq, xs, xfmt)
     wd = dequantize(wq, ws, wfmt)
     bias = None if bias_bf16 is None else bf16_to_f64(bias_bf16)
     return matmul_nt(xd, wd, bias), xq, xs

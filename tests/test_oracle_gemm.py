@@ -163,3 +163,63 @@ def test_tolerance_rejects_planted_mistakes(orc, mistake):
         bad = orc.matmul_nt(xd, wd2, b)
     ok, rep = tolerance.check(_bf16_of(bad), ref)
     assert not ok, (mistake, rep)
+
+
+# ---------------------------------------------------------------- MXFP6 activations
+
+def _fp6_code_of_int(orc, fmt):
+    """code of each integer in -7..7 representable in the format (found by decode search)."""
+    table = {}
+    for c in range(64):
+        v = orc.decode(c, fmt)
+        if v == int(v) and abs(v) <= 7 and not (v == 0 and c != 0):
+            table[int(v)] = c
+    return table
+
+
+@pytest.mark.parametrize("xfmt,wfmt", [(2, 2), (3, 2), (2, 3), (3, 3), (2, 0)])
+def test_exact_integer_gemm_fp6_activations(orc, xfmt, wfmt):
+    """MXFP6 activations (the mxfp6 page's activation_quant_key): small integers with scale
+    byte 127 give exactly numpy's int64 matmul, through both oracle paths."""
+    g = np.random.default_rng(10 + xfmt * 4 + wfmt)
+    M, N, K = 6, 20, 160
+    tx = _fp6_code_of_int(orc, xfmt)
+    tw = _fp6_code_of_int(orc, wfmt) if wfmt else _e4m3_code_of_int(orc)
+    vals = sorted(set(tx) & set(tw))
+    assert {-7, -4, -3, 0, 1, 3, 4, 7} <= set(vals) or {-4, -3, 0, 1, 3, 4} <= set(vals)
+    xi = g.choice(vals, (M, K))
+    wi = g.choice(vals, (N, K))
+    xq = np.vectorize(tx.get)(xi).astype(np.uint8)
+    wq = np.vectorize(tw.get)(wi).astype(np.uint8)
+    s1 = np.full((M, K // 32), 127, np.uint8)
+    s2 = np.full((N, K // 32), 127, np.uint8)
+    exact = (xi @ wi.T).astype(np.float64)
+    y = orc.matmul_nt(orc.dequantize(xq, s1, xfmt), orc.dequantize(wq, s2, wfmt))
+    assert np.array_equal(y, exact)
+    ye = orc.linear_entries(xq, s1, wq, s2, np.repeat(np.arange(M), N), np.tile(np.arange(N), M),
+                            wfmt=wfmt, xfmt=xfmt)
+    assert np.array_equal(ye.reshape(M, N), exact)
+
+
+def test_fp6_activation_scales_and_reference(orc):
+    """linear_ref with MXFP6 activations: x is quantized with the format's own emax (E2M3: a
+    block whose amax is 2^j gets byte j - 2 + 127), and scaling one activation block's scale
+    byte by +1 doubles exactly that block's contribution."""
+    K = 64
+    x = np.zeros((2, K), np.float32)
+    x[0, :32] = 1.0                      # amax 2^0 -> E2M3 byte 125, E3M2 byte 123
+    x[0, 32:] = 3.0                      # amax 1.5 * 2^1 -> E2M3 byte 126, E3M2 byte 124
+    x[1, :] = -0.25                      # amax 2^-2 -> E2M3 byte 123, E3M2 byte 121
+    xb = synth.bf16_bits(x)
+    wq = np.zeros((16, K), np.uint8)
+    wq[:, :] = 0x38                      # E4M3 1.0
+    ws = np.full((16, K // 32), 127, np.uint8)
+    for fmt, emax in ((2, 2), (3, 4)):
+        ref, xq, xs = orc.linear_ref(xb, wq, ws, xfmt=fmt)
+        assert xs.tolist() == [[127 - emax, 128 - emax], [125 - emax, 125 - emax]]
+        # every value is exactly representable, so y is the exact row sum
+        np.testing.assert_array_equal(ref[:, 0], [32 * 1.0 + 32 * 3.0, -0.25 * 64])
+        xs2 = xs.copy()
+        xs2[0, 1] += 1
+        y2 = orc.matmul_nt(orc.dequantize(xq, xs2, fmt), orc.dequantize(wq, ws))
+        np.testing.assert_array_equal(y2[0, 0], 32 * 1.0 + 2 * 32 * 3.0)

@@ -19,7 +19,9 @@ Also measured and printed in the same JSON line:
                 time per call, algorithmic bytes / time against 8 TB/s;
   other_workloads  outlier activations on the pre-quantized entry (2048 x 6144 x 4096, GEMM
                 only), MXFP6 weights (E2M3 and E3M2, 512 x 8192 x 8192, activation quantization
-                included), each over enough rotated sets to exceed the Infinity Cache; and the
+                included) with MXFP8 activations and with MXFP6 activations of the same format
+                (both MFMA operands FP6), each over enough rotated sets to exceed the Infinity
+                Cache; and the
                 latency of one tiny call (16 x 256 x 512) from a HIP graph;
   cpu_baseline  the CPU oracle on a bounded sample of the prefill workload (host cores),
                 run in a separate process (oracle/cpu_bench.py).
@@ -40,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA
+PEAK_FP6_TFLOPS = 10100.0    # MI355X dense FP6 / FP4 MFMA
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 MALL_BYTES = 256 << 20
 
@@ -312,7 +315,18 @@ def main():
                 "us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
                 "mfma_frac_fp8_rate": round(fl / us / 1e6 / PEAK_FP8_TFLOPS, 4),
                 "rotated_sets": len(sets)}
-            del sets, pk_f, wsf
+            # the same weights with MXFP6 activations (same format as the weight): both MFMA
+            # operands FP6, against the 10.1 PFLOP/s dense FP6 peak
+            wsf6 = torch.empty(mxfp8.workspace_bytes_fmt(Mf, Nf, Kf, fname, fname),
+                               dtype=torch.uint8, device=dev)
+            us6 = time_calls(lambda j: mxfp8.linear_fmt(sets[j][0], sets[j][1], Nf, fname, fname,
+                                                        out=sets[j][2], workspace=wsf6),
+                             len(sets), max(50, args.steps))
+            others["w6a6_%s_512x8192x8192" % fname] = {
+                "us": round(us6, 2), "TFLOP/s": round(fl / us6 / 1e6, 1),
+                "mfma_frac_fp6_rate": round(fl / us6 / 1e6 / PEAK_FP6_TFLOPS, 4),
+                "rotated_sets": len(sets)}
+            del sets, pk_f, wsf, wsf6
         del xf, wf
         torch.cuda.empty_cache()
 

@@ -164,6 +164,39 @@ int mxfp8_linear_prequant_batched(const void* xq, const void* xs, int64_t B, int
                                   int64_t K, const void* packed, int64_t N, int fmt,
                                   const void* bias, void* y, void* stream);
 
+/* ---------------------------------------------------------------- MXFP6 activations */
+
+/* MXFP6 activations (mxfp6 page, MxFp6LinearLayerConfig.activation_quant_key: the activation
+ * quantization format of an MXFP6 layer).  afmt selects the activations' element format:
+ * MX_FMT_E4M3 (the MXFP8 layer above) or MX_FMT_E2M3 / MX_FMT_E3M2.  FP6 activations require
+ * FP6 weights (fmt E2M3 or E3M2): with both operands FP6 the scaled MFMA runs at its FP6 rate.
+ * FP6 activations use the same rule as FP6 weights: E8M0 scale per 32 along K from the format's
+ * emax (E2M3: 2, E3M2: 4), round-to-nearest-even, saturating, four 6-bit codes per three bytes
+ * little-endian along K (a block with Inf/NaN: scale 0xFF, codes 0). */
+
+/* Dynamic activation quantization in format afmt:
+ *   x_bf16 [16]  bf16 [M, ldx] (ldx >= K, ldx % 8 == 0)
+ *   xq     [16]  out: E4M3 [M, K] bytes (afmt E4M3) or packed FP6 [M, 3K/4] bytes
+ *   xs           out: E8M0 [M, K/32] row-major
+ * afmt == MX_FMT_E4M3 is mxfp8_quantize_act. */
+int mxfp8_quantize_act_fmt(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, int afmt,
+                           void* xq, void* xs, void* stream);
+
+/* Workspace bytes mxfp8_linear_fmt needs (0 for invalid arguments or M == 0). */
+int64_t mxfp8_workspace_bytes_fmt(int64_t M, int64_t N, int64_t K, int fmt, int afmt);
+
+/* mxfp8_linear with activations quantized to afmt (fmt = the weight's format; FP6 afmt needs
+ * FP6 fmt, otherwise MX_EINVAL).  workspace [16]: ws_bytes >= mxfp8_workspace_bytes_fmt. */
+int mxfp8_linear_fmt(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N,
+                     int fmt, int afmt, const void* bias, void* y, void* workspace,
+                     int64_t ws_bytes, void* stream);
+
+/* mxfp8_linear_prequant with activations in format afmt: xq [16] E4M3 [M, K] or packed FP6
+ * [M, 3K/4]; xs E8M0 [M, K/32] row-major.  Needs no workspace. */
+int mxfp8_linear_prequant_fmt(const void* xq, const void* xs, int64_t M, int64_t K, int afmt,
+                              const void* packed, int64_t N, int fmt, const void* bias, void* y,
+                              void* stream);
+
 /* ---------------------------------------------------------------- modes and tuning */
 
 /* Batch-invariant mode (aiter_flydsl page, is_supported: its split-K kernel is not batch

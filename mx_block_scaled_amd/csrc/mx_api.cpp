@@ -73,9 +73,20 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
-int64_t quant_ws_bytes(int64_t M, int64_t K) {
-  // xq [M, K] then xs [M, K/32], the latter at a 256-byte boundary
-  return ((M * K + 255) / 256) * 256 + M * (K / 32);
+int64_t quant_ws_bytes(int64_t M, int64_t K, int afmt = MX_FMT_E4M3) {
+  // xq [M, K] (E4M3) or [M, 3K/4] (FP6), then xs [M, K/32] at a 256-byte boundary
+  const int64_t row = afmt == MX_FMT_E4M3 ? K : K / 4 * 3;
+  return ((M * row + 255) / 256) * 256 + M * (K / 32);
+}
+
+// (weight, activation) format pairs with kernels: E4M3 activations with any weight format,
+// FP6 activations with FP6 weights
+int check_fmt_pair(int fmt, int afmt) {
+  if (!valid_fmt(fmt)) return fail(MX_EINVAL, "unknown weight format %d", fmt);
+  if (!valid_fmt(afmt)) return fail(MX_EINVAL, "unknown activation format %d", afmt);
+  if (afmt != MX_FMT_E4M3 && fmt == MX_FMT_E4M3)
+    return fail(MX_EINVAL, "FP6 activations (format %d) need FP6 weights", afmt);
+  return MX_OK;
 }
 
 }  // namespace
@@ -312,6 +323,74 @@ int mxfp8_linear_prequant_batched(const void* xq, const void* xs, int64_t B, int
                                     (const uint8_t*)packed, N, fmt, (const uint16_t*)bias,
                                     (uint16_t*)y, (hipStream_t)stream, (int)B, bs),
                     "gemm (batched) launch");
+}
+
+int mxfp8_quantize_act_fmt(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, int afmt,
+                           void* xq, void* xs, void* stream) {
+  if (!valid_fmt(afmt)) return fail(MX_EINVAL, "unknown activation format %d", afmt);
+  if (afmt == MX_FMT_E4M3) return mxfp8_quantize_act(x_bf16, M, K, ldx, xq, xs, stream);
+  int rc = check_mk(M, K);
+  if (rc) return rc;
+  if (M == 0) return ok();
+  if (!x_bf16 || !xq || !xs) return fail(MX_EINVAL, "null pointer (x, xq or xs)");
+  if (ldx < K) return fail(MX_ESHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldx % 8 != 0 || !aligned16(x_bf16) || !aligned16(xq))
+    return fail(MX_EALIGN, "x, xq must be 16-byte aligned and ldx a multiple of 8");
+  if ((rc = check_arch())) return rc;
+  return hip_status(mx::launch_quantize_act_fp6((const uint16_t*)x_bf16, M, K, ldx, afmt,
+                                                (uint8_t*)xq, (uint8_t*)xs, (hipStream_t)stream),
+                    "quantize_act (FP6) launch");
+}
+
+int64_t mxfp8_workspace_bytes_fmt(int64_t M, int64_t N, int64_t K, int fmt, int afmt) {
+  if (!valid_fmt(fmt) || !valid_fmt(afmt) || check_mk(M, K) || check_nk(N, K)) return 0;
+  if (afmt != MX_FMT_E4M3 && fmt == MX_FMT_E4M3) return 0;
+  if (M == 0) return 0;
+  return quant_ws_bytes(M, K, afmt);
+}
+
+int mxfp8_linear_fmt(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N,
+                     int fmt, int afmt, const void* bias, void* y, void* workspace,
+                     int64_t ws_bytes, void* stream) {
+  int rc = check_fmt_pair(fmt, afmt);
+  if (rc) return rc;
+  if (afmt == MX_FMT_E4M3)
+    return mxfp8_linear(x_bf16, M, K, packed, N, fmt, bias, y, workspace, ws_bytes, stream);
+  if ((rc = check_linear_common(M, K, packed, N, fmt, y))) return rc;
+  if (M == 0) return ok();
+  if (!x_bf16) return fail(MX_EINVAL, "null pointer (x)");
+  if (!aligned16(x_bf16)) return fail(MX_EALIGN, "x must be 16-byte aligned");
+  const int64_t need = quant_ws_bytes(M, K, afmt);
+  if (!workspace || ws_bytes < need)
+    return fail(MX_EWORKSPACE, "workspace of %lld bytes given, %lld needed", (long long)ws_bytes, (long long)need);
+  if (!aligned16(workspace)) return fail(MX_EALIGN, "workspace must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* xq = (uint8_t*)workspace;
+  uint8_t* xs = xq + ((M * (K / 4 * 3) + 255) / 256) * 256;
+  hipError_t e = mx::launch_quantize_act_fp6((const uint16_t*)x_bf16, M, K, K, afmt, xq, xs, s);
+  if (e != hipSuccess) return hip_status(e, "quantize_act (FP6) launch");
+  return hip_status(mx::launch_gemm(xq, xs, M, K, (const uint8_t*)packed, N, fmt,
+                                    (const uint16_t*)bias, (uint16_t*)y, s, 1, {}, afmt),
+                    "gemm launch");
+}
+
+int mxfp8_linear_prequant_fmt(const void* xq, const void* xs, int64_t M, int64_t K, int afmt,
+                              const void* packed, int64_t N, int fmt, const void* bias, void* y,
+                              void* stream) {
+  int rc = check_fmt_pair(fmt, afmt);
+  if (rc) return rc;
+  if (afmt == MX_FMT_E4M3)
+    return mxfp8_linear_prequant(xq, xs, M, K, packed, N, fmt, bias, y, stream);
+  if ((rc = check_linear_common(M, K, packed, N, fmt, y))) return rc;
+  if (M == 0) return ok();
+  if (!xq || !xs) return fail(MX_EINVAL, "null pointer (xq or xs)");
+  if (!aligned16(xq)) return fail(MX_EALIGN, "xq must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  return hip_status(mx::launch_gemm((const uint8_t*)xq, (const uint8_t*)xs, M, K,
+                                    (const uint8_t*)packed, N, fmt, (const uint16_t*)bias,
+                                    (uint16_t*)y, (hipStream_t)stream, 1, {}, afmt),
+                    "gemm launch");
 }
 
 int mxfp8_set_batch_invariant(int on) {

@@ -31,7 +31,7 @@ namespace mx {
     if (bias) bias = (const uint16_t*)((const uint8_t*)bias + b_ * bs.bias); \
   } while (0)
 
-template <int WFMT>
+template <int WFMT, int XFMT>
 __global__ __launch_bounds__(256) void k_gemm_generic(const uint8_t* __restrict__ xq,
                                                       const uint8_t* __restrict__ xs, int M, int K,
                                                       const uint8_t* __restrict__ packed, int N,
@@ -42,6 +42,7 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const uint8_t* __restrict_
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int NG = N >> 4, KT = (K + 127) >> 7, KB = K >> 5;
+  const int LDX = XFMT == 0 ? K : K / 4 * 3;   // activation row bytes
   const int ng = blockIdx.x * 4 + w;
   if (ng >= NG) return;  // whole wave leaves; nothing below synchronizes across waves
   const int m0 = blockIdx.y * 32;
@@ -73,14 +74,27 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const uint8_t* __restrict_
     const int kb = 4 * kt + g;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const uint8_t* xr = xq + (int64_t)mrow[t] * K;
-      v4i b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
-      const int k0 = 128 * kt + 16 * g, k1 = k0 + 64;
-      if (mok[t] && k0 < K) b0 = *(const v4i*)(xr + k0);
-      if (mok[t] && k1 < K) b1 = *(const v4i*)(xr + k1);
-      const v8i b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      const uint8_t* xr = xq + (int64_t)mrow[t] * LDX;
+      v8i b;
+      if constexpr (XFMT == 0) {
+        v4i b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+        const int k0 = 128 * kt + 16 * g, k1 = k0 + 64;
+        if (mok[t] && k0 < K) b0 = *(const v4i*)(xr + k0);
+        if (mok[t] && k1 < K) b1 = *(const v4i*)(xr + k1);
+        b = (v8i){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      } else {
+        // FP6 operand: block kb's 24 packed bytes (8-byte aligned: rows are 24 K/32 bytes)
+        v2i d0 = {0, 0}, d1 = {0, 0}, d2 = {0, 0};
+        if (mok[t] && kb < KB) {
+          const uint8_t* p = xr + 24 * kb;
+          d0 = *(const v2i*)p;
+          d1 = *(const v2i*)(p + 8);
+          d2 = *(const v2i*)(p + 16);
+        }
+        b = (v8i){d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], 0, 0};
+      }
       const int sb = kb < KB ? (int)xs[(int64_t)mrow[t] * KB + kb] : 127;
-      acc[t] = mfma16<WFMT, 0>(a, b, acc[t], sa, sb);
+      acc[t] = mfma16<WFMT, XFMT>(a, b, acc[t], sa, sb);
     }
   }
   // epilogue: lane holds n = 16 ng + 4 g + i (i < 4) of activation row m0 + 16 t + r
@@ -149,30 +163,51 @@ __device__ __forceinline__ v4f mfma_opsel(int q, const v8i& a, const v8i& b, v4f
 #define MX_MFMA_ASM(OPSEL, FMT)                                                                 \
   asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 " OPSEL FMT           \
                : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb))
-// A-operand register image of one weight fragment: 32 bytes for E4M3, 24 for FP6
-template <int WFMT> struct AReg { typedef v8i type; };
+#define MX_MFMA_Q(FMT)                                            \
+  do {                                                            \
+    if constexpr (Q == 0) MX_MFMA_ASM(MX_MFMA_OPSEL_0, FMT);      \
+    else if constexpr (Q == 1) MX_MFMA_ASM(MX_MFMA_OPSEL_1, FMT); \
+    else if constexpr (Q == 2) MX_MFMA_ASM(MX_MFMA_OPSEL_2, FMT); \
+    else MX_MFMA_ASM(MX_MFMA_OPSEL_3, FMT);                       \
+  } while (0)
+// operand register image of one 16-row x 128-K fragment: 32 bytes for E4M3, 24 for FP6
+template <int F> struct AReg { typedef v8i type; };
 template <> struct AReg<2> { typedef v6i type; };
 template <> struct AReg<3> { typedef v6i type; };
 
-template <int WFMT, int Q>
-__device__ __forceinline__ void mfma_inplace(v4f& acc, const typename AReg<WFMT>::type& a,
-                                             const v8i& b, uint32_t sa, uint32_t sb) {
+// WFMT = A (weight) format, XFMT = B (activation) format: the cbsz / blgp fields
+template <int WFMT, int XFMT, int Q, class TA, class TB>
+__device__ __forceinline__ void mfma_inplace(v4f& acc, const TA& a, const TB& b, uint32_t sa,
+                                             uint32_t sb) {
   static_assert(Q >= 0 && Q < 4, "op-select byte");
-  if constexpr (WFMT == 0) {
-    if constexpr (Q == 0) MX_MFMA_ASM(MX_MFMA_OPSEL_0, "");
-    else if constexpr (Q == 1) MX_MFMA_ASM(MX_MFMA_OPSEL_1, "");
-    else if constexpr (Q == 2) MX_MFMA_ASM(MX_MFMA_OPSEL_2, "");
-    else MX_MFMA_ASM(MX_MFMA_OPSEL_3, "");
-  } else if constexpr (WFMT == 2) {
-    if constexpr (Q == 0) MX_MFMA_ASM(MX_MFMA_OPSEL_0, " cbsz:2");
-    else if constexpr (Q == 1) MX_MFMA_ASM(MX_MFMA_OPSEL_1, " cbsz:2");
-    else if constexpr (Q == 2) MX_MFMA_ASM(MX_MFMA_OPSEL_2, " cbsz:2");
-    else MX_MFMA_ASM(MX_MFMA_OPSEL_3, " cbsz:2");
+  static_assert(std::is_same<TA, typename AReg<WFMT>::type>::value &&
+                    std::is_same<TB, typename AReg<XFMT>::type>::value,
+                "operand register images: 8 registers for E4M3, 6 for FP6");
+  static_assert(XFMT == 0 || WFMT != 0, "FP6 activations go with FP6 weights");
+#if defined(__HIP_DEVICE_COMPILE__)   // the VGPR operand constraints exist for gfx950 only
+  if constexpr (WFMT == 0) MX_MFMA_Q("");
+  else if constexpr (WFMT == 2 && XFMT == 0) MX_MFMA_Q(" cbsz:2");
+  else if constexpr (WFMT == 3 && XFMT == 0) MX_MFMA_Q(" cbsz:3");
+  else if constexpr (WFMT == 2 && XFMT == 2) MX_MFMA_Q(" cbsz:2 blgp:2");
+  else if constexpr (WFMT == 2 && XFMT == 3) MX_MFMA_Q(" cbsz:2 blgp:3");
+  else if constexpr (WFMT == 3 && XFMT == 2) MX_MFMA_Q(" cbsz:3 blgp:2");
+  else MX_MFMA_Q(" cbsz:3 blgp:3");
+#endif
+}
+
+// Activation (B) operand of one 16-row group from the LDS tile.  E4M3: two 16-byte pieces (K
+// bytes 16 g.. and 64 + 16 g.. of the row).  FP6: block g's 24 bytes, a whole 16-byte chunk `p`
+// and the 8-byte half `q` of its neighbour, which comes first for odd g.
+template <int XFMT>
+__device__ __forceinline__ typename AReg<XFMT>::type lds_b_operand(const uint8_t* p,
+                                                                  const uint8_t* q, bool godd) {
+  if constexpr (XFMT == 0) {
+    const v4i lo = *(const v4i*)p, hi = *(const v4i*)q;
+    return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   } else {
-    if constexpr (Q == 0) MX_MFMA_ASM(MX_MFMA_OPSEL_0, " cbsz:3");
-    else if constexpr (Q == 1) MX_MFMA_ASM(MX_MFMA_OPSEL_1, " cbsz:3");
-    else if constexpr (Q == 2) MX_MFMA_ASM(MX_MFMA_OPSEL_2, " cbsz:3");
-    else MX_MFMA_ASM(MX_MFMA_OPSEL_3, " cbsz:3");
+    const v4i x = *(const v4i*)p;
+    const v2i h = *(const v2i*)q;
+    return godd ? (v6i){h[0], h[1], x[0], x[1], x[2], x[3]} : (v6i){x[0], x[1], x[2], x[3], h[0], h[1]};
   }
 }
 
@@ -181,10 +216,13 @@ __device__ __forceinline__ void mfma_inplace(v4f& acc, const typename AReg<WFMT>
 // 32 FN weight rows x 64 FM activation rows; S LDS stages (the K step being computed plus
 // S - 1 prefetched).  Two waves per SIMD: while one waits on LDS or the barrier, the other
 // keeps the matrix pipe busy, and together they draw about twice the LDS read bandwidth of one.
-template <int WFMT, int FN, int FM, int S>
+// XFMT is the activations' format: E4M3 (128 bytes per row and K step) or, with FP6 weights,
+// E2M3 / E3M2 (96 bytes: four 24-byte blocks); the LDS row slot stays 128 bytes either way.
+template <int WFMT, int XFMT, int FN, int FM, int S>
 struct TileCfg {
   static constexpr int NW = 8, WGN = 2, WGM = 4;
   static constexpr int FB = frag_bytes(WFMT);
+  static constexpr int XB = XFMT == 0 ? 128 : 96;  // activation bytes per row per K step
   static constexpr int BN = 16 * FN * WGN, BM = 16 * FM * WGM;
   static constexpr int A_BYTES = (BN / 16) * FB;   // BN weight rows x one K step
   static constexpr int B_BYTES = BM * 128;         // BM activation rows x 128 bytes
@@ -226,14 +264,14 @@ __device__ __forceinline__ void wait_vm_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
-template <int WFMT, int FN, int FM, int S>
+template <int WFMT, int XFMT, int FN, int FM, int S>
 __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict__ xq,
                                                       const uint8_t* __restrict__ xs, int M, int K,
                                                       const uint8_t* __restrict__ packed, int N,
                                                       const uint16_t* __restrict__ bias,
                                                       uint16_t* __restrict__ y, int tiles_m,
                                                       int tiles_n, int group_m, BatchStrides bs) {
-  using C = TileCfg<WFMT, FN, FM, S>;
+  using C = TileCfg<WFMT, XFMT, FN, FM, S>;
   MX_BATCH_OFFSET(blockIdx.y);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
   uint8_t* const slds = lds + S * C::STAGE;                  // two group-scale buffers
@@ -258,6 +296,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   const int n0 = tn * C::BN, m0 = tm * C::BM;
 
   const int NG = N >> 4, KT = K >> 7, KB = K >> 5;
+  const int LDX = K / 128 * C::XB;   // activation row bytes
   const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * C::FB);
 
   // ---- per-lane DMA sources, as 32-bit offsets from uniform bases (every operand < 2^31 B):
@@ -281,13 +320,16 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     }
   }
   const uint32_t a_lane = C::FB % 1024 == 0 ? (uint32_t)lane * 16 : 0u;
-  // B: wave w copies rows 8 c .. 8 c + 7 for c = w, w + 8, ..., lane -> (row, slot)
+  // B: wave w copies rows 8 c .. 8 c + 7 for c = w, w + 8, ..., lane -> (row, slot); an FP6
+  // row has 6 chunks, so the lanes of slots holding chunks 6 and 7 stay idle
   uint32_t b_off[C::B_PER_WAVE];
+  bool b_on[C::B_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::B_PER_WAVE; ++i) {
     const int row = 8 * (wave + C::NW * i) + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(row);
-    b_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + chunk * 16);
+    b_on[i] = chunk < C::XB / 16;
+    b_off[i] = (uint32_t)(min(m0 + row, M - 1) * LDX + min(chunk, C::XB / 16 - 1) * 16);
   }
   // the p-th tile DMA of a step (p < D: weight chunks first, then activation rows)
   auto issue_one = [&](int kt, int stage, int p) __attribute__((always_inline)) {
@@ -298,7 +340,8 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
             c < C::A_CHUNKS ? base + c * 1024 : scratch);
     } else {
       const int i = p - C::A_PER_WAVE;
-      dma16(xq + (uint32_t)(kt * 128 + b_off[i]), base + C::A_BYTES + (wave + C::NW * i) * 1024);
+      if (XFMT == 0 || b_on[i])
+        dma16(xq + (uint32_t)(kt * C::XB + b_off[i]), base + C::A_BYTES + (wave + C::NW * i) * 1024);
     }
   };
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
@@ -368,6 +411,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     for (int j = 0; j < FM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
   typedef typename AReg<WFMT>::type AR;
+  typedef typename AReg<XFMT>::type BR;
   auto load_a = [&](const uint8_t* base, int i) __attribute__((always_inline)) {
     const uint8_t* fa = base + (wn * FN + i) * C::FB;
     const v4i lo = *(const v4i*)(fa + lane * 16);
@@ -386,6 +430,12 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   // swizzle, leaving one address per half and a constant 2 KiB step per j
   const uint32_t b_lo = (uint32_t)((wm * 16 * FM + r) * 128 + ((g ^ swz(r)) << 4));
   const uint32_t b_hi = (uint32_t)((wm * 16 * FM + r) * 128 + (((4 + g) ^ swz(r)) << 4));
+  // FP6: block g is bytes [24 g, 24 g + 24) of the row slice, i.e. chunk 3g/2 in full plus
+  // half of its neighbour (after it for even g, before it for odd g)
+  const bool godd = (g & 1) != 0;
+  const int c_full = (3 * g + 1) >> 1, c_half = godd ? c_full - 1 : c_full + 1;
+  const uint32_t bx_off = (uint32_t)((wm * 16 * FM + r) * 128 + ((c_full ^ swz(r)) << 4));
+  const uint32_t by_off = (uint32_t)((wm * 16 * FM + r) * 128 + ((c_half ^ swz(r)) << 4) + (godd ? 8 : 0));
   // `mid` runs once the first operand reads are issued and before the first MFMA: the step's
   // DMAs go out there, so their issue overlaps the LDS read latency instead of delaying it.
   auto compute = [&](int stage, auto qc, const uint32_t* sa_in, const uint32_t* sb_in, int sh, auto&& mid) __attribute__((always_inline)) {
@@ -404,13 +454,11 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     const uint8_t* base = lds + stage * C::STAGE;
     const uint8_t* bl = base + C::A_BYTES;
     AR a = load_a(base, 0);
-    v8i b[FM];
+    BR b[FM];
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      const v4i lo = *(const v4i*)(bl + b_lo + j * 2048);
-      const v4i hi = *(const v4i*)(bl + b_hi + j * 2048);
-      b[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    }
+    for (int j = 0; j < FM; ++j)
+      b[j] = lds_b_operand<XFMT>(bl + (XFMT == 0 ? b_lo : bx_off) + j * 2048,
+                                 bl + (XFMT == 0 ? b_hi : by_off) + j * 2048, godd);
     AR an = FN > 1 ? load_a(base, 1) : a;
     __builtin_amdgcn_sched_barrier(0);
     mid();
@@ -423,7 +471,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
       }
 #pragma unroll
       for (int j = 0; j < FM; ++j) {
-        mfma_inplace<WFMT, (Q >= 0 ? Q : 0)>(acc[i][j], a, b[j], sa[i], sb[j]);
+        mfma_inplace<WFMT, XFMT, (Q >= 0 ? Q : 0)>(acc[i][j], a, b[j], sa[i], sb[j]);
       }
       __builtin_amdgcn_sched_barrier(0);
       a = an;
@@ -508,13 +556,13 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   }
 }
 
-template <int WFMT, int FN, int FM, int S>
+template <int WFMT, int XFMT, int FN, int FM, int S>
 static void launch_tile(const uint8_t* xq, const uint8_t* xs, int M, int K, const uint8_t* packed,
                         int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s,
                         int batch, const BatchStrides& bs) {
-  using C = TileCfg<WFMT, FN, FM, S>;
+  using C = TileCfg<WFMT, XFMT, FN, FM, S>;
   const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((k_gemm_tile<WFMT, FN, FM, S>), dim3((unsigned)(tm * tn), (unsigned)batch),
+  hipLaunchKernelGGL((k_gemm_tile<WFMT, XFMT, FN, FM, S>), dim3((unsigned)(tm * tn), (unsigned)batch),
                      dim3(512), 0, s, xq, xs, M, K, packed, N, bias, y, tm, tn, group_m, bs);
 }
 
@@ -544,49 +592,63 @@ static TileChoice choose_tile(int M, int N) {
   return pick;
 }
 
-template <int WFMT>
+template <int WFMT, int XFMT>
 static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int K,
                                const uint8_t* packed, int N, const uint16_t* bias, uint16_t* y,
                                hipStream_t s, int batch, const BatchStrides& bs) {
   const TileChoice c = choose_tile(M, N);
   const int group_m = 4;
-  if (c.fn == 8 && c.fm == 4) launch_tile<WFMT, 8, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
-  else if (c.fn == 7 && c.fm == 4) launch_tile<WFMT, 7, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
-  else if (c.fn == 6 && c.fm == 4) launch_tile<WFMT, 6, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
-  else if (c.fn == 4 && c.fm == 4) launch_tile<WFMT, 4, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+  if (c.fn == 8 && c.fm == 4) launch_tile<WFMT, XFMT, 8, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+  else if (c.fn == 7 && c.fm == 4) launch_tile<WFMT, XFMT, 7, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+  else if (c.fn == 6 && c.fm == 4) launch_tile<WFMT, XFMT, 6, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+  else if (c.fn == 4 && c.fm == 4) launch_tile<WFMT, XFMT, 4, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else if ((long)((N + 127) / 128) * ((M + 127) / 128) <= 256)
     // one tile per CU at most: each workgroup runs the whole K of its tile, where a third LDS
     // stage (deeper prefetch) pays off
-    launch_tile<WFMT, 4, 2, 3>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+    launch_tile<WFMT, XFMT, 4, 2, 3>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else
-    launch_tile<WFMT, 4, 2, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+    launch_tile<WFMT, XFMT, 4, 2, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
-                       uint16_t* y, hipStream_t s, int batch, BatchStrides bs) {
+                       uint16_t* y, hipStream_t s, int batch, BatchStrides bs, int afmt) {
+  // (weight, activation) formats: any weight format with E4M3 activations, or FP6 with FP6
+  const int pair = fmt * 4 + afmt;
+  if (afmt != 0 && (fmt == 0 || (afmt != 2 && afmt != 3))) return hipErrorInvalidValue;
   // the small-M kernel splits K over waves (a different summation order); batch-invariant
   // mode keeps every M on the kernels that add the K steps in sequence
-  if (!batch_invariant() && small_m_quantized(M, K))
+  if (afmt == 0 && !batch_invariant() && small_m_quantized(M, K))
     return launch_linear_small_m(xq, xs, true, M, K, packed, N, fmt, bias, y, s, batch, bs);
   const int m = (int)M, k = (int)K, n = (int)N;
   const bool tiled = (K % 128 == 0) && (((uintptr_t)xs & 3) == 0) && M >= 64 && N >= 128;
   if (tiled) {
-    switch (fmt) {
-      case 0: return launch_tiled<0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
-      case 2: return launch_tiled<2>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
-      case 3: return launch_tiled<3>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
+    switch (pair) {
+      case 0: return launch_tiled<0, 0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
+      case 8: return launch_tiled<2, 0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
+      case 12: return launch_tiled<3, 0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
+      case 10: return launch_tiled<2, 2>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
+      case 11: return launch_tiled<2, 3>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
+      case 14: return launch_tiled<3, 2>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
+      case 15: return launch_tiled<3, 3>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
       default: return hipErrorInvalidValue;
     }
   }
   dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)((M + 31) / 32), (unsigned)batch), block(256);
-  switch (fmt) {
-    case 0: hipLaunchKernelGGL(k_gemm_generic<0>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y, bs); break;
-    case 2: hipLaunchKernelGGL(k_gemm_generic<2>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y, bs); break;
-    case 3: hipLaunchKernelGGL(k_gemm_generic<3>, grid, block, 0, s, xq, xs, m, k, packed, n, bias, y, bs); break;
+#define MX_GENERIC(W, X) \
+  hipLaunchKernelGGL((k_gemm_generic<W, X>), grid, block, 0, s, xq, xs, m, k, packed, n, bias, y, bs)
+  switch (pair) {
+    case 0: MX_GENERIC(0, 0); break;
+    case 8: MX_GENERIC(2, 0); break;
+    case 12: MX_GENERIC(3, 0); break;
+    case 10: MX_GENERIC(2, 2); break;
+    case 11: MX_GENERIC(2, 3); break;
+    case 14: MX_GENERIC(3, 2); break;
+    case 15: MX_GENERIC(3, 3); break;
     default: return hipErrorInvalidValue;
   }
+#undef MX_GENERIC
   return hipGetLastError();
 }
 

@@ -24,6 +24,9 @@ struct BatchStrides {
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
                                uint8_t* xs, hipStream_t s);
+// MXFP6 activations (fmt E2M3 = 2 or E3M2 = 3): xq [M, 3K/4] packed codes, xs [M, K/32].
+hipError_t launch_quantize_act_fp6(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt,
+                                   uint8_t* xq, uint8_t* xs, hipStream_t s);
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int fmt,
                                   uint8_t* wq, uint8_t* ws, hipStream_t s);
 hipError_t launch_prepack(const uint8_t* wq, int64_t ldw, const uint8_t* ws, int64_t ld_ws,
@@ -43,10 +46,12 @@ void force_tile(int fn, int fm);
 void set_batch_invariant(bool on);
 bool batch_invariant();
 
-// GEMM from quantized activations xq [M, K] + xs [M, K/32] (row-major).
+// GEMM from quantized activations xq + xs [M, K/32] (row-major): xq is E4M3 [M, K] (afmt 0)
+// or, with FP6 weights, packed E2M3 / E3M2 [M, 3K/4] (afmt 2 / 3).
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
-                       uint16_t* y, hipStream_t s, int batch = 1, BatchStrides bs = {});
+                       uint16_t* y, hipStream_t s, int batch = 1, BatchStrides bs = {},
+                       int afmt = 0);
 
 // Small-M (decode) path: one launch, K split over the waves of a workgroup.  x is bf16 [M, K]
 // quantized inside the kernel (small_m_fused shapes) or, with quantized = true, E4M3 xq [M, K]

@@ -7,6 +7,9 @@
 // inside a quad, and the conversion is the hardware scaled E4M3 convert with the overflow code
 // mapped to the saturated one.
 //
+// MXFP6 activations (the mxfp6 page's activation_quant_key): one lane per block, hardware
+// scaled FP6 conversion.
+//
 // Weights (load time): any element format, one thread per 32-element block, exact float
 // arithmetic per element (speed is irrelevant there; exactness is checked against the oracle).
 #include "mx_device.h"
@@ -56,6 +59,64 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
   if (blocks > 256 * 16) blocks = 256 * 16;  // grid-stride beyond 16 workgroups per CU
   hipLaunchKernelGGL(k_quantize_act, dim3((unsigned)blocks), dim3(256), 0, s, x, K, ldx, groups,
                      xq, xs);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- activations, MXFP6
+// One lane per MX block: 64 bytes of bf16 in (four 16-byte loads), 24 bytes of packed 6-bit codes
+// and the scale byte out.  The scale follows the format's emax (E2M3: 2, E3M2: 4); the codes
+// come from the hardware scaled conversion (v_cvt_scalef32_pk32_{fp6,bf6}_bf16), which gives
+// RNE(x / scale) saturated at the format maximum, sign kept, packed little-endian in 6-bit
+// fields: the same bits as the exact per-element encode for every finite bf16 and every scale
+// byte.  A block holding Inf/NaN gets scale 0xFF and zero codes (FP6 has no NaN).
+template <int FMT>
+__global__ __launch_bounds__(256) void k_quantize_act_fp6(const uint16_t* __restrict__ x, int64_t K,
+                                                          int64_t ldx, int64_t blocks,
+                                                          uint8_t* __restrict__ xq,
+                                                          uint8_t* __restrict__ xs) {
+  typedef __bf16 v32bf __attribute__((ext_vector_type(32)));
+  const int64_t KB = K >> 5;
+  const int64_t ldq = KB * 24;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < blocks;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = b / KB, kb = b - row * KB;
+    const uint16_t* src = x + row * ldx + kb * 32;
+    v4i v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = *(const v4i*)(src + 8 * i);
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t a = amax8_bf16(v[i]);
+      m = m > a ? m : a;
+    }
+    const uint32_t byte = scale_byte_from_amax<FMT>(m);
+    v6i q = {0, 0, 0, 0, 0, 0};
+    if (byte != 0xFFu) {
+      v32bf xv;
+      __builtin_memcpy(&xv, v, 64);
+      const float sc = e8m0_to_float(byte);
+      if constexpr (FMT == 2) q = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xv, sc);
+      else q = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(xv, sc);
+    }
+    uint8_t* dst = xq + row * ldq + kb * 24;   // 8-byte aligned
+    *(v2i*)dst = (v2i){q[0], q[1]};
+    *(v2i*)(dst + 8) = (v2i){q[2], q[3]};
+    *(v2i*)(dst + 16) = (v2i){q[4], q[5]};
+    xs[row * KB + kb] = (uint8_t)byte;
+  }
+}
+
+hipError_t launch_quantize_act_fp6(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt,
+                                   uint8_t* xq, uint8_t* xs, hipStream_t s) {
+  const int64_t blocks = M * (K >> 5);
+  int64_t grid = (blocks + 255) / 256;
+  if (grid > 256 * 16) grid = 256 * 16;
+  switch (fmt) {
+    case 2: hipLaunchKernelGGL(k_quantize_act_fp6<2>, dim3((unsigned)grid), dim3(256), 0, s, x, K, ldx, blocks, xq, xs); break;
+    case 3: hipLaunchKernelGGL(k_quantize_act_fp6<3>, dim3((unsigned)grid), dim3(256), 0, s, x, K, ldx, blocks, xq, xs); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

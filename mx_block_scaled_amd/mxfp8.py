@@ -20,7 +20,8 @@ __all__ = [
     "quantize_weight", "prepack_weight", "unpack_weight", "prepacked_bytes", "workspace_bytes",
     "linear", "linear_prequant", "MxLinear", "set_tile_config", "set_batch_invariant",
     "prepack_weight_shuffled16", "unpack_weight_shuffled16", "linear_batched",
-    "linear_prequant_batched",
+    "linear_prequant_batched", "quantize_act_fmt", "workspace_bytes_fmt", "linear_fmt",
+    "linear_prequant_fmt",
 ]
 
 FMT = {"e4m3": 0, "e2m3": 2, "e3m2": 3}
@@ -63,6 +64,10 @@ def lib():
             "mxfp8_linear_prequant_batched": (I, [P, P, I64, I64, I64, P, I64, I, P, P, P]),
             "mxfp8_prepack_weight_shuffled16": (I, [P, P, I64, I64, I64, P, P]),
             "mxfp8_unpack_weight_shuffled16": (I, [P, I64, I64, P, P, P]),
+            "mxfp8_quantize_act_fmt": (I, [P, I64, I64, I64, I, P, P, P]),
+            "mxfp8_workspace_bytes_fmt": (I64, [I64, I64, I64, I, I]),
+            "mxfp8_linear_fmt": (I, [P, I64, I64, P, I64, I, I, P, P, P, I64, P]),
+            "mxfp8_linear_prequant_fmt": (I, [P, P, I64, I64, I, P, I64, I, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -295,6 +300,68 @@ def linear_prequant_batched(xq, xs, packed, N, fmt="e4m3", bias=None, out=None):
     _check(lib().mxfp8_linear_prequant_batched(xq.data_ptr(), xs.data_ptr(), B, M, K,
                                                packed.data_ptr(), N, f, b, y.data_ptr(),
                                                _stream(xq)))
+    return y
+
+
+# ---------------------------------------------------------------- MXFP6 activations
+# (mxfp6 page, MxFp6LinearLayerConfig.activation_quant_key): activations quantized to E2M3 or
+# E3M2 (packed four codes per three bytes), with FP6 weights; afmt "e4m3" gives the layer above.
+
+def _act_row_bytes(K, afmt):
+    return K if afmt == 0 else K // 4 * 3
+
+
+def workspace_bytes_fmt(M, N, K, fmt, afmt):
+    return int(lib().mxfp8_workspace_bytes_fmt(M, N, K, _fmt(fmt), _fmt(afmt)))
+
+
+def quantize_act_fmt(x, afmt):
+    """bf16 x [..., K] -> (xq uint8 [M, K] E4M3 or [M, 3K/4] packed FP6, xs uint8 [M, K/32])."""
+    x = _bf16(x, "x")
+    a = _fmt(afmt)
+    K = x.shape[-1]
+    x2 = x.reshape(-1, K)
+    M = x2.shape[0]
+    xq = torch.empty((M, _act_row_bytes(K, a)), dtype=torch.uint8, device=x.device)
+    xs = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().mxfp8_quantize_act_fmt(x2.data_ptr(), M, K, K, a, xq.data_ptr(), xs.data_ptr(),
+                                        _stream(x)))
+    return xq, xs
+
+
+def linear_fmt(x, packed, N, fmt, afmt, bias=None, out=None, workspace=None):
+    """linear() with the activations quantized to afmt (FP6 afmt needs an FP6 weight fmt)."""
+    x = _bf16(x, "x")
+    f, a = _fmt(fmt), _fmt(afmt)
+    lead, K = x.shape[:-1], x.shape[-1]
+    x2 = x.reshape(-1, K)
+    M = x2.shape[0]
+    packed = _u8(packed, "packed")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    b = 0 if bias is None else _bf16(bias, "bias").data_ptr()
+    st = _stream(x)
+    need = workspace_bytes_fmt(M, N, K, f, a)
+    ws = workspace if workspace is not None else _workspace(x.device, st.value, need)
+    _check(lib().mxfp8_linear_fmt(x2.data_ptr(), M, K, packed.data_ptr(), N, f, a, b,
+                                  y.data_ptr(), ws.data_ptr(), ws.numel(), st))
+    return y.reshape(*lead, N)
+
+
+def linear_prequant_fmt(xq, xs, packed, N, K, fmt, afmt, bias=None, out=None):
+    """linear_prequant() with activations in format afmt: xq [M, K] E4M3 or [M, 3K/4] FP6."""
+    xq = _u8(xq, "xq")
+    xs = _u8(xs, "xs")
+    f, a = _fmt(fmt), _fmt(afmt)
+    M = xq.shape[0]
+    if tuple(xq.shape) != (M, _act_row_bytes(K, a)) or tuple(xs.shape) != (M, K // 32):
+        raise ValueError("xq %s / xs %s do not match K = %d in format %d"
+                         % (tuple(xq.shape), tuple(xs.shape), K, a))
+    packed = _u8(packed, "packed")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    b = 0 if bias is None else _bf16(bias, "bias").data_ptr()
+    _check(lib().mxfp8_linear_prequant_fmt(xq.data_ptr(), xs.data_ptr(), M, K, a,
+                                           packed.data_ptr(), N, f, b, y.data_ptr(),
+                                           _stream(xq)))
     return y
 
 

@@ -138,3 +138,34 @@ def test_batched_validation(L):
 def test_tile_config_hook(L):
     assert L.mxfp8_set_tile_config(3, 3) == MX_EINVAL
     assert L.mxfp8_set_tile_config(0, 0) == MX_OK
+
+
+def test_fp6_activation_validation(L):
+    """MXFP6 activations (mxfp6 page, activation_quant_key): format pairs, shapes, workspace."""
+    q = L.mxfp8_quantize_act_fmt
+    assert q(A, 4, 64, 64, 1, B, B, None) == MX_EINVAL          # no E5M2
+    assert q(A, 4, 48, 48, 2, B, B, None) == MX_ESHAPE          # K % 32
+    assert q(A, 4, 64, 32, 3, B, B, None) == MX_ESHAPE          # ldx < K
+    assert q(A + 2, 4, 64, 64, 3, B, B, None) == MX_EALIGN
+    assert q(None, 4, 64, 64, 2, B, B, None) == MX_EINVAL
+    assert q(None, 0, 64, 64, 2, None, None, None) == MX_OK      # M == 0: no-op
+    # workspace: packed FP6 codes [M, 3K/4], then the scales at a 256-byte boundary
+    assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 2, 2) == 64 * 384 + 64 * 16
+    assert L.mxfp8_workspace_bytes_fmt(3, 256, 160, 3, 2) == 512 + 3 * 5
+    assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 0, 2) == 0   # FP6 activations: FP6 weights
+    assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 2, 0) == L.mxfp8_workspace_bytes(64, 256, 512, 2)
+    ws = L.mxfp8_workspace_bytes_fmt(64, 256, 512, 2, 3)
+    f = L.mxfp8_linear_fmt
+    assert f(A, 64, 512, B, 256, 0, 2, None, B, B, ws, None) == MX_EINVAL     # E4M3 weight
+    assert f(A, 64, 512, B, 256, 2, 1, None, B, B, ws, None) == MX_EINVAL
+    assert f(A, 64, 512, B, 256, 2, 3, None, B, B, ws - 1, None) == MX_EWORKSPACE
+    assert f(A, 64, 500, B, 256, 2, 3, None, B, B, ws, None) == MX_ESHAPE
+    assert f(A, 64, 512, B, 250, 2, 3, None, B, B, ws, None) == MX_ESHAPE
+    assert f(A, 64, 512, B, 256, 2, 3, None, B + 8, B, ws, None) == MX_EALIGN
+    assert f(None, 0, 512, B, 256, 3, 3, None, B, None, 0, None) == MX_OK
+    p = L.mxfp8_linear_prequant_fmt
+    assert p(A, B, 64, 512, 2, B, 256, 0, None, B, None) == MX_EINVAL        # E4M3 weight
+    assert p(A, None, 64, 512, 2, B, 256, 2, None, B, None) == MX_EINVAL
+    assert p(A + 8, B, 64, 512, 2, B, 256, 2, None, B, None) == MX_EALIGN
+    assert p(A, B, 64, 512, 3, B, 256, 3, None, None, None) == MX_EINVAL     # y
+    assert p(A, B, 0, 512, 3, B, 256, 2, None, B, None) == MX_OK

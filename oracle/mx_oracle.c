@@ -367,6 +367,37 @@ int orc_linear_entries(const uint8_t* xq, const uint8_t* xs, int64_t K, const ui
     return orc_linear_entries_fmt(xq, xs, ORC_E4M3, K, wq, ws, wfmt, bias, rows, cols, count, out);
 }
 
+/* Root-mean-square normalization of bf16 rows: the producer of a pre-quantized activation.
+ * The Mxfp8LinearKernel page's input_quant_key lets a layer take activations quantized outside
+ * the kernel (row-major [M, K/32] E8M0 scales); the pages name no producer, and the reading
+ * here is the usual RMS norm with a bf16 weight, each product rounded to bf16:
+ *     r   = 1 / sqrt(sum_k x_k^2 / K + eps)                 (fp64, IEEE)
+ *     t_k = bf16(x_k * r)                                   (x_k * r in fp64, then RNE)
+ *     y_k = bf16(t_k * gamma_k)                             (the product is exact, then RNE)
+ * pre (optional) receives x_k * r, the value the first rounding acts on. */
+int orc_rmsnorm(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, const uint16_t* gamma,
+                double eps, uint16_t* y, double* pre)
+{
+    if (K <= 0 || ldx < K || !(eps >= 0.0)) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < rows; ++m) {
+        const uint16_t* xr = x + m * ldx;
+        double ss = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double v = orc_bf16_to_double(xr[k]);
+            ss += v * v;
+        }
+        double r = 1.0 / sqrt(ss / (double)K + eps);
+        for (int64_t k = 0; k < K; ++k) {
+            double v = orc_bf16_to_double(xr[k]) * r;
+            if (pre) pre[m * K + k] = v;
+            uint16_t t = orc_double_to_bf16(v);
+            y[m * K + k] = orc_double_to_bf16(orc_bf16_to_double(t) * orc_bf16_to_double(gamma[k]));
+        }
+    }
+    return 0;
+}
+
 int orc_threads(void)
 {
 #ifdef _OPENMP

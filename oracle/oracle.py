@@ -13,7 +13,7 @@ __all__ = [
     "E4M3", "E2M3", "E3M2", "build", "lib", "threads",
     "bf16_to_f64", "f64_to_bf16", "decode", "encode", "encode_many", "scale_byte", "scale_value",
     "quantize", "dequantize", "fp6_pack", "fp6_unpack", "shuffle16", "unshuffle16",
-    "matmul_nt", "linear_entries", "linear_ref",
+    "matmul_nt", "linear_entries", "linear_ref", "rmsnorm",
 ]
 
 E4M3, E2M3, E3M2 = 0, 2, 3
@@ -60,6 +60,7 @@ def lib():
             "orc_linear_entries": (I, [P, P, I64, P, P, I, P, P, P, I64, P]),
             "orc_linear_entries_fmt": (I, [P, P, I, I64, P, P, I, P, P, P, I64, P]),
             "orc_threads": (I, []),
+            "orc_rmsnorm": (I, [P, I64, I64, I64, P, D, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -219,3 +220,17 @@ def linear_ref(x_bf16, wq, ws, wfmt=E4M3, bias_bf16=None, xfmt=E4M3):
     wd = dequantize(wq, ws, wfmt)
     bias = None if bias_bf16 is None else bf16_to_f64(bias_bf16)
     return matmul_nt(xd, wd, bias), xq, xs
+
+
+def rmsnorm(x_bf16, gamma_bf16, eps):
+    """RMS norm of bf16 rows [rows, K] with a bf16 weight [K] (mx_oracle.c, orc_rmsnorm) ->
+    (y bf16 bits [rows, K], x * r in fp64 before the first bf16 rounding)."""
+    x = _c(x_bf16, np.uint16)
+    g = _c(gamma_bf16, np.uint16)
+    rows, K = x.shape
+    assert g.shape == (K,)
+    y = np.empty((rows, K), np.uint16)
+    pre = np.empty((rows, K), np.float64)
+    if lib().orc_rmsnorm(_p(x), rows, K, K, _p(g), float(eps), _p(y), _p(pre)) != 0:
+        raise ValueError("orc_rmsnorm: bad K or eps")
+    return y, pre

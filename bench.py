@@ -21,7 +21,9 @@ Also measured and printed in the same JSON line:
                 only), MXFP6 weights (E2M3 and E3M2, 512 x 8192 x 8192, activation quantization
                 included) with MXFP8 activations and with MXFP6 activations of the same format
                 (both MFMA operands FP6), each over enough rotated sets to exceed the Infinity
-                Cache; and the
+                Cache; the fused RMS norm + MXFP8 quantizer (producer of pre-quantized
+                activations) on the prefill activations against a torch RMS norm followed by
+                the standalone quantizer; and the
                 latency of one tiny call (16 x 256 x 512) from a HIP graph;
   cpu_baseline  the CPU oracle on a bounded sample of the prefill workload (host cores),
                 run in a separate process (oracle/cpu_bench.py).
@@ -328,6 +330,42 @@ def main():
                 "rotated_sets": len(sets)}
             del sets, pk_f, wsf, wsf6
         del xf, wf
+        torch.cuda.empty_cache()
+
+        # fused producer: RMS norm + MXFP8 quantization of the prefill activations, against a
+        # torch RMS norm followed by the standalone quantizer (same rotated buffers)
+        Mp, Kp = 4096, 4096
+        gp = torch.Generator(device=dev)
+        gp.manual_seed(0)
+        gam = (torch.rand(Kp, generator=gp, device=dev) + 0.5).to(torch.bfloat16)
+        xp_bytes = Mp * Kp * 2
+        sets = rotated(lambda j: (torch.randn((Mp, Kp), generator=gp, device=dev).to(torch.bfloat16),
+                                  torch.empty((Mp, Kp), dtype=torch.uint8, device=dev),
+                                  torch.empty((Mp, Kp // 32), dtype=torch.uint8, device=dev)),
+                       xp_bytes + Mp * Kp + Mp * Kp // 32)
+        L = mxfp8.lib()
+        st = torch.cuda.current_stream(dev).cuda_stream
+
+        def fused(j):
+            x_, q_, s_ = sets[j]
+            rc = L.mxfp8_rmsnorm_quantize_act(x_.data_ptr(), Mp, Kp, Kp, gam.data_ptr(), 1e-6,
+                                              q_.data_ptr(), s_.data_ptr(), None, st)
+            assert rc == 0, L.mxfp8_last_error()
+
+        def separate(j):
+            x_, q_, s_ = sets[j]
+            yn = torch.nn.functional.rms_norm(x_, (Kp,), gam, 1e-6)
+            rc = L.mxfp8_quantize_act(yn.data_ptr(), Mp, Kp, Kp, q_.data_ptr(), s_.data_ptr(), st)
+            assert rc == 0, L.mxfp8_last_error()
+
+        us_f = time_calls(fused, len(sets), max(50, args.steps))
+        us_s = time_calls(separate, len(sets), max(50, args.steps))
+        alg = 3.03125 * Mp * Kp + 2 * Kp
+        others["producer_rmsnorm_quant_4096x4096"] = {
+            "us": round(us_f, 2), "GB/s": round(alg / us_f / 1e3, 1),
+            "hbm_frac": round(alg / us_f / 1e3 / PEAK_HBM_GBS, 4),
+            "us_torch_rms_norm_then_quantizer": round(us_s, 2), "rotated_sets": len(sets)}
+        del sets, gam
         torch.cuda.empty_cache()
 
         # tiny: latency of one call (HIP graph of 64 calls)

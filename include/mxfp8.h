@@ -72,6 +72,21 @@ const char* mxfp8_last_error(void);
 int mxfp8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
                        void* xq, void* xs, void* stream);
 
+/* Fused producer of a pre-quantized activation: RMS norm, then the quantization above (the
+ * Mxfp8LinearKernel page's input_quant_key: a layer may take activations quantized outside
+ * it, with row-major [M, K/32] E8M0 scales; the pages name no producer, and the norm here is
+ * the usual RMS norm with a bf16 weight, each product rounded to bf16):
+ *     r = 1 / sqrt(sum_k x_k^2 / K + eps)   (fp64),   y_k = bf16(bf16(x_k r) gamma_k),
+ * then y is quantized exactly as mxfp8_quantize_act quantizes a bf16 input.
+ *   x_bf16 [16]  bf16 [M, ldx] (ldx >= K, ldx % 8 == 0)
+ *   gamma  [16]  bf16 [K]
+ *   eps          finite, >= 0
+ *   xq [16], xs  out: E4M3 [M, K], E8M0 [M, K/32], both row-major (feed mxfp8_linear_prequant)
+ *   y_bf16 [16]  optional out: the normalized rows y, bf16 [M, K]; NULL = not written */
+int mxfp8_rmsnorm_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
+                               const void* gamma_bf16, float eps, void* xq, void* xs,
+                               void* y_bf16, void* stream);
+
 /* The same MX quantization for weights, in any supported element format, producing the
  * checkpoint layout that mxfp8_prepack_weight takes (compressed_tensors_w8a8_mxfp8 page,
  * create_weights; mxfp6 page for E2M3 / E3M2):

@@ -393,6 +393,25 @@ int mxfp8_linear_prequant_fmt(const void* xq, const void* xs, int64_t M, int64_t
                     "gemm launch");
 }
 
+int mxfp8_rmsnorm_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
+                               const void* gamma_bf16, float eps, void* xq, void* xs,
+                               void* y_bf16, void* stream) {
+  int rc = check_mk(M, K);
+  if (rc) return rc;
+  if (!(eps >= 0.0f) || eps > 1e30f) return fail(MX_EINVAL, "eps = %g must be finite and >= 0", (double)eps);
+  if (M == 0) return ok();
+  if (!x_bf16 || !gamma_bf16 || !xq || !xs) return fail(MX_EINVAL, "null pointer (x, gamma, xq or xs)");
+  if (ldx < K) return fail(MX_ESHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  if (ldx % 8 != 0 || !aligned16(x_bf16) || !aligned16(gamma_bf16) || !aligned16(xq) ||
+      (y_bf16 && !aligned16(y_bf16)))
+    return fail(MX_EALIGN, "x, gamma, xq, y must be 16-byte aligned and ldx a multiple of 8");
+  if ((rc = check_arch())) return rc;
+  return hip_status(mx::launch_rmsnorm_quant((const uint16_t*)x_bf16, M, K, ldx,
+                                             (const uint16_t*)gamma_bf16, eps, (uint8_t*)xq,
+                                             (uint8_t*)xs, (uint16_t*)y_bf16, (hipStream_t)stream),
+                    "rmsnorm_quantize_act launch");
+}
+
 int mxfp8_set_batch_invariant(int on) {
   mx::set_batch_invariant(on != 0);
   return ok();

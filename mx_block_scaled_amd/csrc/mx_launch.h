@@ -27,6 +27,11 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
 // MXFP6 activations (fmt E2M3 = 2 or E3M2 = 3): xq [M, 3K/4] packed codes, xs [M, K/32].
 hipError_t launch_quantize_act_fp6(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt,
                                    uint8_t* xq, uint8_t* xs, hipStream_t s);
+// RMS norm (bf16 weight gamma [K], eps) fused with the E4M3 activation quantization; y
+// (optional) receives the normalized bf16 rows [M, K].
+hipError_t launch_rmsnorm_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                const uint16_t* gamma, float eps, uint8_t* xq, uint8_t* xs,
+                                uint16_t* y, hipStream_t s);
 hipError_t launch_quantize_weight(const uint16_t* w, int64_t N, int64_t K, int64_t ldw, int fmt,
                                   uint8_t* wq, uint8_t* ws, hipStream_t s);
 hipError_t launch_prepack(const uint8_t* wq, int64_t ldw, const uint8_t* ws, int64_t ld_ws,

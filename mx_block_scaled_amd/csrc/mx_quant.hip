@@ -120,6 +120,108 @@ hipError_t launch_quantize_act_fp6(const uint16_t* x, int64_t M, int64_t K, int6
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- fused producer: RMS norm
+// The producer of a pre-quantized activation (the Mxfp8LinearKernel page's input_quant_key lets
+// a layer take activations quantized outside it): r = 1 / sqrt(mean(x^2) + eps) in fp64, rounded
+// once to fp32; y = bf16(bf16(fp32(x r)) gamma); then y quantized as k_quantize_act does.  One
+// wave per row.  Pass 1: sum of squares in fp64, each lane over its columns in order, then a
+// fixed xor butterfly (every lane ends with the same bits).  Pass 2: the two products in fp32
+// (x r is one rounding; t gamma is exact), each rounded to bf16 by the hardware convert (RNE).
+
+// CH > 0: the row (K <= 512 CH) is loaded once, all chunks in flight together, and kept in
+// registers for the second pass; CH == 0: any K, chunk by chunk, re-read in the second pass.
+template <int CH>
+__global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t* __restrict__ x, int M,
+                                                       int K, int64_t ldx,
+                                                       const uint16_t* __restrict__ gamma,
+                                                       double eps, uint8_t* __restrict__ xq,
+                                                       uint8_t* __restrict__ xs,
+                                                       uint16_t* __restrict__ yout) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;   // whole wave; nothing below synchronizes across waves
+  const uint16_t* xr = x + (int64_t)row * ldx;
+  const int chunks = CH > 0 ? CH : (K + 511) >> 9;   // 512 columns per wave-wide pass
+  constexpr int RC = CH > 0 ? CH : 1;
+  v4i xv[RC];
+  if constexpr (CH > 0) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int col = 512 * c + 8 * lane;
+      xv[c] = col < K ? *(const v4i*)(xr + col) : (v4i){0, 0, 0, 0};
+    }
+  }
+  double ss = 0.0;
+#pragma unroll
+  for (int c = 0; c < chunks; ++c) {
+    const int col = 512 * c + 8 * lane;
+    v4i v = {0, 0, 0, 0};
+    if constexpr (CH > 0) v = xv[c];
+    else if (col < K) v = *(const v4i*)(xr + col);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double lo = (double)bf16_to_float((uint32_t)v[i] & 0xFFFFu);
+      const double hi = (double)bf16_to_float((uint32_t)v[i] >> 16);
+      ss = __builtin_fma(lo, lo, ss);
+      ss = __builtin_fma(hi, hi, ss);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  const double r = 1.0 / __builtin_sqrt(ss / (double)K + eps);
+  const float r32 = (float)r;
+  const int KB = K >> 5;
+#pragma unroll
+  for (int c = 0; c < chunks; ++c) {
+    // every lane runs every chunk (the quad reduction needs whole quads); lanes past K work on
+    // a clamped column and store nothing
+    const int col = 512 * c + 8 * lane;
+    const bool live = col < K;
+    const int cc = live ? col : K - 8;
+    v4i v;
+    if constexpr (CH > 0) v = xv[c];
+    else v = *(const v4i*)(xr + cc);
+    const v4i gw = *(const v4i*)(gamma + cc);
+    v4i y8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t w = (uint32_t)v[i], gq = (uint32_t)gw[i];
+      const uint32_t t = pack_bf16x2(__uint_as_float(w << 16) * r32,
+                                     __uint_as_float(w & 0xFFFF0000u) * r32);
+      y8[i] = (int)pack_bf16x2(__uint_as_float(t << 16) * __uint_as_float(gq << 16),
+                               __uint_as_float(t & 0xFFFF0000u) * __uint_as_float(gq & 0xFFFF0000u));
+    }
+    const uint32_t m = quad_max_u32(amax8_bf16(y8));
+    const uint32_t byte = scale_byte_from_amax<0>(m);
+    uint32_t q0, q1;
+    if (byte == 0xFFu) {
+      q0 = q1 = 0x7F7F7F7Fu;
+    } else {
+      const float sc = e8m0_to_float(byte);
+      q0 = cvt4_e4m3((uint32_t)y8[0], (uint32_t)y8[1], sc);
+      q1 = cvt4_e4m3((uint32_t)y8[2], (uint32_t)y8[3], sc);
+    }
+    if (live) {
+      *(v2i*)(xq + (int64_t)row * K + col) = (v2i){(int)q0, (int)q1};
+      if ((lane & 3) == 0) xs[(int64_t)row * KB + (col >> 5)] = (uint8_t)byte;
+      if (yout) *(v4i*)(yout + (int64_t)row * K + col) = y8;
+    }
+  }
+}
+
+hipError_t launch_rmsnorm_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                                const uint16_t* gamma, float eps, uint8_t* xq, uint8_t* xs,
+                                uint16_t* y, hipStream_t s) {
+  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
+  if (K <= 4096)
+    hipLaunchKernelGGL(k_rmsnorm_quant<8>, grid, block, 0, s, x, (int)M, (int)K, ldx, gamma, (double)eps, xq, xs, y);
+  else if (K <= 8192)
+    hipLaunchKernelGGL(k_rmsnorm_quant<16>, grid, block, 0, s, x, (int)M, (int)K, ldx, gamma, (double)eps, xq, xs, y);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_quant<0>, grid, block, 0, s, x, (int)M, (int)K, ldx, gamma, (double)eps, xq, xs, y);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- weights, any format
 
 template <int FMT>

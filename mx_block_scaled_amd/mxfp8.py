@@ -21,7 +21,7 @@ __all__ = [
     "linear", "linear_prequant", "MxLinear", "set_tile_config", "set_batch_invariant",
     "prepack_weight_shuffled16", "unpack_weight_shuffled16", "linear_batched",
     "linear_prequant_batched", "quantize_act_fmt", "workspace_bytes_fmt", "linear_fmt",
-    "linear_prequant_fmt",
+    "linear_prequant_fmt", "rmsnorm_quantize_act",
 ]
 
 FMT = {"e4m3": 0, "e2m3": 2, "e3m2": 3}
@@ -68,6 +68,7 @@ def lib():
             "mxfp8_workspace_bytes_fmt": (I64, [I64, I64, I64, I, I]),
             "mxfp8_linear_fmt": (I, [P, I64, I64, P, I64, I, I, P, P, P, I64, P]),
             "mxfp8_linear_prequant_fmt": (I, [P, P, I64, I64, I, P, I64, I, P, P, P]),
+            "mxfp8_rmsnorm_quantize_act": (I, [P, I64, I64, I64, P, ctypes.c_float, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -138,6 +139,26 @@ def quantize_act(x):
     _check(lib().mxfp8_quantize_act(x2.data_ptr(), M, K, K, xq.data_ptr(), xs.data_ptr(),
                                     _stream(x)))
     return xq, xs
+
+
+def rmsnorm_quantize_act(x, gamma, eps=1e-6, return_y=False):
+    """Fused RMS norm + MXFP8 quantization of bf16 x [..., K] with bf16 weight gamma [K]:
+    (xq [M, K] E4M3, xs [M, K/32] E8M0) ready for linear_prequant, plus the normalized bf16
+    rows y [M, K] when return_y."""
+    x = _bf16(x, "x")
+    gamma = _bf16(gamma, "gamma")
+    K = x.shape[-1]
+    if tuple(gamma.shape) != (K,):
+        raise ValueError("gamma must be [K]")
+    x2 = x.reshape(-1, K)
+    M = x2.shape[0]
+    xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    xs = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    y = torch.empty((M, K), dtype=torch.bfloat16, device=x.device) if return_y else None
+    _check(lib().mxfp8_rmsnorm_quantize_act(x2.data_ptr(), M, K, K, gamma.data_ptr(), float(eps),
+                                            xq.data_ptr(), xs.data_ptr(),
+                                            0 if y is None else y.data_ptr(), _stream(x)))
+    return (xq, xs, y) if return_y else (xq, xs)
 
 
 def quantize_weight(w, fmt="e4m3"):

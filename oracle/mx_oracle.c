@@ -370,11 +370,11 @@ int orc_linear_entries(const uint8_t* xq, const uint8_t* xs, int64_t K, const ui
 /* Root-mean-square normalization of bf16 rows: the producer of a pre-quantized activation.
  * The Mxfp8LinearKernel page's input_quant_key lets a layer take activations quantized outside
  * the kernel (row-major [M, K/32] E8M0 scales); the pages name no producer, and the reading
- * here is the usual RMS norm with a bf16 weight, each product rounded to bf16:
- *     r   = 1 / sqrt(sum_k x_k^2 / K + eps)                 (fp64, IEEE)
- *     t_k = bf16(x_k * r)                                   (x_k * r in fp64, then RNE)
- *     y_k = bf16(t_k * gamma_k)                             (the product is exact, then RNE)
- * pre (optional) receives x_k * r, the value the first rounding acts on. */
+ * here is the usual RMS norm with a bf16 weight, computed as a float norm does it:
+ *     r   = 1 / sqrt(sum_k x_k^2 / K + eps)       (fp64), then r32 = fp32(r) (nearest even)
+ *     p_k = fp32(x_k * r32)                       (the product is exact in fp64; one rounding)
+ *     t_k = bf16(p_k),  y_k = bf16(t_k * gamma_k) (round to nearest even; t * gamma is exact)
+ * pre (optional) receives p_k, the value the bf16 rounding of t acts on. */
 int orc_rmsnorm(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, const uint16_t* gamma,
                 double eps, uint16_t* y, double* pre)
 {
@@ -388,10 +388,11 @@ int orc_rmsnorm(const uint16_t* x, int64_t rows, int64_t K, int64_t ldx, const u
             ss += v * v;
         }
         double r = 1.0 / sqrt(ss / (double)K + eps);
+        double r32 = (double)(float)r;
         for (int64_t k = 0; k < K; ++k) {
-            double v = orc_bf16_to_double(xr[k]) * r;
-            if (pre) pre[m * K + k] = v;
-            uint16_t t = orc_double_to_bf16(v);
+            double p = (double)(float)(orc_bf16_to_double(xr[k]) * r32);
+            if (pre) pre[m * K + k] = p;
+            uint16_t t = orc_double_to_bf16(p);
             y[m * K + k] = orc_double_to_bf16(orc_bf16_to_double(t) * orc_bf16_to_double(gamma[k]));
         }
     }

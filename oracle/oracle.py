@@ -224,7 +224,7 @@ def linear_ref(x_bf16, wq, ws, wfmt=E4M3, bias_bf16=None, xfmt=E4M3):
 
 def rmsnorm(x_bf16, gamma_bf16, eps):
     """RMS norm of bf16 rows [rows, K] with a bf16 weight [K] (mx_oracle.c, orc_rmsnorm) ->
-    (y bf16 bits [rows, K], x * r in fp64 before the first bf16 rounding)."""
+    (y bf16 bits [rows, K], p = fp32(x * fp32(r)) as float64, the value t = bf16(p) rounds)."""
     x = _c(x_bf16, np.uint16)
     g = _c(gamma_bf16, np.uint16)
     rows, K = x.shape

@@ -169,3 +169,16 @@ def test_fp6_activation_validation(L):
     assert p(A + 8, B, 64, 512, 2, B, 256, 2, None, B, None) == MX_EALIGN
     assert p(A, B, 64, 512, 3, B, 256, 3, None, None, None) == MX_EINVAL     # y
     assert p(A, B, 0, 512, 3, B, 256, 2, None, B, None) == MX_OK
+
+
+def test_rmsnorm_quantize_validation(L):
+    f = L.mxfp8_rmsnorm_quantize_act
+    assert f(A, 4, 64, 64, B, -1.0, B, B, None, None) == MX_EINVAL           # eps < 0
+    assert f(A, 4, 64, 64, B, float("nan"), B, B, None, None) == MX_EINVAL
+    assert f(A, 4, 64, 64, B, float("inf"), B, B, None, None) == MX_EINVAL
+    assert f(A, 4, 64, 64, None, 1e-6, B, B, None, None) == MX_EINVAL        # gamma
+    assert f(A, 4, 48, 48, B, 1e-6, B, B, None, None) == MX_ESHAPE           # K % 32
+    assert f(A, 4, 64, 32, B, 1e-6, B, B, None, None) == MX_ESHAPE           # ldx < K
+    assert f(A, 4, 64, 64, B + 2, 1e-6, B, B, None, None) == MX_EALIGN
+    assert f(A, 4, 64, 64, B, 1e-6, B, B, A + 8, None) == MX_EALIGN          # y
+    assert f(None, 0, 64, 64, None, 1e-6, None, None, None, None) == MX_OK   # M == 0

@@ -15,10 +15,6 @@
 
 namespace mx {
 
-// ---------------------------------------------------------------- generic kernel
-// Any M, K % 32 == 0, N % 16 == 0.  Workgroup = 4 waves = 64 weight rows x 32 activation rows;
-// each wave owns one 16-row weight fragment and two 16-row activation tiles, streaming both
-// operands straight from global memory into registers (no LDS).
 // Offsets the operand pointers (kernel parameters) to batch b (byte strides; all zero when
 // unbatched).
 #define MX_BATCH_OFFSET(b)                                                   \
@@ -31,70 +27,90 @@ namespace mx {
     if (bias) bias = (const uint16_t*)((const uint8_t*)bias + b_ * bs.bias); \
   } while (0)
 
-template <int WFMT, int XFMT>
-__global__ __launch_bounds__(256) void k_gemm_generic(const uint8_t* __restrict__ xq,
-                                                      const uint8_t* __restrict__ xs, int M, int K,
-                                                      const uint8_t* __restrict__ packed, int N,
-                                                      const uint16_t* __restrict__ bias,
-                                                      uint16_t* __restrict__ y, BatchStrides bs) {
+// ---------------------------------------------------------------- generic kernel
+// Any M, K % 32 == 0, N % 16 == 0.  One wave per workgroup: a 16-row weight fragment and MT
+// 16-row activation tiles, both operands streamed straight from global memory into registers
+// (no LDS).  The loads of U K steps go out together before their MFMAs, which then run in K
+// order (each output's sum is the same MFMA chain as in the tiled kernel, so rows do not depend
+// on M).  With one fragment per workgroup the weight stream spreads over N / 16 CUs; U = 16
+// with one activation tile (M <= 16), 8 with two, keeps the registers under 256.
+template <int WFMT, int XFMT, int MT>
+__global__ __launch_bounds__(64) void k_gemm_generic(const uint8_t* __restrict__ xq,
+                                                     const uint8_t* __restrict__ xs, int M, int K,
+                                                     const uint8_t* __restrict__ packed, int N,
+                                                     const uint16_t* __restrict__ bias,
+                                                     uint16_t* __restrict__ y, BatchStrides bs) {
   constexpr int FB = frag_bytes(WFMT);
+  constexpr int U = MT == 1 ? 16 : 8;
   MX_BATCH_OFFSET(blockIdx.z);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
   const int r = lane & 15, g = lane >> 4;
   const int NG = N >> 4, KT = (K + 127) >> 7, KB = K >> 5;
   const int LDX = XFMT == 0 ? K : K / 4 * 3;   // activation row bytes
-  const int ng = blockIdx.x * 4 + w;
-  if (ng >= NG) return;  // whole wave leaves; nothing below synchronizes across waves
-  const int m0 = blockIdx.y * 32;
+  const int ng = blockIdx.x;
+  const int m0 = blockIdx.y * 16 * MT;
   const uint8_t* wfr = packed + (int64_t)ng * FB;
   const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * FB) + (int64_t)ng * 64 + lane;
   // activation rows of this lane (clamped so every address is inside x; data is zeroed instead)
-  int mrow[2];
-  bool mok[2];
+  int mrow[MT];
+  bool mok[MT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < MT; ++t) {
     const int m = m0 + 16 * t + r;
     mok[t] = m < M;
     mrow[t] = mok[t] ? m : M - 1;
   }
-  v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint8_t* f = wfr + (int64_t)kt * NG * FB;
-    v8i a;
-    if (WFMT == 0) {
-      const v4i lo = *(const v4i*)(f + lane * 16);
-      const v4i hi = *(const v4i*)(f + 1024 + lane * 16);
-      a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    } else {
-      const v4i lo = *(const v4i*)(f + lane * 16);
-      const v2i hi = *(const v2i*)(f + 1024 + lane * 8);
-      a = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
-    }
-    const int sa = (int)((wsc[(int64_t)(kt >> 2) * NG * 64] >> (8 * (kt & 3))) & 0xFFu);
-    const int kb = 4 * kt + g;
+  v4f acc[MT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint8_t* xr = xq + (int64_t)mrow[t] * LDX;
-      v8i b;
-      if constexpr (XFMT == 0) {
-        v4i b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
-        const int k0 = 128 * kt + 16 * g, k1 = k0 + 64;
-        if (mok[t] && k0 < K) b0 = *(const v4i*)(xr + k0);
-        if (mok[t] && k1 < K) b1 = *(const v4i*)(xr + k1);
-        b = (v8i){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+  for (int t = 0; t < MT; ++t) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int kt0 = 0; kt0 < KT; kt0 += U) {
+    // loads of steps kt0 .. kt0 + U - 1 (steps past the end re-read the last one, unused)
+    v8i a[U], b[U][MT];
+    int sa[U], sb[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int kt = min(kt0 + u, KT - 1);
+      const uint8_t* f = wfr + (int64_t)kt * NG * FB;
+      if (WFMT == 0) {
+        const v4i lo = *(const v4i*)(f + lane * 16);
+        const v4i hi = *(const v4i*)(f + 1024 + lane * 16);
+        a[u] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       } else {
-        // FP6 operand: block kb's 24 packed bytes (8-byte aligned: rows are 24 K/32 bytes)
-        v2i d0 = {0, 0}, d1 = {0, 0}, d2 = {0, 0};
-        if (mok[t] && kb < KB) {
-          const uint8_t* p = xr + 24 * kb;
-          d0 = *(const v2i*)p;
-          d1 = *(const v2i*)(p + 8);
-          d2 = *(const v2i*)(p + 16);
-        }
-        b = (v8i){d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], 0, 0};
+        const v4i lo = *(const v4i*)(f + lane * 16);
+        const v2i hi = *(const v2i*)(f + 1024 + lane * 8);
+        a[u] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
       }
-      const int sb = kb < KB ? (int)xs[(int64_t)mrow[t] * KB + kb] : 127;
-      acc[t] = mfma16<WFMT, XFMT>(a, b, acc[t], sa, sb);
+      sa[u] = (int)((wsc[(int64_t)(kt >> 2) * NG * 64] >> (8 * (kt & 3))) & 0xFFu);
+      const int kb = 4 * kt + g;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const uint8_t* xr = xq + (int64_t)mrow[t] * LDX;
+        if constexpr (XFMT == 0) {
+          v4i b0 = {0, 0, 0, 0}, b1 = {0, 0, 0, 0};
+          const int k0 = 128 * kt + 16 * g, k1 = k0 + 64;
+          if (mok[t] && k0 < K) b0 = *(const v4i*)(xr + k0);
+          if (mok[t] && k1 < K) b1 = *(const v4i*)(xr + k1);
+          b[u][t] = (v8i){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        } else {
+          // FP6 operand: block kb's 24 packed bytes (8-byte aligned: rows are 24 K/32 bytes)
+          v2i d0 = {0, 0}, d1 = {0, 0}, d2 = {0, 0};
+          if (mok[t] && kb < KB) {
+            const uint8_t* p = xr + 24 * kb;
+            d0 = *(const v2i*)p;
+            d1 = *(const v2i*)(p + 8);
+            d2 = *(const v2i*)(p + 16);
+          }
+          b[u][t] = (v8i){d0[0], d0[1], d1[0], d1[1], d2[0], d2[1], 0, 0};
+        }
+        sb[u][t] = kb < KB ? (int)xs[(int64_t)mrow[t] * KB + kb] : 127;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (kt0 + u < KT) {   // wave-uniform
+#pragma unroll
+        for (int t = 0; t < MT; ++t) acc[t] = mfma16<WFMT, XFMT>(a[u], b[u][t], acc[t], sa[u], sb[u][t]);
+      }
     }
   }
   // epilogue: lane holds n = 16 ng + 4 g + i (i < 4) of activation row m0 + 16 t + r
@@ -105,7 +121,7 @@ __global__ __launch_bounds__(256) void k_gemm_generic(const uint8_t* __restrict_
     for (int i = 0; i < 4; ++i) bv[i] = bf16_to_float(bias[n + i]);
   }
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < MT; ++t) {
     if (!mok[t]) continue;
     const v2i o = {(int)pack_bf16x2(acc[t][0] + bv[0], acc[t][1] + bv[1]),
                    (int)pack_bf16x2(acc[t][2] + bv[2], acc[t][3] + bv[3])};
@@ -635,9 +651,17 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t 
       default: return hipErrorInvalidValue;
     }
   }
-  dim3 grid((unsigned)((N / 16 + 3) / 4), (unsigned)((M + 31) / 32), (unsigned)batch), block(256);
-#define MX_GENERIC(W, X) \
-  hipLaunchKernelGGL((k_gemm_generic<W, X>), grid, block, 0, s, xq, xs, m, k, packed, n, bias, y, bs)
+  // one 16-row activation tile per workgroup for M <= 32 (more K steps in flight; at M > 16 two
+  // workgroups read each weight fragment, the second mostly from L2), else two
+  const int mt = M <= 32 ? 1 : 2;
+  dim3 grid((unsigned)(N / 16), (unsigned)((M + 16 * mt - 1) / (16 * mt)), (unsigned)batch), block(64);
+#define MX_GENERIC(W, X)                                                                              \
+  do {                                                                                                \
+    if (mt == 1)                                                                                      \
+      hipLaunchKernelGGL((k_gemm_generic<W, X, 1>), grid, block, 0, s, xq, xs, m, k, packed, n, bias, y, bs); \
+    else                                                                                              \
+      hipLaunchKernelGGL((k_gemm_generic<W, X, 2>), grid, block, 0, s, xq, xs, m, k, packed, n, bias, y, bs); \
+  } while (0)
   switch (pair) {
     case 0: MX_GENERIC(0, 0); break;
     case 8: MX_GENERIC(2, 0); break;

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t* __restric
     }
   }
   double ss = 0.0;
-#pragma unroll
+#pragma unroll RC
   for (int c = 0; c < chunks; ++c) {
     const int col = 512 * c + 8 * lane;
     v4i v = {0, 0, 0, 0};
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t* __restric
   const double r = 1.0 / __builtin_sqrt(ss / (double)K + eps);
   const float r32 = (float)r;
   const int KB = K >> 5;
-#pragma unroll
+#pragma unroll RC
   for (int c = 0; c < chunks; ++c) {
     // every lane runs every chunk (the quad reduction needs whole quads); lanes past K work on
     // a clamped column and store nothing

@@ -74,12 +74,12 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
   const int n = 16 * ng + 4 * g;   // first of this lane's 4 output columns
   const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * FB) + (int64_t)ng * 64 + lane;
 
-  // bias of this lane's output columns, fetched first (the waves that finish a tile use it)
-  float bv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (bias && wave < MT) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) bv[i] = bf16_to_float(bias[n + i]);
-  }
+  // bias of this lane's 4 output columns (the waves that finish a tile use it): one 8-byte load
+  // issued behind the first weight loads, so its latency hides under theirs
+  const bool want_bias = bias != nullptr && wave < MT;
+  const bool bias8 = ((uintptr_t)bias & 7) == 0;
+  v2i braw = {0, 0};
+  bool have_bias = false;
 
   // activation rows of this lane's B operands; rows past M read row M - 1 instead: a B-operand
   // row only feeds its own output column, and those columns are never stored
@@ -133,6 +133,9 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
         if (m < M) xr[m][0][0] = *(const v4i*)((const uint16_t*)xin + (int64_t)m * K + col);
     }
     __builtin_amdgcn_sched_barrier(0);
+    // the group's weight scale word first: loads retire in order, so it is in by the time the
+    // weight is
+    const uint32_t sw = wsc[(int64_t)kt4 * NG * 64];
     v8i a[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -147,7 +150,10 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
         a[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
       }
     }
-    const uint32_t sw = wsc[(int64_t)kt4 * NG * 64];
+    if (want_bias && bias8 && !have_bias) {
+      braw = *(const v2i*)(bias + n);
+      have_bias = true;
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (!QX) {
@@ -195,6 +201,20 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
           acc[t] = mfma_wsel<WFMT>(j, a[j], b, acc[t], sw, sb);
         }
       }
+    }
+  }
+
+  float bv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (want_bias) {
+    if (!have_bias && bias8) braw = *(const v2i*)(bias + n);   // a wave with no K group
+    if (bias8) {
+      bv[0] = bf16_to_float((uint32_t)braw[0] & 0xFFFFu);
+      bv[1] = bf16_to_float((uint32_t)braw[0] >> 16);
+      bv[2] = bf16_to_float((uint32_t)braw[1] & 0xFFFFu);
+      bv[3] = bf16_to_float((uint32_t)braw[1] >> 16);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bv[i] = bf16_to_float(bias[n + i]);
     }
   }
 

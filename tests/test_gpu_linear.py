@@ -320,3 +320,26 @@ def test_batched(M, N, K):
     ref, _, _ = orc.linear_ref(xs_[1], layers[1][1], layers[1][2], 0, bs_[1])
     ok, rep = tolerance.check(host_bf16_bits(y[1]), ref, name="batched-%d-%d-%d" % (M, N, K))
     assert ok, rep
+
+
+@pytest.mark.parametrize("M", [5, 24, 300])
+def test_bias_at_odd_offset(M):
+    """A bias that starts 2 bytes past an 8-byte boundary (a slice of a larger tensor): the
+    small-M kernels' 8-byte bias load falls back to element loads."""
+    g = np.random.default_rng(M)
+    N, K = 144, 512
+    x = synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    w = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    bfull = synth.bf16_bits((g.standard_normal(N + 1) * 0.1).astype(np.float32))
+    wq, ws = orc.quantize(w)
+    layer = mxfp8.MxLinear(u8_dev(wq), u8_dev(ws), 0)
+    bias_t = bf16_dev(bfull)[1:]
+    assert bias_t.data_ptr() % 8 == 2
+    banner("bias at odd offset", M)
+    y = mxfp8.linear(bf16_dev(x), layer.packed, N, 0, bias_t)
+    ref, xq, xs = orc.linear_ref(x, wq, ws, 0, bfull[1:])
+    ok, rep = tolerance.check(host_bf16_bits(y), ref, name="bias-odd-%d" % M)
+    assert ok, rep
+    y2 = mxfp8.linear_prequant(u8_dev(xq), u8_dev(xs), layer.packed, N, 0, bias_t)
+    ok, rep = tolerance.check(host_bf16_bits(y2), ref, name="bias-odd-prequant-%d" % M)
+    assert ok, rep

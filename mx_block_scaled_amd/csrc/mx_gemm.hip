@@ -130,11 +130,11 @@ __global__ __launch_bounds__(64) void k_gemm_generic(const uint8_t* __restrict__
 }
 
 // ---------------------------------------------------------------- LDS-tiled kernel (large M)
-// Workgroup tile: 256 weight rows (n) x 256 activation rows (m), K step 128, 4 waves, each wave a
-// 128 x 128 quadrant = 8 x 8 MFMA tiles (256 fp32 accumulators per lane).  Both operand tiles
-// are copied global -> LDS with the 16-byte direct-to-LDS load (lane i of an instruction lands
-// at LDS base + 16 i), double buffered:
-//   A (weight): 16 prepacked fragments of one K step are contiguous in global memory, so the
+// Workgroup tile: 32 FN weight rows (n) x 64 FM activation rows (m), K step 128, 8 waves in a
+// 2 (n) x 4 (m) grid, each wave FN x FM MFMA tiles of 16 x 16 (TileCfg below).  Both operand
+// tiles are copied global -> LDS with the 16-byte direct-to-LDS load (lane i of an instruction
+// lands at LDS base + 16 i), in S stages:
+//   A (weight): the prepacked fragments of one K step are contiguous in global memory, so the
 //     LDS image is a plain copy and each lane's MFMA operand is one (or two) lane-contiguous
 //     16-byte LDS reads — conflict-free.
 //   B (activations, row-major [M, K]): 128-byte row slices; the 16-byte chunk c of row r is kept
@@ -237,6 +237,11 @@ __device__ __forceinline__ typename AReg<XFMT>::type lds_b_operand(const uint8_t
 template <int WFMT, int XFMT, int FN, int FM, int S>
 struct TileCfg {
   static constexpr int NW = 8, WGN = 2, WGM = 4;
+  // The copies are issued by waves 0-3 only, one per SIMD (waves w and w + 4 share a SIMD):
+  // a wave stalls while it issues a copy, and the SIMD's other wave keeps the matrix pipe busy
+  // meanwhile (all eight waves issuing their share measured 5-6 % slower, two or one slower
+  // still).
+  static constexpr int NDW = 4;
   static constexpr int FB = frag_bytes(WFMT);
   static constexpr int XB = XFMT == 0 ? 128 : 96;  // activation bytes per row per K step
   static constexpr int BN = 16 * FN * WGN, BM = 16 * FM * WGM;
@@ -244,24 +249,24 @@ struct TileCfg {
   static constexpr int B_BYTES = BM * 128;         // BM activation rows x 128 bytes
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int A_CHUNKS = A_BYTES / 1024;  // 1 KiB DMA instructions
-  static constexpr int A_PER_WAVE = (A_CHUNKS + NW - 1) / NW;   // surplus slots -> scratch
-  static constexpr int B_PER_WAVE = B_BYTES / 1024 / NW;
-  static constexpr int D = A_PER_WAVE + B_PER_WAVE;   // vector-memory ops per wave per step
+  static constexpr int A_PER_WAVE = (A_CHUNKS + NDW - 1) / NDW;   // surplus slots -> scratch
+  static constexpr int B_PER_WAVE = B_BYTES / 1024 / NDW;
+  static constexpr int D = A_PER_WAVE + B_PER_WAVE;   // vector-memory ops per copy wave per step
   // scales of 4 K steps ("group"), staged in LDS with 4-byte DMA (256 B per instruction): the
   // weight's BN/16 fragments x 64 lane words, the activations' BM rows x 16 B
   static constexpr int SA_PIECES = BN / 16, SB_PIECES = BM / 16;
-  static constexpr int SA_PER_WAVE = (SA_PIECES + NW - 1) / NW;
-  static constexpr int SB_PER_WAVE = (SB_PIECES + NW - 1) / NW;
+  static constexpr int SA_PER_WAVE = (SA_PIECES + NDW - 1) / NDW;
+  static constexpr int SB_PER_WAVE = (SB_PIECES + NDW - 1) / NDW;
   static constexpr int SA_BYTES = SA_PIECES * 256, SB_BYTES = SB_PIECES * 256;
   static constexpr int SCALE_BYTES = SA_BYTES + SB_BYTES;
-  static constexpr int SL = SA_PER_WAVE + SB_PER_WAVE;  // scale DMAs per wave per group
+  static constexpr int SL = SA_PER_WAVE + SB_PER_WAVE;  // scale DMAs per copy wave per group
   static constexpr int SCRATCH = 1024;                  // target of surplus DMA slots
   // epilogue: bf16 tile [BM][BN]; a row pitch of 16 (mod 256) bytes puts the 8-byte writes of
   // a wave (16 rows x 4 column groups) on distinct bank pairs
   static constexpr int OUT_PITCH = (BN * 2 - 16 + 255) / 256 * 256 + 16;
   static constexpr int LDS_MAIN = S * STAGE + 2 * SCALE_BYTES + SCRATCH;
   static constexpr int LDS_BYTES = LDS_MAIN > BM * OUT_PITCH ? LDS_MAIN : BM * OUT_PITCH;
-  static_assert(A_BYTES % 1024 == 0 && B_BYTES % (1024 * NW) == 0, "1 KiB DMA chunks");
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % (1024 * NDW) == 0, "1 KiB DMA chunks");
   static_assert(S >= 2 && LDS_BYTES <= 160 * 1024, "must fit the 160 KiB LDS");
   // vector-memory ops issued after the DMA of step kt when step kt starts (q = kt % 4): the
   // DMAs of the next S - 2 steps, plus one group of scale DMAs if one was issued in between
@@ -318,14 +323,14 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   // ---- per-lane DMA sources, as 32-bit offsets from uniform bases (every operand < 2^31 B):
   // each DMA address is then a 64-bit scalar base plus a 32-bit lane offset, the instruction's
   // own base + offset form, and no 64-bit per-lane address stays live
-  // A: wave w copies 1 KiB chunks w, w + 8, ... of the stage's A block (fragments clamped to
+  // A: copy wave w copies 1 KiB chunks w, w + 4, ... of the stage's A block (fragments clamped to
   // NG); chunk indices past the block are surplus slots aimed at the scratch area
   // (E4M3 fragments are 2 KiB, so a chunk lies in one fragment and the offset is uniform +
   // lane * 16; FP6 fragments are 1.5 KiB and a chunk may straddle two, so the offset is per lane)
   uint32_t a_off[C::A_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::A_PER_WAVE; ++i) {
-    const int c = min(wave + C::NW * i, C::A_CHUNKS - 1);
+    const int c = min(wave + C::NDW * i, C::A_CHUNKS - 1);
     if (C::FB % 1024 == 0) {
       const int f = c * 1024 / C::FB;
       a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (c * 1024 - f * C::FB));
@@ -336,13 +341,13 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     }
   }
   const uint32_t a_lane = C::FB % 1024 == 0 ? (uint32_t)lane * 16 : 0u;
-  // B: wave w copies rows 8 c .. 8 c + 7 for c = w, w + 8, ..., lane -> (row, slot); an FP6
+  // B: copy wave w copies rows 8 c .. 8 c + 7 for c = w, w + 4, ..., lane -> (row, slot); an FP6
   // row has 6 chunks, so the lanes of slots holding chunks 6 and 7 stay idle
   uint32_t b_off[C::B_PER_WAVE];
   bool b_on[C::B_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::B_PER_WAVE; ++i) {
-    const int row = 8 * (wave + C::NW * i) + (lane >> 3);
+    const int row = 8 * (wave + C::NDW * i) + (lane >> 3);
     const int chunk = (lane & 7) ^ swz(row);
     b_on[i] = chunk < C::XB / 16;
     b_off[i] = (uint32_t)(min(m0 + row, M - 1) * LDX + min(chunk, C::XB / 16 - 1) * 16);
@@ -351,18 +356,20 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   auto issue_one = [&](int kt, int stage, int p) __attribute__((always_inline)) {
     uint8_t* base = lds + stage * C::STAGE;
     if (p < C::A_PER_WAVE) {
-      const int c = wave + C::NW * p;     // wave-uniform
+      const int c = wave + C::NDW * p;     // wave-uniform
       dma16(packed + (uint32_t)(kt * NG * C::FB + a_off[p] + a_lane),
             c < C::A_CHUNKS ? base + c * 1024 : scratch);
     } else {
       const int i = p - C::A_PER_WAVE;
       if (XFMT == 0 || b_on[i])
-        dma16(xq + (uint32_t)(kt * C::XB + b_off[i]), base + C::A_BYTES + (wave + C::NW * i) * 1024);
+        dma16(xq + (uint32_t)(kt * C::XB + b_off[i]), base + C::A_BYTES + (wave + C::NDW * i) * 1024);
     }
   };
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    if (wave < C::NDW) {
 #pragma unroll
-    for (int p = 0; p < C::D; ++p) issue_one(kt, stage, p);
+      for (int p = 0; p < C::D; ++p) issue_one(kt, stage, p);
+    }
   };
 
   // ---- per-lane scale DMA sources (4-byte DMA: one instruction moves 64 lanes x 4 B = 256 B)
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   uint32_t sa_src[C::SA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::SA_PER_WAVE; ++i) {
-    const int c = min(wave + C::NW * i, C::SA_PIECES - 1);
+    const int c = min(wave + C::NDW * i, C::SA_PIECES - 1);
     sa_src[i] = (uint32_t)(min((n0 >> 4) + c, NG - 1) * 256 + lane * 4);
   }
   // activations: piece c moves rows 16 c .. 16 c + 15, 4 words (16 B) each; lane l takes row
@@ -378,22 +385,23 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   uint32_t sb_src[C::SB_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::SB_PER_WAVE; ++i) {
-    const int c = min(wave + C::NW * i, C::SB_PIECES - 1);
+    const int c = min(wave + C::NDW * i, C::SB_PIECES - 1);
     sb_src[i] = (uint32_t)(min(m0 + 16 * c + (lane >> 2), M - 1) * KB);
   }
   const int q4 = (lane & 3) * 4;
   auto issue_scales = [&](int kt4, int sbuf) __attribute__((always_inline)) {
     uint8_t* base = slds + sbuf * C::SCALE_BYTES;
+    if (wave >= C::NDW) return;
 #pragma unroll
     for (int i = 0; i < C::SA_PER_WAVE; ++i) {
-      const int c = wave + C::NW * i;
+      const int c = wave + C::NDW * i;
       dma4((const uint8_t*)wsc + (uint32_t)(kt4 * NG * 256 + sa_src[i]),
            c < C::SA_PIECES ? base + c * 256 : scratch);
     }
     const int col = min(16 * kt4 + q4, KB - 4);
 #pragma unroll
     for (int i = 0; i < C::SB_PER_WAVE; ++i) {
-      const int c = wave + C::NW * i;
+      const int c = wave + C::NDW * i;
       dma4(xs + (uint32_t)(sb_src[i] + col), c < C::SB_PIECES ? base + C::SA_BYTES + c * 256 : scratch);
     }
   };

@@ -506,12 +506,13 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   uint32_t sa[FN], sb[FM];
   const int KT4 = (KT + 3) >> 2;
   const int KT4f = KT >> 2;               // groups of four whole K steps
-  // prologue: scales of group 0 (waited for and read), then the DMAs of steps 0 .. S-2
+  // prologue: scales of group 0 and the DMAs of steps 0 .. S-2 go out together; the scales
+  // are waited for (the tile DMAs of steps 1 .. S-2 may still be in flight) and read
   issue_scales(0, 0);
-  wait_vm_barrier<0>();
-  read_scales(0, 0, sa, sb);
 #pragma unroll
   for (int st = 0; st < S - 1; ++st) issue(min(st, KT - 1), st);
+  wait_vm_barrier<(S - 1) * C::D>();
+  read_scales(0, 0, sa, sb);
 
   // One K step of a full group.  At the top, the tiles of step kt have landed once at most
   // vm_after(q) later memory operations are outstanding (vmcnt retires in issue order); the

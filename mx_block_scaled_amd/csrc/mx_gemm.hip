@@ -252,12 +252,13 @@ struct TileCfg {
   static constexpr int A_PER_WAVE = (A_CHUNKS + NDW - 1) / NDW;   // surplus slots -> scratch
   static constexpr int B_PER_WAVE = B_BYTES / 1024 / NDW;
   static constexpr int D = A_PER_WAVE + B_PER_WAVE;   // vector-memory ops per copy wave per step
-  // scales of 4 K steps ("group"), staged in LDS with 4-byte DMA (256 B per instruction): the
-  // weight's BN/16 fragments x 64 lane words, the activations' BM rows x 16 B
-  static constexpr int SA_PIECES = BN / 16, SB_PIECES = BM / 16;
+  // scales of 4 K steps ("group") staged in LDS: the weight's BN/16 fragments x 64 lane words,
+  // moved 4 fragments (1 KiB) per 16-byte DMA; the activations' BM rows x 16 B, moved 16 rows
+  // (256 B) per 4-byte DMA, since a row's 16 bytes need not be 16-byte aligned
+  static constexpr int SA_PIECES = (BN / 16 + 3) / 4, SB_PIECES = BM / 16;
   static constexpr int SA_PER_WAVE = (SA_PIECES + NDW - 1) / NDW;
   static constexpr int SB_PER_WAVE = (SB_PIECES + NDW - 1) / NDW;
-  static constexpr int SA_BYTES = SA_PIECES * 256, SB_BYTES = SB_PIECES * 256;
+  static constexpr int SA_BYTES = SA_PIECES * 1024, SB_BYTES = SB_PIECES * 256;
   static constexpr int SCALE_BYTES = SA_BYTES + SB_BYTES;
   static constexpr int SL = SA_PER_WAVE + SB_PER_WAVE;  // scale DMAs per copy wave per group
   static constexpr int SCRATCH = 1024;                  // target of surplus DMA slots
@@ -372,13 +373,14 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     }
   };
 
-  // ---- per-lane scale DMA sources (4-byte DMA: one instruction moves 64 lanes x 4 B = 256 B)
-  // weight: piece c moves fragment n0/16 + c's 64 lane words
+  // ---- per-lane scale DMA sources
+  // weight (16-byte DMA): chunk c moves fragments n0/16 + 4 c .. + 3, the 64 lane words of each
+  // (fragments past N are clamped; their words land beyond the tile's and are never read)
   uint32_t sa_src[C::SA_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < C::SA_PER_WAVE; ++i) {
     const int c = min(wave + C::NDW * i, C::SA_PIECES - 1);
-    sa_src[i] = (uint32_t)(min((n0 >> 4) + c, NG - 1) * 256 + lane * 4);
+    sa_src[i] = (uint32_t)(min((n0 >> 4) + 4 * c + (lane >> 4), NG - 1) * 256 + (lane & 15) * 16);
   }
   // activations: piece c moves rows 16 c .. 16 c + 15, 4 words (16 B) each; lane l takes row
   // 16 c + l / 4, word l % 4 (columns clamped inside the row at issue time)
@@ -395,8 +397,8 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
 #pragma unroll
     for (int i = 0; i < C::SA_PER_WAVE; ++i) {
       const int c = wave + C::NDW * i;
-      dma4((const uint8_t*)wsc + (uint32_t)(kt4 * NG * 256 + sa_src[i]),
-           c < C::SA_PIECES ? base + c * 256 : scratch);
+      dma16((const uint8_t*)wsc + (uint32_t)(kt4 * NG * 256 + sa_src[i]),
+            c < C::SA_PIECES ? base + c * 1024 : scratch);
     }
     const int col = min(16 * kt4 + q4, KB - 4);
 #pragma unroll

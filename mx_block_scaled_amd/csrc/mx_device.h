@@ -90,11 +90,11 @@ __device__ __forceinline__ float bf16_to_float(uint32_t b16) { return __uint_as_
 
 // fp32 -> bf16 bits, round to nearest even (hardware conversion).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  uint16_t ua, ub;
-  __builtin_memcpy(&ua, &a, 2);
-  __builtin_memcpy(&ub, &b, 2);
-  return (uint32_t)ua | ((uint32_t)ub << 16);
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  const v2bf b = __builtin_convertvector((v2f){lo, hi}, v2bf);   // one v_cvt_pk_bf16_f32
+  uint32_t u;
+  __builtin_memcpy(&u, &b, 4);
+  return u;
 }
 
 // max over the 4 lanes of a quad (lanes 4j..4j+3), unsigned.

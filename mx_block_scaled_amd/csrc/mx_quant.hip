@@ -123,38 +123,43 @@ hipError_t launch_quantize_act_fp6(const uint16_t* x, int64_t M, int64_t K, int6
 // ---------------------------------------------------------------- fused producer: RMS norm
 // The producer of a pre-quantized activation (the Mxfp8LinearKernel page's input_quant_key lets
 // a layer take activations quantized outside it): r = 1 / sqrt(mean(x^2) + eps) in fp64, rounded
-// once to fp32; y = bf16(bf16(fp32(x r)) gamma); then y quantized as k_quantize_act does.  One
-// wave per row.  Pass 1: sum of squares in fp64, each lane over its columns in order, then a
-// fixed xor butterfly (every lane ends with the same bits).  Pass 2: the two products in fp32
-// (x r is one rounding; t gamma is exact), each rounded to bf16 by the hardware convert (RNE).
+// once to fp32; y = bf16(bf16(fp32(x r)) gamma); then y quantized as k_quantize_act does.
+// Pass 1: sum of squares in fp64 (a fixed order, so every lane ends with the same bits).  Pass 2:
+// the two products in fp32 (x r is one rounding; t gamma is exact), each rounded to bf16 by the
+// hardware convert (RNE).
 
-// CH > 0: the row (K <= 512 CH) is loaded once, all chunks in flight together, and kept in
-// registers for the second pass; CH == 0: any K, chunk by chunk, re-read in the second pass.
-template <int CH>
-__global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t* __restrict__ x, int M,
-                                                       int K, int64_t ldx,
-                                                       const uint16_t* __restrict__ gamma,
-                                                       double eps, uint8_t* __restrict__ xq,
-                                                       uint8_t* __restrict__ xs,
-                                                       uint16_t* __restrict__ yout) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= M) return;   // whole wave; nothing below synchronizes across waves
+// One row per workgroup of WPR waves; lane L = 64 h + lane of wave h takes columns
+// 512 WPR c + 8 L .. + 7 of pass c.  CH > 0: the row (K <= 512 WPR CH) is loaded once, all
+// chunks in flight together, and kept in registers for the second pass; CH == 0: any K, chunk
+// by chunk, re-read in the second pass.  The sum of squares: four fp64 partial sums per lane,
+// a fixed xor butterfly per wave, then the waves' sums added in wave order.
+template <int CH, int WPR>
+__global__ __launch_bounds__(64 * WPR) void k_rmsnorm_quant(const uint16_t* __restrict__ x, int M,
+                                                            int K, int64_t ldx,
+                                                            const uint16_t* __restrict__ gamma,
+                                                            double eps, uint8_t* __restrict__ xq,
+                                                            uint8_t* __restrict__ xs,
+                                                            uint16_t* __restrict__ yout) {
+  __shared__ double part[WPR];
+  const int lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+  const int L = 64 * h + lane;
+  constexpr int SPAN = 512 * WPR;
+  const int row = blockIdx.x;
   const uint16_t* xr = x + (int64_t)row * ldx;
-  const int chunks = CH > 0 ? CH : (K + 511) >> 9;   // 512 columns per wave-wide pass
+  const int chunks = CH > 0 ? CH : (K + SPAN - 1) / SPAN;
   constexpr int RC = CH > 0 ? CH : 1;
   v4i xv[RC];
   if constexpr (CH > 0) {
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const int col = 512 * c + 8 * lane;
+      const int col = SPAN * c + 8 * L;
       xv[c] = col < K ? *(const v4i*)(xr + col) : (v4i){0, 0, 0, 0};
     }
   }
-  double ss = 0.0;
+  double s4[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll RC
   for (int c = 0; c < chunks; ++c) {
-    const int col = 512 * c + 8 * lane;
+    const int col = SPAN * c + 8 * L;
     v4i v = {0, 0, 0, 0};
     if constexpr (CH > 0) v = xv[c];
     else if (col < K) v = *(const v4i*)(xr + col);
@@ -162,12 +167,20 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t* __restric
     for (int i = 0; i < 4; ++i) {
       const double lo = (double)bf16_to_float((uint32_t)v[i] & 0xFFFFu);
       const double hi = (double)bf16_to_float((uint32_t)v[i] >> 16);
-      ss = __builtin_fma(lo, lo, ss);
-      ss = __builtin_fma(hi, hi, ss);
+      s4[i] = __builtin_fma(lo, lo, s4[i]);
+      s4[i] = __builtin_fma(hi, hi, s4[i]);
     }
   }
+  double ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if constexpr (WPR > 1) {
+    if (lane == 0) part[h] = ss;
+    __syncthreads();
+    ss = part[0];
+#pragma unroll
+    for (int w = 1; w < WPR; ++w) ss += part[w];
+  }
   const double r = 1.0 / __builtin_sqrt(ss / (double)K + eps);
   const float r32 = (float)r;
   const int KB = K >> 5;
@@ -175,7 +188,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t* __restric
   for (int c = 0; c < chunks; ++c) {
     // every lane runs every chunk (the quad reduction needs whole quads); lanes past K work on
     // a clamped column and store nothing
-    const int col = 512 * c + 8 * lane;
+    const int col = SPAN * c + 8 * L;
     const bool live = col < K;
     const int cc = live ? col : K - 8;
     v4i v;
@@ -209,16 +222,26 @@ __global__ __launch_bounds__(256) void k_rmsnorm_quant(const uint16_t* __restric
   }
 }
 
+template <int WPR>
+static void launch_rms(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                       float eps, uint8_t* xq, uint8_t* xs, uint16_t* y, hipStream_t s) {
+  const dim3 grid((unsigned)M), block(64 * WPR);
+  if (K <= 4096)
+    hipLaunchKernelGGL((k_rmsnorm_quant<8 / WPR, WPR>), grid, block, 0, s, x, (int)M, (int)K, ldx, gamma, (double)eps, xq, xs, y);
+  else if (K <= 8192)
+    hipLaunchKernelGGL((k_rmsnorm_quant<16 / WPR, WPR>), grid, block, 0, s, x, (int)M, (int)K, ldx, gamma, (double)eps, xq, xs, y);
+  else
+    hipLaunchKernelGGL((k_rmsnorm_quant<0, WPR>), grid, block, 0, s, x, (int)M, (int)K, ldx, gamma, (double)eps, xq, xs, y);
+}
+
 hipError_t launch_rmsnorm_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                 const uint16_t* gamma, float eps, uint8_t* xq, uint8_t* xs,
                                 uint16_t* y, hipStream_t s) {
-  const dim3 grid((unsigned)((M + 3) / 4)), block(256);
-  if (K <= 4096)
-    hipLaunchKernelGGL(k_rmsnorm_quant<8>, grid, block, 0, s, x, (int)M, (int)K, ldx, gamma, (double)eps, xq, xs, y);
-  else if (K <= 8192)
-    hipLaunchKernelGGL(k_rmsnorm_quant<16>, grid, block, 0, s, x, (int)M, (int)K, ldx, gamma, (double)eps, xq, xs, y);
-  else
-    hipLaunchKernelGGL(k_rmsnorm_quant<0>, grid, block, 0, s, x, (int)M, (int)K, ldx, gamma, (double)eps, xq, xs, y);
+  if (M == 0) return hipSuccess;
+  // about 16 elements per lane: more waves in flight hide the load latency and the serial
+  // per-row work (measured on 4096 x 4096: 15.3 us with 4 waves per row, 18.6 us with one)
+  if (K <= 4096) launch_rms<4>(x, M, K, ldx, gamma, eps, xq, xs, y, s);
+  else launch_rms<8>(x, M, K, ldx, gamma, eps, xq, xs, y, s);
   return hipGetLastError();
 }
 

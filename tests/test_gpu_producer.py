@@ -41,7 +41,8 @@ def _inputs(M, K, seed, outliers=False):
 
 @pytest.mark.parametrize("M,K,eps,outliers", [(64, 4096, 1e-6, False), (37, 608, 1e-5, True),
                                               (5, 32, 0.0, False), (300, 1024, 1e-6, True),
-                                              (4096, 4096, 1e-6, False)])
+                                              (4096, 4096, 1e-6, False), (33, 8192, 1e-6, True),
+                                              (6, 5120, 1e-6, False), (3, 12320, 1e-5, True)])
 def test_rmsnorm_quantize(M, K, eps, outliers):
     x, gamma = _inputs(M, K, M + K, outliers)
     banner("rmsnorm+quant", M, K, eps, outliers)

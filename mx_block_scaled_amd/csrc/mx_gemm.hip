@@ -64,7 +64,8 @@ __global__ __launch_bounds__(64) void k_gemm_generic(const uint8_t* __restrict__
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
   for (int kt0 = 0; kt0 < KT; kt0 += U) {
-    // loads of steps kt0 .. kt0 + U - 1 (steps past the end re-read the last one, unused)
+    // loads of steps kt0 .. kt0 + U - 1 (steps past the end re-read the last one, unused); the
+    // weight, used once per call, with non-temporal loads
     v8i a[U], b[U][MT];
     int sa[U], sb[U][MT];
 #pragma unroll
@@ -72,12 +73,12 @@ __global__ __launch_bounds__(64) void k_gemm_generic(const uint8_t* __restrict__
       const int kt = min(kt0 + u, KT - 1);
       const uint8_t* f = wfr + (int64_t)kt * NG * FB;
       if (WFMT == 0) {
-        const v4i lo = *(const v4i*)(f + lane * 16);
-        const v4i hi = *(const v4i*)(f + 1024 + lane * 16);
+        const v4i lo = __builtin_nontemporal_load((const v4i*)(f + lane * 16));
+        const v4i hi = __builtin_nontemporal_load((const v4i*)(f + 1024 + lane * 16));
         a[u] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       } else {
-        const v4i lo = *(const v4i*)(f + lane * 16);
-        const v2i hi = *(const v2i*)(f + 1024 + lane * 8);
+        const v4i lo = __builtin_nontemporal_load((const v4i*)(f + lane * 16));
+        const v2i hi = __builtin_nontemporal_load((const v2i*)(f + 1024 + lane * 8));
         a[u] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
       }
       sa[u] = (int)((wsc[(int64_t)(kt >> 2) * NG * 64] >> (8 * (kt & 3))) & 0xFFu);
@@ -574,12 +575,16 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     }
   }
   __syncthreads();
+  // non-temporal stores: the output streams out instead of displacing the operand panels that
+  // the running tiles still read from the caches (about 8 % on the prefill GEMM with operands
+  // and outputs rotated over more memory than the Infinity Cache holds)
   constexpr int ROW_PIECES = C::BN * 2 / 16;          // 16-byte pieces per tile row
 #pragma unroll 4
   for (int p = tid; p < C::BM * ROW_PIECES; p += C::NW * 64) {
     const int ml = p / ROW_PIECES, cp = p - ml * ROW_PIECES;
     const int m = m0 + ml, n = n0 + cp * 8;
-    if (m < M && n < N) *(v4i*)(y + (int64_t)m * N + n) = *(const v4i*)(lds + ml * C::OUT_PITCH + cp * 16);
+    if (m < M && n < N)
+      __builtin_nontemporal_store(*(const v4i*)(lds + ml * C::OUT_PITCH + cp * 16), (v4i*)(y + (int64_t)m * N + n));
   }
 }
 

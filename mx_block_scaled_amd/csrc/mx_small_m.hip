@@ -10,6 +10,8 @@
 //    scale word) before using any of it, so the full weight is in flight at once;
 //  * the 8 per-wave partial sums are added in LDS in wave order (a split-K whose reduction
 //    order is fixed, so results do not depend on timing), then bias, one bf16 rounding, store.
+//  * the weight is read with non-temporal loads: each byte is used once per call, and the hint
+//    keeps it from displacing cached data (about 10 % per call at M = 1, 4096 x 4096).
 // Activations come either as bf16 (M <= 16: quantized inside the kernel, bit-identical to
 // k_quantize_act) or pre-quantized (E4M3 xq + row-major E8M0 xs, M <= 32).
 //
@@ -141,12 +143,12 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
     for (int j = 0; j < 4; ++j) {
       const int kt = min(4 * kt4 + j, KT - 1);
       const uint8_t* f = packed + ((int64_t)kt * NG + ng) * FB;
-      const v4i lo = *(const v4i*)(f + lane * 16);
+      const v4i lo = __builtin_nontemporal_load((const v4i*)(f + lane * 16));
       if (WFMT == 0) {
-        const v4i hi = *(const v4i*)(f + 1024 + lane * 16);
+        const v4i hi = __builtin_nontemporal_load((const v4i*)(f + 1024 + lane * 16));
         a[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       } else {
-        const v2i hi = *(const v2i*)(f + 1024 + lane * 8);
+        const v2i hi = __builtin_nontemporal_load((const v2i*)(f + 1024 + lane * 8));
         a[j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
       }
     }

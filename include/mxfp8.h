@@ -134,8 +134,13 @@ int mxfp8_unpack_weight_shuffled16(const void* packed, int64_t N, int64_t K, voi
 
 /* ---------------------------------------------------------------- the linear layer */
 
-/* Workspace bytes mxfp8_linear needs for (M, N, K, fmt) (0 when none is needed).
- * The workspace holds the quantized activations between the quantizer and the GEMM. */
+/* Workspace bytes mxfp8_linear needs for (M, N, K, fmt) (0 for M == 0 or invalid arguments).
+ * Layout: 64 KiB of counters, then the quantized activations between the quantizer and the
+ * GEMM, or, for decode shapes (16 <= M <= 32, N % 64 == 0, K % 128 == 0), the partial sums of
+ * the workgroups that split K.  The counters must be zero before a workspace is first used
+ * (allocate it zero-filled); every call leaves them zero, so a workspace stays valid for any
+ * later call of any entry point, shape or stream order.  The same layout serves
+ * mxfp8_linear_batched and mxfp8_linear_fmt. */
 int64_t mxfp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt);
 
 /* y = dequant(quantize(x)) . dequant(W)^T (+ bias), bf16 out (aiter_flydsl page,
@@ -144,7 +149,8 @@ int64_t mxfp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt);
  *   packed    [16]  from mxfp8_prepack_weight with the same N, K, fmt
  *   bias            bf16 [N] or NULL; added in fp32 before the single bf16 rounding
  *   y         [16]  out: bf16 [M, N] row-major (round to nearest even)
- *   workspace [16]  device buffer of ws_bytes >= mxfp8_workspace_bytes(M, N, K, fmt) */
+ *   workspace [16]  device buffer of ws_bytes >= mxfp8_workspace_bytes(M, N, K, fmt), its first
+ *                   64 KiB zero before its first use (see mxfp8_workspace_bytes) */
 int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N,
                  int fmt, const void* bias, void* y, void* workspace, int64_t ws_bytes,
                  void* stream);

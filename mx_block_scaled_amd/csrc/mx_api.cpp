@@ -74,9 +74,27 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 int64_t quant_ws_bytes(int64_t M, int64_t K, int afmt = MX_FMT_E4M3) {
-  // xq [M, K] (E4M3) or [M, 3K/4] (FP6), then xs [M, K/32] at a 256-byte boundary
+  // the counter prefix, xq [M, K] (E4M3) or [M, 3K/4] (FP6), then xs [M, K/32] at a 256-byte
+  // boundary
   const int64_t row = afmt == MX_FMT_E4M3 ? K : K / 4 * 3;
-  return ((M * row + 255) / 256) * 256 + M * (K / 32);
+  return mx::kWorkspacePrefix + ((M * row + 255) / 256) * 256 + M * (K / 32);
+}
+
+// decode shapes that mxfp8_linear runs on the kernel splitting K across workgroups (outside
+// batch-invariant mode).  Its cross-workgroup sum costs about 2 us of memory round trips at
+// the end (store, count, load); below 16 rows the single-workgroup split of the small-M kernel
+// is faster (4096 x 4096: 6.3 against 7.6 us at M = 8; 8.2 against 7.7 at M = 16, 10.7 against
+// 9.2 at M = 32, where the small-M path needs a separate quantizer launch)
+constexpr int64_t kSkMinM = 16;
+bool sk_shape(int64_t M, int64_t N, int64_t K) { return M >= kSkMinM && mx::decode_sk_ok(M, N, K); }
+
+int64_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
+  int64_t need = quant_ws_bytes(M, K);
+  if (sk_shape(M, N, K)) {
+    const int64_t sk = mx::kWorkspacePrefix + mx::decode_sk_workspace(M, N, K);
+    if (sk > need) need = sk;
+  }
+  return need;
 }
 
 // (weight, activation) format pairs with kernels: E4M3 activations with any weight format,
@@ -204,7 +222,7 @@ int mxfp8_unpack_weight_shuffled16(const void* packed, int64_t N, int64_t K, voi
 int64_t mxfp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
   if (!valid_fmt(fmt) || check_mk(M, K) || check_nk(N, K)) return 0;
   if (M == 0) return 0;
-  return quant_ws_bytes(M, K);
+  return linear_ws_bytes(M, N, K);
 }
 
 static int check_linear_common(int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
@@ -227,18 +245,23 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, i
   if (M == 0) return ok();
   if (!x_bf16) return fail(MX_EINVAL, "null pointer (x)");
   if (!aligned16(x_bf16)) return fail(MX_EALIGN, "x must be 16-byte aligned");
-  const int64_t need = quant_ws_bytes(M, K);
+  const int64_t need = linear_ws_bytes(M, N, K);
   if (!workspace || ws_bytes < need)
     return fail(MX_EWORKSPACE, "workspace of %lld bytes given, %lld needed", (long long)ws_bytes, (long long)need);
   if (!aligned16(workspace)) return fail(MX_EALIGN, "workspace must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
   hipStream_t s = (hipStream_t)stream;
+  if (!mx::batch_invariant() && sk_shape(M, N, K))   // decode: K split across workgroups
+    return hip_status(mx::launch_linear_decode_sk((const uint16_t*)x_bf16, M, K,
+                                                  (const uint8_t*)packed, N, fmt,
+                                                  (const uint16_t*)bias, (uint16_t*)y, workspace, s),
+                      "linear (decode, split K) launch");
   if (!mx::batch_invariant() && mx::small_m_fused(M, K))   // decode: quantizer fused in
     return hip_status(mx::launch_linear_small_m(x_bf16, nullptr, false, M, K,
                                                 (const uint8_t*)packed, N, fmt,
                                                 (const uint16_t*)bias, (uint16_t*)y, s),
                       "linear (small M) launch");
-  uint8_t* xq = (uint8_t*)workspace;
+  uint8_t* xq = (uint8_t*)workspace + mx::kWorkspacePrefix;
   uint8_t* xs = xq + ((M * K + 255) / 256) * 256;
   hipError_t e = mx::launch_quantize_act((const uint16_t*)x_bf16, M, K, K, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "quantize_act launch");
@@ -290,7 +313,7 @@ int mxfp8_linear_batched(const void* x_bf16, int64_t B, int64_t M, int64_t K, co
                                                 (const uint16_t*)bias, (uint16_t*)y, s, (int)B, bs),
                       "linear (batched, small M) launch");
   }
-  uint8_t* xq = (uint8_t*)workspace;
+  uint8_t* xq = (uint8_t*)workspace + mx::kWorkspacePrefix;
   uint8_t* xs = xq + ((B * M * K + 255) / 256) * 256;
   hipError_t e = mx::launch_quantize_act((const uint16_t*)x_bf16, B * M, K, K, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "quantize_act launch");
@@ -346,6 +369,7 @@ int64_t mxfp8_workspace_bytes_fmt(int64_t M, int64_t N, int64_t K, int fmt, int 
   if (!valid_fmt(fmt) || !valid_fmt(afmt) || check_mk(M, K) || check_nk(N, K)) return 0;
   if (afmt != MX_FMT_E4M3 && fmt == MX_FMT_E4M3) return 0;
   if (M == 0) return 0;
+  if (afmt == MX_FMT_E4M3) return linear_ws_bytes(M, N, K);   // mxfp8_linear's
   return quant_ws_bytes(M, K, afmt);
 }
 
@@ -366,7 +390,7 @@ int mxfp8_linear_fmt(const void* x_bf16, int64_t M, int64_t K, const void* packe
   if (!aligned16(workspace)) return fail(MX_EALIGN, "workspace must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
   hipStream_t s = (hipStream_t)stream;
-  uint8_t* xq = (uint8_t*)workspace;
+  uint8_t* xq = (uint8_t*)workspace + mx::kWorkspacePrefix;
   uint8_t* xs = xq + ((M * (K / 4 * 3) + 255) / 256) * 256;
   hipError_t e = mx::launch_quantize_act_fp6((const uint16_t*)x_bf16, M, K, K, afmt, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "quantize_act (FP6) launch");

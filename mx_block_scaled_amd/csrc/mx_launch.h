@@ -61,6 +61,19 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t 
 // Small-M (decode) path: one launch, K split over the waves of a workgroup.  x is bf16 [M, K]
 // quantized inside the kernel (small_m_fused shapes) or, with quantized = true, E4M3 xq [M, K]
 // plus xs [M, K/32] (small_m_quantized shapes).
+// Every workspace starts with this many bytes of counters, which must be zero before the
+// workspace's first use; every call leaves them zero.  The rest holds the quantized activations
+// or the decode kernel's partial sums.
+constexpr int64_t kWorkspacePrefix = 64 * 1024;
+
+// Decode with K also split across workgroups, quantizer fused (M <= 32, K % 128 == 0,
+// N % 64 == 0): the counters of the workspace prefix, then decode_sk_workspace bytes of
+// partial sums.
+bool decode_sk_ok(int64_t M, int64_t N, int64_t K);
+int64_t decode_sk_workspace(int64_t M, int64_t N, int64_t K);
+hipError_t launch_linear_decode_sk(const uint16_t* x, int64_t M, int64_t K, const uint8_t* packed,
+                                   int64_t N, int fmt, const uint16_t* bias, uint16_t* y,
+                                   void* workspace, hipStream_t s);
 bool small_m_fused(int64_t M, int64_t K);
 bool small_m_quantized(int64_t M, int64_t K);
 hipError_t launch_linear_small_m(const void* x, const uint8_t* xs, bool quantized, int64_t M,

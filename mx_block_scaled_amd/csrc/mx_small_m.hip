@@ -238,6 +238,250 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Decode with the K dimension also split across workgroups (M <= 32, bf16 activations).
+// Workgroup (b, p) computes 64 output columns (weight fragments 4 b .. 4 b + 3) over K part p
+// of P; its 8 waves take that part's K steps in turn.  Per K step a wave loads its activation
+// rows straight in the MFMA operand layout and quantizes them there: lane (r, g) holds row r's
+// K bytes [16 g, 16 g + 16) and [64 + 16 g, ...), i.e. halves of MX blocks g / 2 and 2 + g / 2,
+// whose maxima are completed with the lane 16 apart; the block scale the MFMA reads from lane
+// r + 16 b is then fetched from the lane that computed it.  The codes and scales are those of
+// k_quantize_act, bit for bit.  Each workgroup reads only its K part of x, and no second
+// launch quantizes x first.
+// Reduction: the 8 wave partials in wave order (LDS), then, with P > 1, the P workgroup
+// partials of a column group in part order by the last of them to arrive (a counter per
+// column group in the workspace, left at zero by that workgroup; no workgroup ever waits).
+
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t v) {
+  // ds_swizzle, bit-mask mode: lane i of each 32-lane half reads lane i ^ 16
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+}
+
+constexpr int kSkMaxParts = 8;
+
+template <int WFMT, int MT>
+__global__ __launch_bounds__(512) void k_linear_decode_sk(const uint16_t* __restrict__ x, int M,
+                                                          int K, const uint8_t* __restrict__ packed,
+                                                          int N, const uint16_t* __restrict__ bias,
+                                                          uint16_t* __restrict__ y, int P,
+                                                          uint32_t* __restrict__ cnt,
+                                                          v4f* __restrict__ part) {
+  constexpr int FB = frag_bytes(WFMT);
+  constexpr int CT = 4 * MT;                    // (fragment, activation tile) pairs
+  __shared__ v4f red[kWaves][CT][64];
+  __shared__ int last;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int NG = N >> 4, KT = K >> 7;
+  const int bx = blockIdx.x, p = blockIdx.y, NG4 = gridDim.x;
+  const int ng0 = 4 * bx;
+  const int kt_lo = (int)((int64_t)p * KT / P), kt_hi = (int)((int64_t)(p + 1) * KT / P);
+  const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * FB) + (int64_t)ng0 * 64 + lane;
+
+  // activation rows of this lane; rows past M repeat row M - 1 (their outputs are not stored)
+  int mrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) mrow[t] = min(16 * t + r, M - 1);
+  v4f acc[4][MT];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[c][t] = (v4f){0.f, 0.f, 0.f, 0.f};
+
+  for (int kt = kt_lo + wave; kt < kt_hi; kt += kWaves) {
+    // activations first (L2-resident after the first workgroups), then the weight (HBM, read
+    // once: non-temporal)
+    v4i xv[MT][4];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      const uint16_t* xr = x + (int64_t)mrow[t] * K + 128 * kt + 16 * g;
+      xv[t][0] = *(const v4i*)xr;
+      xv[t][1] = *(const v4i*)(xr + 8);
+      xv[t][2] = *(const v4i*)(xr + 64);
+      xv[t][3] = *(const v4i*)(xr + 72);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t sw[4];
+    v8i a[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sw[c] = wsc[(int64_t)(kt >> 2) * NG * 64 + c * 64];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const uint8_t* f = packed + ((int64_t)kt * NG + ng0 + c) * FB;
+      const v4i lo = __builtin_nontemporal_load((const v4i*)(f + lane * 16));
+      if (WFMT == 0) {
+        const v4i hi = __builtin_nontemporal_load((const v4i*)(f + 1024 + lane * 16));
+        a[c] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const v2i hi = __builtin_nontemporal_load((const v2i*)(f + 1024 + lane * 8));
+        a[c] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // quantize in the operand layout
+    v8i b[MT];
+    uint32_t sb[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      uint32_t m0 = amax8_bf16(xv[t][0]), m1 = amax8_bf16(xv[t][2]);
+      const uint32_t m0b = amax8_bf16(xv[t][1]), m1b = amax8_bf16(xv[t][3]);
+      m0 = m0 > m0b ? m0 : m0b;
+      m1 = m1 > m1b ? m1 : m1b;
+      const uint32_t o0 = lane_xor16(m0), o1 = lane_xor16(m1);
+      m0 = m0 > o0 ? m0 : o0;    // block g / 2
+      m1 = m1 > o1 ? m1 : o1;    // block 2 + g / 2
+      const uint32_t e0 = scale_byte_from_amax<0>(m0), e1 = scale_byte_from_amax<0>(m1);
+      uint32_t q[8];
+      if (e0 == 0xFFu) {
+        q[0] = q[1] = q[2] = q[3] = 0x7F7F7F7Fu;   // block holds Inf/NaN: NaN codes
+      } else {
+        const float sc = e8m0_to_float(e0);
+        q[0] = cvt4_e4m3((uint32_t)xv[t][0][0], (uint32_t)xv[t][0][1], sc);
+        q[1] = cvt4_e4m3((uint32_t)xv[t][0][2], (uint32_t)xv[t][0][3], sc);
+        q[2] = cvt4_e4m3((uint32_t)xv[t][1][0], (uint32_t)xv[t][1][1], sc);
+        q[3] = cvt4_e4m3((uint32_t)xv[t][1][2], (uint32_t)xv[t][1][3], sc);
+      }
+      if (e1 == 0xFFu) {
+        q[4] = q[5] = q[6] = q[7] = 0x7F7F7F7Fu;
+      } else {
+        const float sc = e8m0_to_float(e1);
+        q[4] = cvt4_e4m3((uint32_t)xv[t][2][0], (uint32_t)xv[t][2][1], sc);
+        q[5] = cvt4_e4m3((uint32_t)xv[t][2][2], (uint32_t)xv[t][2][3], sc);
+        q[6] = cvt4_e4m3((uint32_t)xv[t][3][0], (uint32_t)xv[t][3][1], sc);
+        q[7] = cvt4_e4m3((uint32_t)xv[t][3][2], (uint32_t)xv[t][3][3], sc);
+      }
+      b[t] = (v8i){(int)q[0], (int)q[1], (int)q[2], (int)q[3], (int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+      // the MFMA takes block g's scale from this lane: g = 0 and 3 computed it (e0 of block 0,
+      // e1 of block 3); block 1 sits in e0 of g = 2 and block 2 in e1 of g = 1 (lane ^ 48)
+      const uint32_t give = g == 1 ? e1 : e0;
+      const uint32_t got = (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 48) << 2, (int)give);
+      sb[t] = g == 0 ? e0 : (g == 3 ? e1 : got);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+        acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            a[c], b[t], acc[c][t], WFMT, 0, 0, (int)(sw[c] >> (8 * (kt & 3))), 0, (int)sb[t]);
+  }
+
+  // wave partials, summed in wave order: wave w < CT finishes pair w = (c, t)
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[wave][c * MT + t][lane] = acc[c][t];
+  __syncthreads();
+  v4f s = {0.f, 0.f, 0.f, 0.f};
+  if (wave < CT) {
+    s = red[0][wave][lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) s += red[w][wave][lane];
+  }
+  if (P > 1) {
+    // The partials go through device-coherent accesses (agent-scope atomic stores and loads,
+    // which bypass the non-coherent caches), so the exchange needs no cache write-back or
+    // invalidation: a workgroup's stores have completed (vmcnt 0) before its thread 0 counts it
+    // in, and the last one reads the others' partials after its count.
+    if (wave < CT) {
+      uint64_t* dst = (uint64_t*)(part + ((int64_t)(p * NG4 + bx) * CT + wave) * 64 + lane);
+      uint64_t v[2];
+      __builtin_memcpy(v, &s, 16);
+      __hip_atomic_store(dst, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 1, v[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): the stores are done
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(&cnt[bx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(P - 1);
+    __syncthreads();
+    if (!last) return;
+    if (wave < CT) {
+      // all parts' loads in flight together, then the sum in part order, whichever workgroup
+      // finished last
+      uint64_t v[kSkMaxParts][2];
+#pragma unroll
+      for (int q = 0; q < kSkMaxParts; ++q) {
+        if (q < P) {
+          const uint64_t* src = (const uint64_t*)(part + ((int64_t)(q * NG4 + bx) * CT + wave) * 64 + lane);
+          v[q][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          v[q][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kSkMaxParts; ++q) {
+        if (q < P) {
+          v4f t;
+          __builtin_memcpy(&t, v[q], 16);
+          s = q == 0 ? t : s + t;
+        }
+      }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&cnt[bx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (wave < CT) {
+    const int c = wave / MT, t = wave % MT;
+    const int m = 16 * t + r, n = 16 * (ng0 + c) + 4 * g;
+    if (m < M) {
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bv[i] = bf16_to_float(bias[n + i]);
+      }
+      const v2i o = {(int)pack_bf16x2(s[0] + bv[0], s[1] + bv[1]),
+                     (int)pack_bf16x2(s[2] + bv[2], s[3] + bv[3])};
+      *(v2i*)(y + (int64_t)m * N + n) = o;
+    }
+  }
+}
+
+// K parts: about 256 workgroups, at least 8 K steps (one per wave) in each part, at most 8
+int decode_sk_parts(int64_t N, int64_t K) {
+  const int64_t ng4 = N / 64, kt = K / 128;
+  int64_t p = (256 + ng4 - 1) / ng4;
+  int64_t pmax = kt / 8 > 1 ? kt / 8 : 1;
+  if (pmax > kSkMaxParts) pmax = kSkMaxParts;
+  if (p > pmax) p = pmax;
+  return (int)(p < 1 ? 1 : p);
+}
+
+bool decode_sk_ok(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && M <= 32 && K % 128 == 0 && N % 64 == 0 && N / 64 * 4 <= kWorkspacePrefix;
+}
+
+int64_t decode_sk_workspace(int64_t M, int64_t N, int64_t K) {
+  const int64_t mt = M <= 16 ? 1 : 2;
+  return decode_sk_parts(N, K) * (N / 64) * 4 * mt * 64 * 16;
+}
+
+hipError_t launch_linear_decode_sk(const uint16_t* x, int64_t M, int64_t K, const uint8_t* packed,
+                                   int64_t N, int fmt, const uint16_t* bias, uint16_t* y,
+                                   void* workspace, hipStream_t s) {
+  if (!decode_sk_ok(M, N, K)) return hipErrorInvalidValue;
+  const int P = decode_sk_parts(N, K);
+  uint32_t* cnt = (uint32_t*)workspace;
+  v4f* part = (v4f*)((uint8_t*)workspace + kWorkspacePrefix);
+  const dim3 grid((unsigned)(N / 64), (unsigned)P), block(512);
+  const int m = (int)M, k = (int)K, n = (int)N;
+#define MX_SK(W)                                                                                      \
+  do {                                                                                                \
+    if (M <= 16)                                                                                      \
+      hipLaunchKernelGGL((k_linear_decode_sk<W, 1>), grid, block, 0, s, x, m, k, packed, n, bias, y, P, cnt, part); \
+    else                                                                                              \
+      hipLaunchKernelGGL((k_linear_decode_sk<W, 2>), grid, block, 0, s, x, m, k, packed, n, bias, y, P, cnt, part); \
+  } while (0)
+  switch (fmt) {
+    case 0: MX_SK(0); break;
+    case 2: MX_SK(2); break;
+    case 3: MX_SK(3); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MX_SK
+  return hipGetLastError();
+}
+
 bool small_m_fused(int64_t M, int64_t K) { return M >= 1 && M <= 16 && K % 128 == 0; }
 bool small_m_quantized(int64_t M, int64_t K) { return M >= 1 && M <= 32 && K % 128 == 0; }
 

@@ -234,7 +234,7 @@ def _workspace(device, stream, nbytes):
     key = (device, stream)
     t = _ws_cache.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+        t = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)   # counter prefix zero
         _ws_cache[key] = t
     return t
 

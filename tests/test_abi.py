@@ -62,7 +62,13 @@ def test_quantize_act_validation(L):
 
 def test_linear_validation(L):
     ws = L.mxfp8_workspace_bytes(64, 256, 512, 0)
-    assert ws >= 64 * 512 + 64 * 16
+    assert ws == 65536 + 64 * 512 + 64 * 16     # counter prefix, xq, xs
+    # decode shapes with K split across workgroups (16 <= M <= 32, N % 64 == 0): the prefix,
+    # then the partial sums (4 K parts x N/64 column groups x (fragment, tile) pairs x 1 KiB)
+    assert L.mxfp8_workspace_bytes(32, 4096, 4096, 0) == 65536 + 4 * 64 * 8 * 1024
+    assert L.mxfp8_workspace_bytes(16, 4096, 4096, 0) == 65536 + 4 * 64 * 4 * 1024
+    assert L.mxfp8_workspace_bytes(8, 4096, 4096, 0) == 65536 + 8 * 4096 + 8 * 128
+    assert L.mxfp8_workspace_bytes(1, 4096, 4096, 0) == 65536 + 4096 + 128
     assert L.mxfp8_linear(A, 64, 512, B, 256, 0, None, B, B, ws - 1, None) == MX_EWORKSPACE
     assert L.mxfp8_linear(A, 64, 512, B, 256, 0, None, B, None, ws, None) == MX_EWORKSPACE
     assert L.mxfp8_linear(A, 64, 512, B, 250, 0, None, B, B, ws, None) == MX_ESHAPE   # N % 16
@@ -149,9 +155,10 @@ def test_fp6_activation_validation(L):
     assert q(A + 2, 4, 64, 64, 3, B, B, None) == MX_EALIGN
     assert q(None, 4, 64, 64, 2, B, B, None) == MX_EINVAL
     assert q(None, 0, 64, 64, 2, None, None, None) == MX_OK      # M == 0: no-op
-    # workspace: packed FP6 codes [M, 3K/4], then the scales at a 256-byte boundary
-    assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 2, 2) == 64 * 384 + 64 * 16
-    assert L.mxfp8_workspace_bytes_fmt(3, 256, 160, 3, 2) == 512 + 3 * 5
+    # workspace: the 64 KiB counter prefix, packed FP6 codes [M, 3K/4], then the scales at a
+    # 256-byte boundary
+    assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 2, 2) == 65536 + 64 * 384 + 64 * 16
+    assert L.mxfp8_workspace_bytes_fmt(3, 256, 160, 3, 2) == 65536 + 512 + 3 * 5
     assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 0, 2) == 0   # FP6 activations: FP6 weights
     assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 2, 0) == L.mxfp8_workspace_bytes(64, 256, 512, 2)
     ws = L.mxfp8_workspace_bytes_fmt(64, 256, 512, 2, 3)

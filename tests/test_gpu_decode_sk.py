@@ -1,0 +1,149 @@
+"""GPU parity of the decode path that splits K across workgroups (mxfp8_linear with bf16
+activations, 16 <= M <= 32, N % 64 == 0, K % 128 == 0).
+
+That kernel quantizes the activations itself, in the MFMA operand layout, and adds the K parts
+of a column group in a fixed order chosen by the last workgroup to finish (a counter in the
+workspace, which every call leaves at zero).  Checked here:
+- the layer against the fp64 oracle to the usual bar, for one to eight K parts, ragged parts,
+  every weight format, with and without bias, outlier channels and all-zero blocks;
+- a block holding Inf: its rows are NaN, as in the oracle, and the other rows are unaffected;
+- repeated calls and calls of other shapes and entry points sharing one workspace: results
+  repeat bit for bit (the counters come back to zero);
+- the calls replayed from a HIP graph, each replay against the eager results.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from mx_block_scaled_amd import mxfp8, synth
+from tests import tolerance
+from tests.gpu_helpers import DEV, banner, bf16_dev, host_bf16_bits, u8_dev
+
+pytestmark = pytest.mark.gpu
+
+FMTS = {0: "e4m3", 2: "e2m3", 3: "e3m2"}
+
+# (M, N, K): K parts = min(ceil(256 / (N / 64)), max(1, K / 1024), 8)
+SHAPES = [
+    (16, 64, 128),      # one part, one K step: seven idle waves; one activation tile
+    (16, 4096, 4096),   # four parts of 8 K steps
+    (32, 4096, 4096),   # the decode workload's shape, two activation tiles
+    (17, 4096, 4480),   # 35 K steps in four parts of 8 or 9
+    (20, 1024, 8192),   # eight parts
+    (32, 16384, 1024),  # 256 column groups: one part, no cross-workgroup sum
+    (24, 640, 2560),    # ten column groups, two parts of 10 K steps
+]
+
+
+def _inputs(M, N, K, seed):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((M, K)).astype(np.float32)
+    x[:, g.choice(K, max(1, K // 100), replace=False)] *= 60.0       # outlier channels
+    xb = x.reshape(M, K // 32, 32)
+    xb[g.integers(0, M, 2), g.integers(0, K // 32, 2)] = 0.0          # all-zero blocks
+    w = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    b = synth.bf16_bits((g.standard_normal(N) * 0.05).astype(np.float32))
+    return synth.bf16_bits(x), w, b
+
+
+def _layer(w_bits, fmt, b_bits):
+    wq, ws = orc.quantize(w_bits, fmt)
+    wstore = wq if fmt == 0 else orc.fp6_pack(wq)
+    return mxfp8.MxLinear(u8_dev(wstore), u8_dev(ws), fmt,
+                          bias=None if b_bits is None else bf16_dev(b_bits)), wq, ws
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("fmt", [0, 2, 3])
+def test_decode_split_k_matches_oracle(M, N, K, fmt):
+    if fmt != 0 and (M, N, K) in [(32, 16384, 1024), (20, 1024, 8192)]:
+        pytest.skip("the FP6 formats are covered on the other shapes")
+    x, w, b = _inputs(M, N, K, M * 7 + N + K + fmt)
+    use_bias = (M + fmt) % 2 == 0
+    layer, wq, ws = _layer(w, fmt, b if use_bias else None)
+    banner("decode split-K", M, N, K, FMTS[fmt], "bias" if use_bias else "no bias")
+    y = layer(bf16_dev(x))
+    ref, _, _ = orc.linear_ref(x, wq, ws, fmt, b if use_bias else None)
+    ok, rep = tolerance.check(host_bf16_bits(y), ref, name="sk-%d-%d-%d-%d" % (M, N, K, fmt))
+    assert ok, rep
+
+
+def test_decode_split_k_inf_block():
+    M, N, K = 19, 2048, 4096
+    x, w, b = _inputs(M, N, K, 5)
+    x[3, 1000] = 0x7F80                     # +Inf in row 3
+    layer, wq, ws = _layer(w, 0, b)
+    banner("decode split-K, Inf block", M, N, K)
+    y = host_bf16_bits(layer(bf16_dev(x)))
+    ref, _, _ = orc.linear_ref(x, wq, ws, 0, b)
+    yf = tolerance.bf16_to_f64(y)
+    assert np.isnan(yf[3]).all() and np.isnan(ref[3]).all()
+    keep = np.arange(M) != 3
+    ok, rep = tolerance.check(y[keep], ref[keep], name="sk-inf")
+    assert ok, rep
+
+
+def test_decode_split_k_workspace_reuse():
+    """One workspace for a sequence of calls of several shapes and entry points: every call
+    repeats its first result bit for bit, so the counters are back at zero after each call."""
+    K = 4096
+    g = np.random.default_rng(11)
+    shapes = [(32, 4096), (16, 1024), (3, 4096), (300, 256), (1, 4096), (20, 640)]
+    ws_bytes = max(mxfp8.workspace_bytes(M, N, K) for M, N in shapes)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=DEV)
+    calls = []
+    for M, N in shapes:
+        x = bf16_dev(synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32)))
+        wb = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+        wq, wsc = orc.quantize(wb, 0)
+        pk = mxfp8.prepack_weight(u8_dev(wq), u8_dev(wsc), 0)
+        calls.append((x, pk, N))
+    banner("decode split-K workspace reuse", shapes)
+    first = [mxfp8.linear(x, pk, N, 0, workspace=ws).clone() for x, pk, N in calls]
+    assert int(ws[:65536].count_nonzero()) == 0
+    for rnd in range(3):
+        for i in ([0, 1, 2, 3, 4, 5] if rnd != 1 else [5, 3, 0, 0, 2, 1, 4]):
+            x, pk, N = calls[i]
+            y = mxfp8.linear(x, pk, N, 0, workspace=ws)
+            assert torch.equal(y.view(torch.int16), first[i].view(torch.int16)), (rnd, i)
+    torch.cuda.synchronize()
+    assert int(ws[:65536].count_nonzero()) == 0
+
+
+def test_decode_split_k_graph_replay():
+    """The calls captured in a HIP graph: no memset nodes; every replay, with eager work and
+    synchronizations in between, equals the eager results."""
+    g = np.random.default_rng(12)
+    N = K = 4096
+    wb = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    wq, wsc = orc.quantize(wb, 0)
+    pk = mxfp8.prepack_weight(u8_dev(wq), u8_dev(wsc), 0)
+    xs = [bf16_dev(synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32))) for M in (32, 16, 2)]
+    ws = torch.zeros(max(mxfp8.workspace_bytes(x.shape[0], N, K) for x in xs),
+                     dtype=torch.uint8, device=DEV)
+    ys = [torch.empty((x.shape[0], N), dtype=torch.bfloat16, device=DEV) for x in xs]
+    banner("decode split-K graph replay")
+    eager = [mxfp8.linear(x, pk, N, 0, out=torch.empty_like(y), workspace=ws).clone()
+             for x, y in zip(xs, ys)]
+    s = torch.cuda.Stream(DEV)
+    s.wait_stream(torch.cuda.current_stream(DEV))
+    with torch.cuda.stream(s):
+        for x, y in zip(xs, ys):
+            mxfp8.linear(x, pk, N, 0, out=y, workspace=ws)
+    torch.cuda.current_stream(DEV).wait_stream(s)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        for x, y in zip(xs, ys):
+            mxfp8.linear(x, pk, N, 0, out=y, workspace=ws)
+    for rep in range(4):
+        for y in ys:
+            y.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y.view(torch.int16), e.view(torch.int16)), rep
+        # eager work between replays, on the same workspace
+        mxfp8.linear(xs[1], pk, N, 0, workspace=ws)
+        torch.cuda.synchronize()

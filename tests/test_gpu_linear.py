@@ -225,11 +225,24 @@ def test_small_m_fused(M, N, K, fmt):
     x, w, b = _small_inputs(M, N, K, M * 131 + N + K + fmt)
     banner("linear small-M", M, N, K, FMTS[fmt])
     y, layer = _full_check(x, w, fmt, b, name="small-%d-%d-%d-%d" % (M, N, K, fmt))
-    # the pre-quantized entry runs the same kernel with the same summation order, so feeding
-    # it the oracle's quantization of x must reproduce the bf16 entry's result bit for bit
     xq, xs = orc.quantize(x, orc.E4M3)
     y2 = layer.apply_quantized(u8_dev(xq), u8_dev(xs))
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    if _splits_k(M, N, K):
+        # the bf16 entry splits K across workgroups here and adds in another order: both
+        # entries against the oracle
+        ref, _, _ = orc.linear_ref(x, *orc.quantize(w, fmt), fmt, b)
+        ok, rep = tolerance.check(host_bf16_bits(y2), ref, name="small-prequant")
+        assert ok, rep
+    else:
+        # the pre-quantized entry runs the same kernel with the same summation order, so
+        # feeding it the oracle's quantization of x must reproduce the bf16 entry's result bit
+        # for bit
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def _splits_k(M, N, K):
+    """shapes on which mxfp8_linear runs the decode kernel that splits K across workgroups"""
+    return 16 <= M <= 32 and N % 64 == 0 and K % 128 == 0
 
 
 @pytest.mark.parametrize("M", [1, 8, 32])
@@ -239,7 +252,13 @@ def test_decode_prequant_matches_fused(M):
     y = layer(bf16_dev(d["x"]))
     xq, xs = orc.quantize(d["x"], orc.E4M3)
     y2 = layer.apply_quantized(u8_dev(xq), u8_dev(xs))
-    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    if _splits_k(M, 4096, 4096):   # different kernels: each against the oracle
+        ref, _, _ = orc.linear_ref(d["x"], wq, ws, 0, d["bias"])
+        for yy, nm in ((y, "bf16 entry"), (y2, "pre-quantized entry")):
+            ok, rep = tolerance.check(host_bf16_bits(yy), ref, name=nm)
+            assert ok, rep
+    else:
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
 @pytest.mark.parametrize("fmt", [0, 2])

@@ -21,7 +21,7 @@ __all__ = [
     "linear", "linear_prequant", "MxLinear", "set_tile_config", "set_batch_invariant",
     "prepack_weight_shuffled16", "unpack_weight_shuffled16", "linear_batched",
     "linear_prequant_batched", "quantize_act_fmt", "workspace_bytes_fmt", "linear_fmt",
-    "linear_prequant_fmt", "rmsnorm_quantize_act",
+    "linear_prequant_fmt", "rmsnorm_quantize_act", "new_workspace",
 ]
 
 FMT = {"e4m3": 0, "e2m3": 2, "e3m2": 3}
@@ -126,6 +126,13 @@ def prepacked_bytes(N, K, fmt="e4m3"):
 
 def workspace_bytes(M, N, K, fmt="e4m3"):
     return int(lib().mxfp8_workspace_bytes(M, N, K, _fmt(fmt)))
+
+
+def new_workspace(nbytes, device="cuda"):
+    """A workspace for the ``workspace=`` arguments: ``nbytes`` (from workspace_bytes) of device
+    memory, zero-filled.  Its first 64 KiB are counters that must be zero before the first call
+    and that every call leaves zero; a workspace allocated otherwise must be zeroed once."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 def quantize_act(x):
@@ -234,13 +241,16 @@ def _workspace(device, stream, nbytes):
     key = (device, stream)
     t = _ws_cache.get(key)
     if t is None or t.numel() < nbytes:
-        t = torch.zeros(max(nbytes, 1), dtype=torch.uint8, device=device)   # counter prefix zero
+        t = new_workspace(nbytes, device)
         _ws_cache[key] = t
     return t
 
 
 def linear(x, packed, N, fmt="e4m3", bias=None, out=None, workspace=None):
-    """y = MX-quantized x [..., K] times the prepacked weight, (+ bias), bf16 [..., N]."""
+    """y = MX-quantized x [..., K] times the prepacked weight, (+ bias), bf16 [..., N].
+
+    ``workspace``: a uint8 device tensor of at least workspace_bytes(M, N, K, fmt) bytes from
+    new_workspace (zero-filled); by default one is kept per device and stream."""
     x = _bf16(x, "x")
     f = _fmt(fmt)
     lead, K = x.shape[:-1], x.shape[-1]

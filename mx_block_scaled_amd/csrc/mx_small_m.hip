@@ -20,6 +20,10 @@
 // block, reduced with DPP), writes the codes to a wave-private LDS image, and the MFMA operands
 // are then read back from LDS in the operand layout.  Working directly in the operand layout
 // would quantize 16 rows per wave whatever M is.
+//
+// From 16 rows on (bf16 entry), k_linear_decode_sk below also splits K across workgroups, so
+// that each workgroup reads only a part of the activations; there the operand layout is the
+// cheaper place to quantize.
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -239,7 +243,8 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode with the K dimension also split across workgroups (M <= 32, bf16 activations).
+// Decode with the K dimension also split across workgroups (M <= 32, bf16 activations; used
+// from M = 16 on).
 // Workgroup (b, p) computes 64 output columns (weight fragments 4 b .. 4 b + 3) over K part p
 // of P; its 8 waves take that part's K steps in turn.  Per K step a wave loads its activation
 // rows straight in the MFMA operand layout and quantizes them there: lane (r, g) holds row r's

@@ -599,7 +599,8 @@ static void launch_tile(const uint8_t* xq, const uint8_t* xs, int M, int K, cons
 }
 
 // Tile choice: the configurations below are compiled; pick the one whose tile count fills the
-// 256 CUs in the fewest (and fullest) waves, preferring larger tiles on ties.
+// 256 CUs in the fewest (and fullest) waves, preferring larger tiles on ties; a batched launch
+// counts the tiles of all its layers.
 struct TileChoice { int fn, fm; };
 // compiled tiles (fn, fm) -> workgroup tile 32 fn x 64 fm, two LDS stages
 static std::atomic<int> g_force_tile{0};   // fn * 16 + fm, 0 = automatic
@@ -607,7 +608,7 @@ void force_tile(int fn, int fm) { g_force_tile.store(fn * 16 + fm); }
 static std::atomic<bool> g_batch_invariant{false};
 void set_batch_invariant(bool on) { g_batch_invariant.store(on); }
 bool batch_invariant() { return g_batch_invariant.load(std::memory_order_relaxed); }
-static TileChoice choose_tile(int M, int N) {
+static TileChoice choose_tile(int M, int N, int batch) {
   const int f = g_force_tile.load(std::memory_order_relaxed);
   if (f) return TileChoice{f / 16, f % 16};
   static const TileChoice opts[] = {{8, 4}, {7, 4}, {6, 4}, {4, 4}, {4, 2}};
@@ -615,7 +616,7 @@ static TileChoice choose_tile(int M, int N) {
   TileChoice pick = opts[0];
   for (const TileChoice& o : opts) {
     const int bn = 32 * o.fn, bm = 64 * o.fm;
-    const long tiles = (long)((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+    const long tiles = (long)((N + bn - 1) / bn) * ((M + bm - 1) / bm) * batch;
     const long waves = (tiles + 255) / 256;
     // time ~ waves x per-tile work, per-tile work ~ bn * bm (+ a fixed operand-load cost)
     const double cost = (double)waves * ((double)bn * bm + 64.0 * (bn + bm));
@@ -628,13 +629,13 @@ template <int WFMT, int XFMT>
 static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int K,
                                const uint8_t* packed, int N, const uint16_t* bias, uint16_t* y,
                                hipStream_t s, int batch, const BatchStrides& bs) {
-  const TileChoice c = choose_tile(M, N);
+  const TileChoice c = choose_tile(M, N, batch);
   const int group_m = 4;
   if (c.fn == 8 && c.fm == 4) launch_tile<WFMT, XFMT, 8, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else if (c.fn == 7 && c.fm == 4) launch_tile<WFMT, XFMT, 7, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else if (c.fn == 6 && c.fm == 4) launch_tile<WFMT, XFMT, 6, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else if (c.fn == 4 && c.fm == 4) launch_tile<WFMT, XFMT, 4, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
-  else if ((long)((N + 127) / 128) * ((M + 127) / 128) <= 256)
+  else if ((long)((N + 127) / 128) * ((M + 127) / 128) * batch <= 256)
     // one tile per CU at most: each workgroup runs the whole K of its tile, where a third LDS
     // stage (deeper prefetch) pays off
     launch_tile<WFMT, XFMT, 4, 2, 3>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);

@@ -176,3 +176,27 @@ def test_fused_quantizers_bit_exact_through_identity_weight(M):
     # the layer's output is a sum started at +0, so a code of -0 comes out as +0
     expect[expect == 0x8000] = 0
     assert np.array_equal(y, expect), np.argwhere(y != expect)[:8]
+
+
+@pytest.mark.parametrize("M", [8, 100])
+@pytest.mark.parametrize("fmt", [2, 3])
+def test_fp6_activations_bit_exact_through_identity_weight(M, fmt):
+    """W6A6 through the identity weight (the format's 1.0 on the diagonal): every output is one
+    dequantized FP6 activation, so the layer equals the oracle's dequantize(quantize(x, fmt)) bit
+    for bit, which pins the FP6 operand reads of the generic (M = 8) and tiled (M = 100)
+    kernels as well as the FP6 quantizer."""
+    K = N = 1024
+    g = np.random.default_rng(M + fmt)
+    x = g.standard_normal((M, K)).astype(np.float32)
+    x[:, g.choice(K, 10, replace=False)] *= 50.0
+    x.reshape(M, K // 32, 32)[g.integers(0, M, 2), g.integers(0, K // 32, 2)] = 0.0
+    x_bits = synth.bf16_bits(x)
+    layer, wq, ws = _layer(synth.bf16_bits(np.eye(N, K, dtype=np.float32)), fmt, None)
+    banner("identity weight, W6A6", M, N, K, FMTS[fmt])
+    ws_t = mxfp8.new_workspace(mxfp8.workspace_bytes_fmt(M, N, K, fmt, fmt), DEV)
+    y = host_bf16_bits(mxfp8.linear_fmt(bf16_dev(x_bits), layer.packed, N, fmt, fmt,
+                                        workspace=ws_t))
+    xq, xs = orc.quantize(x_bits, fmt)
+    expect = orc.f64_to_bf16(orc.dequantize(xq, xs, fmt))
+    expect[expect == 0x8000] = 0
+    assert np.array_equal(y, expect), np.argwhere(y != expect)[:8]

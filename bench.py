@@ -78,10 +78,12 @@ def main():
     ap.add_argument("--no-others", action="store_true",
                     help="skip the outlier, MXFP6 and tiny workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["all", "gemm", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "gemm", "copy", "decode"], default="all",
                     help="counter runs: 'gemm' launches only the prefill GEMM (pre-quantized "
-                         "entry) --steps times; 'copy' copies a 1 GiB device buffer 3 times, the "
-                         "calibration of the HBM byte counters")
+                         "entry) --steps times; 'decode' runs the decode calls (M = 1, 8, 32) "
+                         "--steps times each over the rotated weights, without a graph; 'copy' "
+                         "copies a 1 GiB device buffer 3 times, the calibration of the HBM byte "
+                         "counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -102,6 +104,24 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copied_bytes_per_launch": 1 << 30, "launches": 3}))
+        return
+
+    if args.only == "decode":
+        dd = synth.make("decode32")
+        Nd = Kd = 4096
+        w0 = torch.from_numpy(dd["w"].view(np.int16)).view(torch.bfloat16).to(dev)
+        wq, ws = mxfp8.quantize_weight(w0, "e4m3")
+        pk = mxfp8.prepack_weight(wq, ws, "e4m3")
+        bias = torch.from_numpy(dd["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
+        pks = [pk] + [pk.clone() for _ in range(31)]
+        for Md in (1, 8, 32):
+            xd = torch.from_numpy(dd["x"][:Md].view(np.int16)).view(torch.bfloat16).to(dev)
+            yd = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
+            wsd = mxfp8.new_workspace(mxfp8.workspace_bytes(Md, Nd, Kd), dev)
+            for i in range(args.steps):
+                mxfp8.linear(xd, pks[i % 32], Nd, "e4m3", bias, out=yd, workspace=wsd)
+            torch.cuda.synchronize()
+        print(json.dumps({"decode_calls_per_M": args.steps, "M": [1, 8, 32], "N": Nd, "K": Kd}))
         return
 
     # ------------------------------------------------------------ prefill workload

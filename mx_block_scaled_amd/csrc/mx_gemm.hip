@@ -465,7 +465,24 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   const uint32_t by_off = (uint32_t)((wm * 16 * FM + r) * 128 + ((c_half ^ swz(r)) << 4) + (godd ? 8 : 0));
   // `mid` runs once the first operand reads are issued and before the first MFMA: the step's
   // DMAs go out there, so their issue overlaps the LDS read latency instead of delaying it.
-  auto compute = [&](int stage, auto qc, const uint32_t* sa_in, const uint32_t* sb_in, int sh, auto&& mid) __attribute__((always_inline)) {
+  // operands of the previous step's last weight fragment: its MFMAs run after the next
+  // barrier, covering the latency of that step's first LDS reads (same order per accumulator)
+  // The last TN MFMAs of a step (last weight fragment x last TN activation tiles) run at the
+  // top of the next step, after its barrier and first LDS reads, so that the two waves of a SIMD
+  // do not both stall on those reads with an empty matrix pipe; each accumulator still sees
+  // the K steps in order, so results do not change.  The 8 x 4 tile has no registers to spare.
+  constexpr int TN = FN >= 8 ? 0 : (FM < 2 ? FM : 2);
+  AR a_tail;
+  BR b_tail[TN > 0 ? TN : 1];
+  uint32_t sa_tail = 0, sb_tail[TN > 0 ? TN : 1];
+  auto run_tail = [&](bool have) __attribute__((always_inline)) {
+    if (TN > 0 && have) {
+      asm volatile("s_nop 2" ::: "memory");   // the tail scale words are VALU-written
+#pragma unroll
+      for (int j = 0; j < TN; ++j) mfma_inplace<WFMT, XFMT, 0>(acc[FN - 1][FM - TN + j], a_tail, b_tail[j], sa_tail, sb_tail[j]);
+    }
+  };
+  auto compute = [&](int stage, auto qc, const uint32_t* sa_in, const uint32_t* sb_in, int sh, bool have_tail, auto&& mid) __attribute__((always_inline)) {
     constexpr int Q = decltype(qc)::value;
     // remainder steps: the step's scale byte shifted into byte 0 (op-select 0); the nops keep
     // two wait states between these VALU writes and the MFMAs that read them
@@ -488,6 +505,8 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
                                  bl + (XFMT == 0 ? b_hi : by_off) + j * 2048, godd);
     AR an = FN > 1 ? load_a(base, 1) : a;
     __builtin_amdgcn_sched_barrier(0);
+    run_tail(have_tail);
+    __builtin_amdgcn_sched_barrier(0);
     mid();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -497,13 +516,25 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
         an2 = load_a(base, i + 2);
       }
 #pragma unroll
-      for (int j = 0; j < FM; ++j) {
+      for (int j = 0; j < (i == FN - 1 ? FM - TN : FM); ++j) {
         mfma_inplace<WFMT, XFMT, (Q >= 0 ? Q : 0)>(acc[i][j], a, b[j], sa[i], sb[j]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      a = an;
-      an = an2;
+      if (i < FN - 1) {
+        a = an;
+        an = an2;
+      }
     }
+    // the last TN MFMAs wait for the next step (their scale words shifted to byte 0)
+    constexpr int QS = Q >= 0 ? 8 * Q : 0;
+    a_tail = a;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      b_tail[j] = b[FM - TN + j];
+      sb_tail[j] = sb[FM - TN + j] >> QS;
+    }
+    sa_tail = sa[FN - 1] >> QS;
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   uint32_t sa[FN], sb[FM];
@@ -528,7 +559,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     wait_vm_barrier<C::vm_after(Q)>();
     if (Q == 0 && kt > 0) read_scales(kt >> 2, (kt >> 2) & 1, sa, sb);
     // this step's DMAs: tile DMAs first, then (first step of a group) the scale DMAs
-    compute(kt % S, qc, sa, sb, 0, [&]() __attribute__((always_inline)) {
+    compute(kt % S, qc, sa, sb, 0, kt > 0, [&]() __attribute__((always_inline)) {
       issue(min(kt + S - 1, KT - 1), (kt + S - 1) % S);
       if (Q == 0) issue_scales(min((kt >> 2) + 1, KT4 - 1), ((kt >> 2) + 1) & 1);
     });
@@ -543,10 +574,11 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   for (int kt = 4 * KT4f; kt < KT; ++kt) {
     wait_vm_barrier<0>();
     if (kt == 4 * KT4f && KT4f > 0) read_scales(KT4f, KT4f & 1, sa, sb);
-    compute(kt % S, std::integral_constant<int, -1>(), sa, sb, 8 * (kt & 3), [&]() __attribute__((always_inline)) {
+    compute(kt % S, std::integral_constant<int, -1>(), sa, sb, 8 * (kt & 3), kt > 0, [&]() __attribute__((always_inline)) {
       if (kt + S - 1 < KT) issue(kt + S - 1, (kt + S - 1) % S);
     });
   }
+  run_tail(KT > 0);
   // all DMAs landed and all waves done with the stages before LDS is reused for the output;
   // the nops give the last MFMAs (issued as assembly, so untracked by the compiler's hazard
   // checks) their result latency before VALU code reads the accumulators

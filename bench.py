@@ -290,7 +290,7 @@ def main():
             return [make_set(j) for j in range(n)]
 
         def time_calls(fn, n_sets, iters):
-            for j in range(max(2 * n_sets, 30)):   # warm: every set touched, steady clock
+            for j in range(max(2 * n_sets, 100)):   # warm: every set touched, steady clock
                 fn(j % n_sets)
             torch.cuda.synchronize()
             stream = torch.cuda.current_stream(dev)

@@ -16,7 +16,10 @@ Also measured and printed in the same JSON line:
                 still matches it, else null;
   decode        the decode workload (x [M, 4096], M in {1, 8, 32}, weight [4096, 4096], bias),
                 one fused call each, replayed from a HIP graph over 32 rotated weight copies:
-                time per call, algorithmic bytes / time against 8 TB/s;
+                time per call, algorithmic bytes / time against 8 TB/s; the same for M = 64
+                and 128 (prefill chunks too small to fill the GPU with output tiles: the
+                tiled GEMM with K split across workgroups), and every M again in
+                batch-invariant mode;
   other_workloads  outlier activations on the pre-quantized entry (2048 x 6144 x 4096, GEMM
                 only), MXFP6 weights (E2M3 and E3M2, 512 x 8192 x 8192, activation quantization
                 included) with MXFP8 activations and with MXFP6 activations of the same format
@@ -213,7 +216,7 @@ def main():
         del xs_, ps_, ys_, wsb
         torch.cuda.empty_cache()
         decode = {}
-        dd = synth.make("decode32")
+        dd = synth.make("decode32", M=128)     # rows 0..31: decode; up to 128: chunk sizes
         Nd = Kd = 4096
         w0 = torch.from_numpy(dd["w"].view(np.int16)).view(torch.bfloat16).to(dev)
         wq, ws = mxfp8.quantize_weight(w0, "e4m3")
@@ -221,7 +224,7 @@ def main():
         bias = torch.from_numpy(dd["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
         RD = 32
         pks = [pk] + [pk.clone() for _ in range(RD - 1)]
-        for Md in (1, 8, 32):
+        for Md in (1, 8, 32, 64, 128):
             xd = torch.from_numpy(dd["x"][:Md].view(np.int16)).view(torch.bfloat16).to(dev)
             yd = torch.empty((Md, Nd), dtype=torch.bfloat16, device=dev)
             wsd = torch.zeros(max(1, mxfp8.workspace_bytes(Md, Nd, Kd)), dtype=torch.uint8, device=dev)
@@ -433,7 +436,8 @@ def main():
         pkb = torch.cat(pks)
         del pks, wq, ws
         yb = torch.empty((Bb, Mb, Nb), dtype=torch.bfloat16, device=dev)
-        wsb2 = torch.zeros(mxfp8.workspace_bytes(Bb * Mb, Nb, Kb), dtype=torch.uint8, device=dev)
+        wsb2 = torch.zeros(max(mxfp8.workspace_bytes(Bb * Mb, Nb, Kb), mxfp8.workspace_bytes(Mb, Nb, Kb)),
+                           dtype=torch.uint8, device=dev)   # batched call and single calls
         P = mxfp8.prepacked_bytes(Nb, Kb)
         us_b = time_calls(lambda j: mxfp8.linear_batched(xb, pkb, Nb, "e4m3", out=yb, workspace=wsb2),
                           1, max(20, args.steps // 4))

@@ -88,8 +88,17 @@ int64_t quant_ws_bytes(int64_t M, int64_t K, int afmt = MX_FMT_E4M3) {
 constexpr int64_t kSkMinM = 16;
 bool sk_shape(int64_t M, int64_t N, int64_t K) { return M >= kSkMinM && mx::decode_sk_ok(M, N, K); }
 
+// the split-K partial sums of the tiled GEMM follow the quantized activations
+int64_t split_offset(int64_t M, int64_t K, int afmt = MX_FMT_E4M3) {
+  return (quant_ws_bytes(M, K, afmt) + 255) / 256 * 256;
+}
+int64_t quant_split_ws_bytes(int64_t M, int64_t N, int64_t K, int afmt = MX_FMT_E4M3) {
+  const int64_t sb = mx::gemm_split_bytes(M, N, K);
+  return sb ? split_offset(M, K, afmt) + sb : quant_ws_bytes(M, K, afmt);
+}
+
 int64_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  int64_t need = quant_ws_bytes(M, K);
+  int64_t need = quant_split_ws_bytes(M, N, K);
   if (sk_shape(M, N, K)) {
     const int64_t sk = mx::kWorkspacePrefix + mx::decode_sk_workspace(M, N, K);
     if (sk > need) need = sk;
@@ -263,10 +272,11 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, i
                       "linear (small M) launch");
   uint8_t* xq = (uint8_t*)workspace + mx::kWorkspacePrefix;
   uint8_t* xs = xq + ((M * K + 255) / 256) * 256;
+  float* part = mx::gemm_split_bytes(M, N, K) ? (float*)((uint8_t*)workspace + split_offset(M, K)) : nullptr;
   hipError_t e = mx::launch_quantize_act((const uint16_t*)x_bf16, M, K, K, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "quantize_act launch");
   return hip_status(mx::launch_gemm(xq, xs, M, K, (const uint8_t*)packed, N, fmt,
-                                    (const uint16_t*)bias, (uint16_t*)y, s),
+                                    (const uint16_t*)bias, (uint16_t*)y, s, 1, {}, 0, part),
                     "gemm launch");
 }
 
@@ -370,7 +380,7 @@ int64_t mxfp8_workspace_bytes_fmt(int64_t M, int64_t N, int64_t K, int fmt, int 
   if (afmt != MX_FMT_E4M3 && fmt == MX_FMT_E4M3) return 0;
   if (M == 0) return 0;
   if (afmt == MX_FMT_E4M3) return linear_ws_bytes(M, N, K);   // mxfp8_linear's
-  return quant_ws_bytes(M, K, afmt);
+  return quant_split_ws_bytes(M, N, K, afmt);
 }
 
 int mxfp8_linear_fmt(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N,
@@ -384,7 +394,7 @@ int mxfp8_linear_fmt(const void* x_bf16, int64_t M, int64_t K, const void* packe
   if (M == 0) return ok();
   if (!x_bf16) return fail(MX_EINVAL, "null pointer (x)");
   if (!aligned16(x_bf16)) return fail(MX_EALIGN, "x must be 16-byte aligned");
-  const int64_t need = quant_ws_bytes(M, K, afmt);
+  const int64_t need = quant_split_ws_bytes(M, N, K, afmt);
   if (!workspace || ws_bytes < need)
     return fail(MX_EWORKSPACE, "workspace of %lld bytes given, %lld needed", (long long)ws_bytes, (long long)need);
   if (!aligned16(workspace)) return fail(MX_EALIGN, "workspace must be 16-byte aligned");
@@ -392,10 +402,11 @@ int mxfp8_linear_fmt(const void* x_bf16, int64_t M, int64_t K, const void* packe
   hipStream_t s = (hipStream_t)stream;
   uint8_t* xq = (uint8_t*)workspace + mx::kWorkspacePrefix;
   uint8_t* xs = xq + ((M * (K / 4 * 3) + 255) / 256) * 256;
+  float* part = mx::gemm_split_bytes(M, N, K) ? (float*)((uint8_t*)workspace + split_offset(M, K, afmt)) : nullptr;
   hipError_t e = mx::launch_quantize_act_fp6((const uint16_t*)x_bf16, M, K, K, afmt, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "quantize_act (FP6) launch");
   return hip_status(mx::launch_gemm(xq, xs, M, K, (const uint8_t*)packed, N, fmt,
-                                    (const uint16_t*)bias, (uint16_t*)y, s, 1, {}, afmt),
+                                    (const uint16_t*)bias, (uint16_t*)y, s, 1, {}, afmt, part),
                     "gemm launch");
 }
 

@@ -293,7 +293,8 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
                                                       const uint8_t* __restrict__ packed, int N,
                                                       const uint16_t* __restrict__ bias,
                                                       uint16_t* __restrict__ y, int tiles_m,
-                                                      int tiles_n, int group_m, BatchStrides bs) {
+                                                      int tiles_n, int group_m, BatchStrides bs,
+                                                      float* __restrict__ part) {
   using C = TileCfg<WFMT, XFMT, FN, FM, S>;
   MX_BATCH_OFFSET(blockIdx.y);
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
@@ -318,9 +319,21 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   const int tn = (t % gsz) / gm;
   const int n0 = tn * C::BN, m0 = tm * C::BM;
 
-  const int NG = N >> 4, KT = K >> 7, KB = K >> 5;
+  const int NG = N >> 4, KB = K >> 5;
   const int LDX = K / 128 * C::XB;   // activation row bytes
-  const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * C::FB);
+  const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)(K >> 7) * NG * C::FB);
+  // K part of this workgroup (split K: grid z, whole groups of four K steps; one part unless
+  // `part` is given): the operand and scale bases move to the part's first step
+  const int pz = blockIdx.z, NP = gridDim.z;
+  const int G = ((K >> 7) + 3) >> 2;
+  const int g_lo = (int)((int64_t)pz * G / NP), g_hi = (int)((int64_t)(pz + 1) * G / NP);
+  const int kt_lo = 4 * g_lo;
+  const int KT = min(K >> 7, 4 * g_hi) - kt_lo;   // K steps of this part
+  const int KBr = KB - 4 * kt_lo;                 // scale bytes of a row from this part on
+  packed += (int64_t)kt_lo * NG * C::FB;
+  wsc += (int64_t)g_lo * NG * 64;
+  xq += (int64_t)kt_lo * C::XB;
+  xs += 4 * kt_lo;
 
   // ---- per-lane DMA sources, as 32-bit offsets from uniform bases (every operand < 2^31 B):
   // each DMA address is then a 64-bit scalar base plus a 32-bit lane offset, the instruction's
@@ -401,7 +414,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
       dma16((const uint8_t*)wsc + (uint32_t)(kt4 * NG * 256 + sa_src[i]),
             c < C::SA_PIECES ? base + c * 1024 : scratch);
     }
-    const int col = min(16 * kt4 + q4, KB - 4);
+    const int col = min(16 * kt4 + q4, KBr - 4);
 #pragma unroll
     for (int i = 0; i < C::SB_PER_WAVE; ++i) {
       const int c = wave + C::NDW * i;
@@ -414,7 +427,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     const uint8_t* base = slds + sbuf * C::SCALE_BYTES;
 #pragma unroll
     for (int i = 0; i < FN; ++i) sa[i] = *(const uint32_t*)(base + (wn * FN + i) * 256 + lane * 4);
-    const int left = KB - 16 * kt4;   // scale bytes of a row from this group on
+    const int left = KBr - 16 * kt4;   // scale bytes of a row from this group on
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
       const v4i w = *(const v4i*)(base + C::SA_BYTES + (wm * 16 * FM + 16 * j + r) * 16);
@@ -587,6 +600,22 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   asm volatile("s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 
+  if (part) {
+    // split K: this part's fp32 sums, row-major [part][M][N], for k_splitk_reduce to add in part
+    // order (bias and rounding there); written once, read once: non-temporal
+    float* pp = part + (int64_t)pz * M * N;
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const int n = n0 + wn * 16 * FN + 16 * i + 4 * g;
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        const int m = m0 + wm * 16 * FM + 16 * j + r;
+        if (m < M && n < N) __builtin_nontemporal_store(acc[i][j], (v4f*)(pp + (int64_t)m * N + n));
+      }
+    }
+    return;
+  }
+
   // ---- epilogue: bias, bf16 rounding, through LDS as a row-major [BM][BN] tile (rows padded
   // by 16 B so the 8-byte writes of a wave hit distinct banks), then 16-byte coalesced stores.
   // Lane holds n = 16 (wn FN + i) + 4 g + (0..3) of activation row wm 16 FM + 16 j + r.
@@ -623,11 +652,60 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
 template <int WFMT, int XFMT, int FN, int FM, int S>
 static void launch_tile(const uint8_t* xq, const uint8_t* xs, int M, int K, const uint8_t* packed,
                         int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s,
-                        int batch, const BatchStrides& bs) {
+                        int batch, const BatchStrides& bs, int parts = 1, float* part = nullptr) {
   using C = TileCfg<WFMT, XFMT, FN, FM, S>;
   const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((k_gemm_tile<WFMT, XFMT, FN, FM, S>), dim3((unsigned)(tm * tn), (unsigned)batch),
-                     dim3(512), 0, s, xq, xs, M, K, packed, N, bias, y, tm, tn, group_m, bs);
+  hipLaunchKernelGGL((k_gemm_tile<WFMT, XFMT, FN, FM, S>),
+                     dim3((unsigned)(tm * tn), (unsigned)batch, (unsigned)parts), dim3(512), 0, s,
+                     xq, xs, M, K, packed, N, bias, y, tm, tn, group_m, bs, part);
+}
+
+// Split K: the K parts' fp32 sums [P][M][N] added in part order, + bias, one bf16 rounding.
+// Four outputs per thread (N % 16 == 0), all parts' loads in flight together.
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ part, int P,
+                                                      int64_t MN, int N,
+                                                      const uint16_t* __restrict__ bias,
+                                                      uint16_t* __restrict__ y) {
+  for (int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4; i < MN;
+       i += (int64_t)gridDim.x * blockDim.x * 4) {
+    v4f v[kMaxSplit];
+#pragma unroll
+    for (int p = 0; p < kMaxSplit; ++p)
+      if (p < P) v[p] = __builtin_nontemporal_load((const v4f*)(part + p * MN + i));
+    v4f sum = v[0];
+#pragma unroll
+    for (int p = 1; p < kMaxSplit; ++p)
+      if (p < P) sum += v[p];
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+      const int n = (int)(i % N);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[e] = bf16_to_float(bias[n + e]);
+    }
+    const v2i o = {(int)pack_bf16x2(sum[0] + bv[0], sum[1] + bv[1]),
+                   (int)pack_bf16x2(sum[2] + bv[2], sum[3] + bv[3])};
+    *(v2i*)(y + i) = o;
+  }
+}
+
+// K parts for a single-layer tiled GEMM (M > 32) that would occupy at most 96 of the 256 CUs
+// with 128 x 128 tiles: about 256 workgroups, each at least one group of four K steps, at most
+// kMaxSplit parts; 1 = no split.  (At 128 tiles, two parts measured slower than none: the parts'
+// fp32 traffic then costs more than the idle half of the CUs; at 96 tiles, faster.)
+int gemm_split_parts(int64_t M, int64_t N, int64_t K) {
+  if (M <= 32 || K % 128 != 0 || N < 128) return 1;   // up to 32 rows: the decode kernels
+  const int64_t t = ((N + 127) / 128) * ((M + 127) / 128);
+  const int64_t G = (K / 128 + 3) / 4;
+  if (t > 96) return 1;
+  int64_t p = 256 / t;
+  if (p > kMaxSplit) p = kMaxSplit;
+  if (p > G) p = G;
+  return p < 2 ? 1 : (int)p;
+}
+
+int64_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
+  const int p = gemm_split_parts(M, N, K);
+  return p > 1 ? (int64_t)p * M * N * 4 : 0;
 }
 
 // Tile choice: the configurations below are compiled; pick the one whose tile count fills the
@@ -660,9 +738,20 @@ static TileChoice choose_tile(int M, int N, int batch) {
 template <int WFMT, int XFMT>
 static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int K,
                                const uint8_t* packed, int N, const uint16_t* bias, uint16_t* y,
-                               hipStream_t s, int batch, const BatchStrides& bs) {
-  const TileChoice c = choose_tile(M, N, batch);
+                               hipStream_t s, int batch, const BatchStrides& bs, float* part) {
   const int group_m = 4;
+  const int parts = part && batch == 1 && !batch_invariant() && g_force_tile.load() == 0
+                        ? gemm_split_parts(M, N, K) : 1;
+  if (parts > 1) {
+    // too few 128 x 128 tiles for the CUs: K parts on grid z, then the ordered sum
+    launch_tile<WFMT, XFMT, 4, 2, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s, 1, bs, parts, part);
+    const int64_t MN = (int64_t)M * N;
+    int64_t blocks = (MN / 4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, parts, MN, N, bias, y);
+    return hipGetLastError();
+  }
+  const TileChoice c = choose_tile(M, N, batch);
   if (c.fn == 8 && c.fm == 4) launch_tile<WFMT, XFMT, 8, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else if (c.fn == 7 && c.fm == 4) launch_tile<WFMT, XFMT, 7, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else if (c.fn == 6 && c.fm == 4) launch_tile<WFMT, XFMT, 6, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
@@ -678,7 +767,8 @@ static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int 
 
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
-                       uint16_t* y, hipStream_t s, int batch, BatchStrides bs, int afmt) {
+                       uint16_t* y, hipStream_t s, int batch, BatchStrides bs, int afmt,
+                       float* part) {
   // (weight, activation) formats: any weight format with E4M3 activations, or FP6 with FP6
   const int pair = fmt * 4 + afmt;
   if (afmt != 0 && (fmt == 0 || (afmt != 2 && afmt != 3))) return hipErrorInvalidValue;
@@ -687,16 +777,18 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t 
   if (afmt == 0 && !batch_invariant() && small_m_quantized(M, K))
     return launch_linear_small_m(xq, xs, true, M, K, packed, N, fmt, bias, y, s, batch, bs);
   const int m = (int)M, k = (int)K, n = (int)N;
-  const bool tiled = (K % 128 == 0) && (((uintptr_t)xs & 3) == 0) && M >= 64 && N >= 128;
+  // rows 33..63 go to the tiled kernel when it splits K (weight streamed by 256 workgroups)
+  const bool split = part && batch == 1 && !batch_invariant() && gemm_split_parts(M, N, K) > 1;
+  const bool tiled = (K % 128 == 0) && (((uintptr_t)xs & 3) == 0) && (M >= 64 || (split && M > 32)) && N >= 128;
   if (tiled) {
     switch (pair) {
-      case 0: return launch_tiled<0, 0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
-      case 8: return launch_tiled<2, 0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
-      case 12: return launch_tiled<3, 0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
-      case 10: return launch_tiled<2, 2>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
-      case 11: return launch_tiled<2, 3>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
-      case 14: return launch_tiled<3, 2>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
-      case 15: return launch_tiled<3, 3>(xq, xs, m, k, packed, n, bias, y, s, batch, bs);
+      case 0: return launch_tiled<0, 0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs, part);
+      case 8: return launch_tiled<2, 0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs, part);
+      case 12: return launch_tiled<3, 0>(xq, xs, m, k, packed, n, bias, y, s, batch, bs, part);
+      case 10: return launch_tiled<2, 2>(xq, xs, m, k, packed, n, bias, y, s, batch, bs, part);
+      case 11: return launch_tiled<2, 3>(xq, xs, m, k, packed, n, bias, y, s, batch, bs, part);
+      case 14: return launch_tiled<3, 2>(xq, xs, m, k, packed, n, bias, y, s, batch, bs, part);
+      case 15: return launch_tiled<3, 3>(xq, xs, m, k, packed, n, bias, y, s, batch, bs, part);
       default: return hipErrorInvalidValue;
     }
   }

@@ -52,11 +52,16 @@ void set_batch_invariant(bool on);
 bool batch_invariant();
 
 // GEMM from quantized activations xq + xs [M, K/32] (row-major): xq is E4M3 [M, K] (afmt 0)
-// or, with FP6 weights, packed E2M3 / E3M2 [M, 3K/4] (afmt 2 / 3).
+// or, with FP6 weights, packed E2M3 / E3M2 [M, 3K/4] (afmt 2 / 3).  With `part` (room for
+// gemm_split_bytes(M, N, K) bytes) a single layer with few tiles splits K across workgroups and
+// adds the parts in a second launch; without it K is never split across workgroups.
+constexpr int kMaxSplit = 8;
+int gemm_split_parts(int64_t M, int64_t N, int64_t K);
+int64_t gemm_split_bytes(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t K,
                        const uint8_t* packed, int64_t N, int fmt, const uint16_t* bias,
                        uint16_t* y, hipStream_t s, int batch = 1, BatchStrides bs = {},
-                       int afmt = 0);
+                       int afmt = 0, float* part = nullptr);
 
 // Small-M (decode) path: one launch, K split over the waves of a workgroup.  x is bf16 [M, K]
 // quantized inside the kernel (small_m_fused shapes) or, with quantized = true, E4M3 xq [M, K]

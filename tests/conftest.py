@@ -13,8 +13,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are collected everywhere but only run where a device exists; the driver
-    # selects them with -m gpu on the GPU box and -m "not gpu" here.
+    # GPU tests are collected everywhere; run them with -m gpu on a machine with an MI355X
+    # and deselect them with -m "not gpu" elsewhere.
     pass
 
 

@@ -136,8 +136,9 @@ int mxfp8_unpack_weight_shuffled16(const void* packed, int64_t N, int64_t K, voi
 
 /* Workspace bytes mxfp8_linear needs for (M, N, K, fmt) (0 for M == 0 or invalid arguments).
  * Layout: 64 KiB of counters, then the quantized activations between the quantizer and the
- * GEMM, or, for decode shapes (16 <= M <= 32, N % 64 == 0, K % 128 == 0), the partial sums of
- * the workgroups that split K.  When M > 32 and the layer has at most 96 tiles of 128 x 128
+ * GEMM, or, for decode shapes (16 <= M <= 64, N % 64 == 0, K % 128 == 0; above 32 rows only
+ * while a workgroup's share of x, M x K / P bf16 for its K part, is at most 256 KiB), the
+ * partial sums of the workgroups that split K.  Otherwise, when M > 32 and the layer has at most 96 tiles of 128 x 128
  * outputs (K % 128 == 0, N >= 128), the quantized activations are followed (at the next
  * 256-byte boundary) by fp32 partial sums [P][M][N] of the P <= 8 K parts that the GEMM then
  * computes in separate workgroups and adds in part order in a second launch, so that the call

@@ -84,9 +84,15 @@ int64_t quant_ws_bytes(int64_t M, int64_t K, int afmt = MX_FMT_E4M3) {
 // batch-invariant mode).  Its cross-workgroup sum costs about 2 us of memory round trips at
 // the end (store, count, load); below 16 rows the single-workgroup split of the small-M kernel
 // is faster (4096 x 4096: 6.3 against 7.6 us at M = 8; 8.2 against 7.7 at M = 16, 10.7 against
-// 9.2 at M = 32, where the small-M path needs a separate quantizer launch)
+// 9.2 at M = 32, where the small-M path needs a separate quantizer launch).  From 33 rows on it
+// is kept while one workgroup's share of x (M rows x K / P bf16) stays within 256 KiB; above
+// that the tiled GEMM with K split across workgroups is faster (4096 x 4096: 10.8 against 14.1
+// us at M = 33, 13.1 against 15.2 at M = 64; 8192 x 8192, M = 64: 28.1 against 24.5 us)
 constexpr int64_t kSkMinM = 16;
-bool sk_shape(int64_t M, int64_t N, int64_t K) { return M >= kSkMinM && mx::decode_sk_ok(M, N, K); }
+bool sk_shape(int64_t M, int64_t N, int64_t K) {
+  if (M < kSkMinM || !mx::decode_sk_ok(M, N, K)) return false;
+  return M <= 32 || M * (K / mx::decode_sk_parts(N, K)) * 2 <= (256 << 10);
+}
 
 // the split-K partial sums of the tiled GEMM follow the quantized activations
 int64_t split_offset(int64_t M, int64_t K, int afmt = MX_FMT_E4M3) {
@@ -97,13 +103,16 @@ int64_t quant_split_ws_bytes(int64_t M, int64_t N, int64_t K, int afmt = MX_FMT_
   return sb ? split_offset(M, K, afmt) + sb : quant_ws_bytes(M, K, afmt);
 }
 
+// mxfp8_linear's workspace: the split-K decode kernel's partial sums on its shapes (or, in
+// batch-invariant mode, the quantized activations), otherwise the quantized activations and,
+// where the tiled GEMM splits K, its partial sums
 int64_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
-  int64_t need = quant_split_ws_bytes(M, N, K);
   if (sk_shape(M, N, K)) {
     const int64_t sk = mx::kWorkspacePrefix + mx::decode_sk_workspace(M, N, K);
-    if (sk > need) need = sk;
+    const int64_t q = quant_ws_bytes(M, K);
+    return sk > q ? sk : q;
   }
-  return need;
+  return quant_split_ws_bytes(M, N, K);
 }
 
 // (weight, activation) format pairs with kernels: E4M3 activations with any weight format,
@@ -272,7 +281,8 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, i
                       "linear (small M) launch");
   uint8_t* xq = (uint8_t*)workspace + mx::kWorkspacePrefix;
   uint8_t* xs = xq + ((M * K + 255) / 256) * 256;
-  float* part = mx::gemm_split_bytes(M, N, K) ? (float*)((uint8_t*)workspace + split_offset(M, K)) : nullptr;
+  float* part = !sk_shape(M, N, K) && mx::gemm_split_bytes(M, N, K)
+                    ? (float*)((uint8_t*)workspace + split_offset(M, K)) : nullptr;
   hipError_t e = mx::launch_quantize_act((const uint16_t*)x_bf16, M, K, K, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "quantize_act launch");
   return hip_status(mx::launch_gemm(xq, xs, M, K, (const uint8_t*)packed, N, fmt,

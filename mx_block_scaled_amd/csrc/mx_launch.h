@@ -71,10 +71,11 @@ hipError_t launch_gemm(const uint8_t* xq, const uint8_t* xs, int64_t M, int64_t 
 // or the decode kernel's partial sums.
 constexpr int64_t kWorkspacePrefix = 64 * 1024;
 
-// Decode with K also split across workgroups, quantizer fused (M <= 32, K % 128 == 0,
+// Decode with K also split across workgroups, quantizer fused (M <= 64, K % 128 == 0,
 // N % 64 == 0): the counters of the workspace prefix, then decode_sk_workspace bytes of
-// partial sums.
+// partial sums.  decode_sk_parts: the number of K parts (workgroups per column group).
 bool decode_sk_ok(int64_t M, int64_t N, int64_t K);
+int decode_sk_parts(int64_t N, int64_t K);
 int64_t decode_sk_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear_decode_sk(const uint16_t* x, int64_t M, int64_t K, const uint8_t* packed,
                                    int64_t N, int fmt, const uint16_t* bias, uint16_t* y,

@@ -243,8 +243,8 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------------
-// Decode with the K dimension also split across workgroups (M <= 32, bf16 activations; used
-// from M = 16 on).
+// Decode with the K dimension also split across workgroups (M <= 64 in up to four 16-row
+// activation tiles, bf16 activations; used from M = 16 on).
 // Workgroup (b, p) computes 64 output columns (weight fragments 4 b .. 4 b + 3) over K part p
 // of P; its 8 waves take that part's K steps in turn.  Per K step a wave loads its activation
 // rows straight in the MFMA operand layout and quantizes them there: lane (r, g) holds row r's
@@ -263,6 +263,7 @@ __device__ __forceinline__ uint32_t lane_xor16(uint32_t v) {
 }
 
 constexpr int kSkMaxParts = 8;
+constexpr int kSkMaxM = 64;     // up to four 16-row activation tiles
 
 template <int WFMT, int MT>
 __global__ __launch_bounds__(512) void k_linear_decode_sk(const uint16_t* __restrict__ x, int M,
@@ -372,29 +373,40 @@ __global__ __launch_bounds__(512) void k_linear_decode_sk(const uint16_t* __rest
             a[c], b[t], acc[c][t], WFMT, 0, 0, (int)(sw[c] >> (8 * (kt & 3))), 0, (int)sb[t]);
   }
 
-  // wave partials, summed in wave order: wave w < CT finishes pair w = (c, t)
+  // wave partials, summed in wave order: wave w finishes pairs w, w + 8, ... of the CT pairs
+  // (c, t), pair index c MT + t
+  constexpr int PPW = (CT + kWaves - 1) / kWaves;
 #pragma unroll
   for (int c = 0; c < 4; ++c)
 #pragma unroll
     for (int t = 0; t < MT; ++t) red[wave][c * MT + t][lane] = acc[c][t];
   __syncthreads();
-  v4f s = {0.f, 0.f, 0.f, 0.f};
-  if (wave < CT) {
-    s = red[0][wave][lane];
+  v4f s[PPW];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) s += red[w][wave][lane];
+  for (int u = 0; u < PPW; ++u) {
+    const int pr = wave + kWaves * u;
+    s[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+    if (pr < CT) {
+      s[u] = red[0][pr][lane];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) s[u] += red[w][pr][lane];
+    }
   }
   if (P > 1) {
     // The partials go through device-coherent accesses (agent-scope atomic stores and loads,
     // which bypass the non-coherent caches), so the exchange needs no cache write-back or
     // invalidation: a workgroup's stores have completed (vmcnt 0) before its thread 0 counts it
     // in, and the last one reads the others' partials after its count.
-    if (wave < CT) {
-      uint64_t* dst = (uint64_t*)(part + ((int64_t)(p * NG4 + bx) * CT + wave) * 64 + lane);
-      uint64_t v[2];
-      __builtin_memcpy(v, &s, 16);
-      __hip_atomic_store(dst, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(dst + 1, v[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+      const int pr = wave + kWaves * u;
+      if (pr < CT) {
+        uint64_t* dst = (uint64_t*)(part + ((int64_t)(p * NG4 + bx) * CT + pr) * 64 + lane);
+        uint64_t v[2];
+        __builtin_memcpy(v, &s[u], 16);
+        __hip_atomic_store(dst, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 1, v[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): the stores are done
     __syncthreads();
@@ -403,41 +415,49 @@ __global__ __launch_bounds__(512) void k_linear_decode_sk(const uint16_t* __rest
              (uint32_t)(P - 1);
     __syncthreads();
     if (!last) return;
-    if (wave < CT) {
-      // all parts' loads in flight together, then the sum in part order, whichever workgroup
-      // finished last
-      uint64_t v[kSkMaxParts][2];
 #pragma unroll
-      for (int q = 0; q < kSkMaxParts; ++q) {
-        if (q < P) {
-          const uint64_t* src = (const uint64_t*)(part + ((int64_t)(q * NG4 + bx) * CT + wave) * 64 + lane);
-          v[q][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          v[q][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int u = 0; u < PPW; ++u) {
+      const int pr = wave + kWaves * u;
+      if (pr < CT) {
+        // all parts' loads in flight together, then the sum in part order, whichever
+        // workgroup finished last
+        uint64_t v[kSkMaxParts][2];
+#pragma unroll
+        for (int q = 0; q < kSkMaxParts; ++q) {
+          if (q < P) {
+            const uint64_t* src = (const uint64_t*)(part + ((int64_t)(q * NG4 + bx) * CT + pr) * 64 + lane);
+            v[q][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v[q][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
         }
-      }
 #pragma unroll
-      for (int q = 0; q < kSkMaxParts; ++q) {
-        if (q < P) {
-          v4f t;
-          __builtin_memcpy(&t, v[q], 16);
-          s = q == 0 ? t : s + t;
+        for (int q = 0; q < kSkMaxParts; ++q) {
+          if (q < P) {
+            v4f t;
+            __builtin_memcpy(&t, v[q], 16);
+            s[u] = q == 0 ? t : s[u] + t;
+          }
         }
       }
     }
     if (threadIdx.x == 0) __hip_atomic_store(&cnt[bx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  if (wave < CT) {
-    const int c = wave / MT, t = wave % MT;
-    const int m = 16 * t + r, n = 16 * (ng0 + c) + 4 * g;
-    if (m < M) {
-      float bv[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bv[i] = bf16_to_float(bias[n + i]);
+  for (int u = 0; u < PPW; ++u) {
+    const int pr = wave + kWaves * u;
+    if (pr < CT) {
+      const int c = pr / MT, t = pr % MT;
+      const int m = 16 * t + r, n = 16 * (ng0 + c) + 4 * g;
+      if (m < M) {
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bv[i] = bf16_to_float(bias[n + i]);
+        }
+        const v2i o = {(int)pack_bf16x2(s[u][0] + bv[0], s[u][1] + bv[1]),
+                       (int)pack_bf16x2(s[u][2] + bv[2], s[u][3] + bv[3])};
+        *(v2i*)(y + (int64_t)m * N + n) = o;
       }
-      const v2i o = {(int)pack_bf16x2(s[0] + bv[0], s[1] + bv[1]),
-                     (int)pack_bf16x2(s[2] + bv[2], s[3] + bv[3])};
-      *(v2i*)(y + (int64_t)m * N + n) = o;
     }
   }
 }
@@ -453,11 +473,11 @@ int decode_sk_parts(int64_t N, int64_t K) {
 }
 
 bool decode_sk_ok(int64_t M, int64_t N, int64_t K) {
-  return M >= 1 && M <= 32 && K % 128 == 0 && N % 64 == 0 && N / 64 * 4 <= kWorkspacePrefix;
+  return M >= 1 && M <= kSkMaxM && K % 128 == 0 && N % 64 == 0 && N / 64 * 4 <= kWorkspacePrefix;
 }
 
 int64_t decode_sk_workspace(int64_t M, int64_t N, int64_t K) {
-  const int64_t mt = M <= 16 ? 1 : 2;
+  const int64_t mt = (M + 15) / 16;
   return decode_sk_parts(N, K) * (N / 64) * 4 * mt * 64 * 16;
 }
 
@@ -474,8 +494,12 @@ hipError_t launch_linear_decode_sk(const uint16_t* x, int64_t M, int64_t K, cons
   do {                                                                                                \
     if (M <= 16)                                                                                      \
       hipLaunchKernelGGL((k_linear_decode_sk<W, 1>), grid, block, 0, s, x, m, k, packed, n, bias, y, P, cnt, part); \
-    else                                                                                              \
+    else if (M <= 32)                                                                                 \
       hipLaunchKernelGGL((k_linear_decode_sk<W, 2>), grid, block, 0, s, x, m, k, packed, n, bias, y, P, cnt, part); \
+    else if (M <= 48)                                                                                 \
+      hipLaunchKernelGGL((k_linear_decode_sk<W, 3>), grid, block, 0, s, x, m, k, packed, n, bias, y, P, cnt, part); \
+    else                                                                                              \
+      hipLaunchKernelGGL((k_linear_decode_sk<W, 4>), grid, block, 0, s, x, m, k, packed, n, bias, y, P, cnt, part); \
   } while (0)
   switch (fmt) {
     case 0: MX_SK(0); break;

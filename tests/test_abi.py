@@ -61,12 +61,21 @@ def test_quantize_act_validation(L):
 
 
 def test_linear_validation(L):
+    assert L.mxfp8_workspace_bytes(65, 256, 512, 0) == 65536 + 65 * 512 + 65 * 16  # prefix, xq, xs
+    # 64 rows: the split-K decode kernel in one K part (4 column groups x 16 pairs x 1 KiB),
+    # or, in batch-invariant mode, the quantized activations, which need less
     ws = L.mxfp8_workspace_bytes(64, 256, 512, 0)
-    assert ws == 65536 + 64 * 512 + 64 * 16     # counter prefix, xq, xs
-    # decode shapes with K split across workgroups (16 <= M <= 32, N % 64 == 0): the prefix,
+    assert ws == 65536 + 4 * 16 * 1024
+    # decode shapes with K split across workgroups (16 <= M <= 64, N % 64 == 0): the prefix,
     # then the partial sums (4 K parts x N/64 column groups x (fragment, tile) pairs x 1 KiB)
     assert L.mxfp8_workspace_bytes(32, 4096, 4096, 0) == 65536 + 4 * 64 * 8 * 1024
     assert L.mxfp8_workspace_bytes(16, 4096, 4096, 0) == 65536 + 4 * 64 * 4 * 1024
+    assert L.mxfp8_workspace_bytes(48, 4096, 4096, 0) == 65536 + 4 * 64 * 12 * 1024
+    assert L.mxfp8_workspace_bytes(64, 4096, 4096, 0) == 65536 + 4 * 64 * 16 * 1024
+    # above 64 rows, 32 tiles of 128 x 128: the quantized activations, then 8 K parts of fp32
+    # sums of the tiled GEMM
+    q = 65536 + 65 * 4096 + 65 * 128
+    assert L.mxfp8_workspace_bytes(65, 4096, 4096, 0) == (q + 255) // 256 * 256 + 8 * 65 * 4096 * 4
     assert L.mxfp8_workspace_bytes(8, 4096, 4096, 0) == 65536 + 8 * 4096 + 8 * 128
     assert L.mxfp8_workspace_bytes(1, 4096, 4096, 0) == 65536 + 4096 + 128
     assert L.mxfp8_linear(A, 64, 512, B, 256, 0, None, B, B, ws - 1, None) == MX_EWORKSPACE

@@ -1,5 +1,5 @@
 """GPU parity of the decode path that splits K across workgroups (mxfp8_linear with bf16
-activations, 16 <= M <= 32, N % 64 == 0, K % 128 == 0).
+activations, 16 <= M <= 64, N % 64 == 0, K % 128 == 0).
 
 That kernel quantizes the activations itself, in the MFMA operand layout, and adds the K parts
 of a column group in a fixed order chosen by the last workgroup to finish (a counter in the
@@ -33,6 +33,10 @@ SHAPES = [
     (20, 1024, 8192),   # eight parts
     (32, 16384, 1024),  # 256 column groups: one part, no cross-workgroup sum
     (24, 640, 2560),    # ten column groups, two parts of 10 K steps
+    (33, 4096, 4096),   # three activation tiles, the third with one row
+    (48, 2048, 4096),   # three full tiles, eight parts
+    (64, 4096, 4096),   # four tiles: each wave finishes two (fragment, tile) pairs
+    (57, 1024, 1152),   # four tiles, one part of 9 K steps: no cross-workgroup sum
 ]
 
 
@@ -89,7 +93,8 @@ def test_decode_split_k_workspace_reuse():
     repeats its first result bit for bit, so the counters are back at zero after each call."""
     K = 4096
     g = np.random.default_rng(11)
-    shapes = [(32, 4096), (16, 1024), (3, 4096), (300, 256), (1, 4096), (20, 640)]
+    shapes = [(32, 4096), (16, 1024), (3, 4096), (300, 256), (1, 4096), (20, 640), (64, 4096),
+              (100, 4096)]
     ws_bytes = max(mxfp8.workspace_bytes(M, N, K) for M, N in shapes)
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=DEV)
     calls = []
@@ -103,7 +108,7 @@ def test_decode_split_k_workspace_reuse():
     first = [mxfp8.linear(x, pk, N, 0, workspace=ws).clone() for x, pk, N in calls]
     assert int(ws[:65536].count_nonzero()) == 0
     for rnd in range(3):
-        for i in ([0, 1, 2, 3, 4, 5] if rnd != 1 else [5, 3, 0, 0, 2, 1, 4]):
+        for i in ([0, 1, 2, 3, 4, 5, 6, 7] if rnd != 1 else [5, 3, 7, 0, 6, 0, 2, 1, 4]):
             x, pk, N = calls[i]
             y = mxfp8.linear(x, pk, N, 0, workspace=ws)
             assert torch.equal(y.view(torch.int16), first[i].view(torch.int16)), (rnd, i)
@@ -119,7 +124,8 @@ def test_decode_split_k_graph_replay():
     wb = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
     wq, wsc = orc.quantize(wb, 0)
     pk = mxfp8.prepack_weight(u8_dev(wq), u8_dev(wsc), 0)
-    xs = [bf16_dev(synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32))) for M in (32, 16, 2)]
+    xs = [bf16_dev(synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32)))
+          for M in (32, 16, 2, 64, 100)]
     ws = torch.zeros(max(mxfp8.workspace_bytes(x.shape[0], N, K) for x in xs),
                      dtype=torch.uint8, device=DEV)
     ys = [torch.empty((x.shape[0], N), dtype=torch.bfloat16, device=DEV) for x in xs]
@@ -149,13 +155,13 @@ def test_decode_split_k_graph_replay():
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("M", [1, 8, 16, 32, 100])
+@pytest.mark.parametrize("M", [1, 8, 16, 32, 50, 64, 100])
 def test_fused_quantizers_bit_exact_through_identity_weight(M):
     """With W = I (E4M3 1.0 on the diagonal, scale 2^0) every output is one dequantized
     activation, exact in fp32 and in bf16, so the layer's output equals the oracle's
     dequantize(quantize(x)) bit for bit: a bit-level check of the quantizer each path fuses
-    (small-M kernel at M = 1 and 8, split-K decode kernel at 16 and 32, quantizer launch + tiled
-    GEMM at 100).  Inputs hold outlier channels, all-zero blocks, values that saturate at 448
+    (small-M kernel at M = 1 and 8, split-K decode kernel at 16, 32, 50 and 64, quantizer launch
+    + tiled GEMM at 100).  Inputs hold outlier channels, all-zero blocks, values that saturate at 448
     after scaling, bf16 subnormals and exact rounding ties."""
     K = N = 2048
     g = np.random.default_rng(M + 77)

@@ -242,7 +242,7 @@ def test_small_m_fused(M, N, K, fmt):
 
 def _splits_k(M, N, K):
     """shapes on which mxfp8_linear runs the decode kernel that splits K across workgroups"""
-    return 16 <= M <= 32 and N % 64 == 0 and K % 128 == 0
+    return 16 <= M <= 64 and N % 64 == 0 and K % 128 == 0
 
 
 @pytest.mark.parametrize("M", [1, 8, 32])

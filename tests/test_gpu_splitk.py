@@ -1,5 +1,7 @@
 """GPU parity of the tiled GEMM with K split across workgroups (single layers whose 128 x 128
-tiles would fill at most 96 of the 256 CUs, 33 <= M, through an entry point with a workspace).
+tiles would fill at most 96 of the 256 CUs, through an entry point with a workspace: with bf16
+activations from 33 rows on where the split-K decode kernel is not taken (M > 64, or a
+workgroup's share of x above 256 KiB there), with MXFP6 activations from 33 rows on).
 
 Each workgroup computes one tile over one K part (whole groups of four K steps) and writes
 fp32 sums; a second kernel adds the parts in part order, adds the bias and rounds once.
@@ -23,12 +25,14 @@ FMTS = {0: "e4m3", 2: "e2m3", 3: "e3m2"}
 
 # (M, N, K): parts = min(8, 256 // tiles, groups of four K steps)
 SHAPES = [
-    (33, 4096, 4096),    # 32 tiles, 8 parts of one group
-    (64, 2048, 4096),    # 16 tiles, 8 parts
+    (65, 4096, 4096),    # 32 tiles, 8 parts of one group
+    (80, 2048, 4096),    # 16 tiles, 8 parts
     (100, 4096, 4480),   # 32 tiles, 35 K steps in 9 groups: 8 parts, the last of 4 + 3 steps
     (128, 4096, 4096),   # 32 tiles, 8 parts
     (256, 1040, 8192),   # 18 tiles (ragged N), 8 parts of 2 groups
     (300, 4096, 2048),   # 96 tiles, 2 parts of 2 groups (ragged M)
+    (48, 8192, 8192),    # 64 tiles, 4 parts: a workgroup's share of x would exceed 256 KiB in
+                         # the split-K decode kernel, so 48 rows take this path
 ]
 
 
@@ -51,7 +55,7 @@ def _layer(w_bits, fmt, b_bits):
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("fmt", [0, 2, 3])
 def test_split_k_matches_oracle(M, N, K, fmt):
-    if fmt != 0 and (M, N, K) in [(256, 1040, 8192), (300, 4096, 2048)]:
+    if fmt != 0 and (M, N, K) in [(256, 1040, 8192), (300, 4096, 2048), (48, 8192, 8192)]:
         pytest.skip("the FP6 formats are covered on the other shapes")
     x, w, b = _inputs(M, N, K, M + N + K + fmt)
     use_bias = (M + fmt) % 2 == 0
@@ -67,8 +71,9 @@ def test_split_k_matches_oracle(M, N, K, fmt):
 
 @pytest.mark.parametrize("fmt", [2, 3])
 def test_split_k_fp6_activations(fmt):
-    """W6A6 (mxfp8_linear_fmt): the same split with FP6 activation rows of 96 bytes per K step."""
-    M, N, K = 64, 2048, 2048
+    """W6A6 (mxfp8_linear_fmt): the same split with FP6 activation rows of 96 bytes per K step,
+    from 33 rows on."""
+    M, N, K = 33, 2048, 2048
     x, w, b = _inputs(M, N, K, 40 + fmt)
     layer, wq, ws = _layer(w, fmt, b)
     banner("tiled split-K, W6A6", M, N, K, FMTS[fmt])

@@ -17,9 +17,9 @@ Also measured and printed in the same JSON line:
   decode        the decode workload (x [M, 4096], M in {1, 8, 32}, weight [4096, 4096], bias),
                 one fused call each, replayed from a HIP graph over 32 rotated weight copies:
                 time per call, algorithmic bytes / time against 8 TB/s; the same for M = 64
-                and 128 (prefill chunks too small to fill the GPU with output tiles: the
-                tiled GEMM with K split across workgroups), and every M again in
-                batch-invariant mode;
+                and 128 (prefill chunks too small to fill the GPU with output tiles, where K
+                is split across workgroups: the split-K decode kernel at 64 rows, the tiled
+                GEMM at 128), and every M again in batch-invariant mode;
   other_workloads  outlier activations on the pre-quantized entry (2048 x 6144 x 4096, GEMM
                 only), MXFP6 weights (E2M3 and E3M2, 512 x 8192 x 8192, activation quantization
                 included) with MXFP8 activations and with MXFP6 activations of the same format

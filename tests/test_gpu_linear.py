@@ -362,3 +362,42 @@ def test_bias_at_odd_offset(M):
     y2 = mxfp8.linear_prequant(u8_dev(xq), u8_dev(xs), layer.packed, N, 0, bias_t)
     ok, rep = tolerance.check(host_bf16_bits(y2), ref, name="bias-odd-prequant-%d" % M)
     assert ok, rep
+
+
+# one shape per mxfp8_linear path: small-M fused, split-K decode (2 and 4 row tiles), split-K
+# tiled GEMM with its reduction launch (8 and 2 K parts), tiled GEMM, generic GEMM
+# (K % 128 != 0)
+PATH_SHAPES = [(8, 1024, 2048), (32, 1024, 4096), (64, 2048, 4096), (100, 2048, 4096),
+               (300, 4096, 4096), (300, 8192, 1024), (40, 512, 1120)]
+
+
+@pytest.mark.parametrize("M,N,K", PATH_SHAPES)
+def test_workspace_and_output_bounds_every_path(M, N, K):
+    """Each path writes only y [M, N] and the first workspace_bytes(M, N, K) bytes of its
+    workspace: guard bands around both keep their fill, the counters are left at zero, and a
+    second call into the same buffers repeats the first result bit for bit."""
+    g = np.random.default_rng(M + N + K)
+    x = bf16_dev(synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32)))
+    wb = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    b = bf16_dev(synth.bf16_bits((g.standard_normal(N) * 0.05).astype(np.float32)))
+    wq, wsc = orc.quantize(wb, 0)
+    pk = mxfp8.prepack_weight(u8_dev(wq), u8_dev(wsc), 0)
+    guard = 8192
+    need = mxfp8.workspace_bytes(M, N, K)
+    wbig = torch.full((need + 2 * guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    wbig[guard:guard + 65536].zero_()                         # counters start at zero
+    ws = wbig[guard:guard + need]
+    ybig = torch.full((M * N + 2 * guard,), -7777.0, dtype=torch.bfloat16, device=DEV)
+    y = ybig[guard:guard + M * N].view(M, N)
+    banner("bounds of every path", M, N, K, "workspace", need)
+    mxfp8.linear(x, pk, N, 0, b, out=y, workspace=ws)
+    y1 = y.clone()
+    mxfp8.linear(x, pk, N, 0, b, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y1.view(torch.int16))
+    assert bool((wbig[:guard] == 0xA5).all()) and bool((wbig[guard + need:] == 0xA5).all())
+    assert int(ws[:65536].count_nonzero()) == 0
+    assert bool((ybig[:guard] == -7777.0).all()) and bool((ybig[guard + M * N:] == -7777.0).all())
+    ref, _, _ = orc.linear_ref(host_bf16_bits(x), wq, wsc, 0, host_bf16_bits(b))
+    ok, rep = tolerance.check(host_bf16_bits(y), ref, name="bounds-%d-%d-%d" % (M, N, K))
+    assert ok, rep

@@ -119,6 +119,55 @@ __device__ __forceinline__ uint32_t amax8_bf16(const v4i& v) {
   return m;
 }
 
+// ds_swizzle, bit-mask mode: lane i of each 32-lane half reads lane i ^ 16
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+}
+
+// One 16-row activation tile of a 128-wide K step, quantized to E4M3 (OCP MX rule: the same
+// codes and scales as k_quantize_act) straight in the scaled MFMA's B-operand layout.  Lane
+// (r, g) = (lane % 16, lane / 16) brings row r's bf16 elements 16 g .. 16 g + 15 (xv[0], xv[1])
+// and 64 + 16 g .. 64 + 16 g + 15 (xv[2], xv[3]): halves of MX blocks g / 2 and 2 + g / 2,
+// whose other halves are in lane ^ 16.  Out: the lane's 32 operand bytes and the scale byte
+// the MFMA reads from this lane, that of block g.
+__device__ __forceinline__ void quantize_tile_operand_e4m3(const v4i (&xv)[4], int lane, v8i& b,
+                                                           uint32_t& sb) {
+  const int g = lane >> 4;
+  uint32_t m0 = amax8_bf16(xv[0]), m1 = amax8_bf16(xv[2]);
+  const uint32_t m0b = amax8_bf16(xv[1]), m1b = amax8_bf16(xv[3]);
+  m0 = m0 > m0b ? m0 : m0b;
+  m1 = m1 > m1b ? m1 : m1b;
+  const uint32_t o0 = lane_xor16(m0), o1 = lane_xor16(m1);
+  m0 = m0 > o0 ? m0 : o0;    // block g / 2
+  m1 = m1 > o1 ? m1 : o1;    // block 2 + g / 2
+  const uint32_t e0 = scale_byte_from_amax<0>(m0), e1 = scale_byte_from_amax<0>(m1);
+  uint32_t q[8];
+  if (e0 == 0xFFu) {
+    q[0] = q[1] = q[2] = q[3] = 0x7F7F7F7Fu;   // block holds Inf/NaN: NaN codes
+  } else {
+    const float sc = e8m0_to_float(e0);
+    q[0] = cvt4_e4m3((uint32_t)xv[0][0], (uint32_t)xv[0][1], sc);
+    q[1] = cvt4_e4m3((uint32_t)xv[0][2], (uint32_t)xv[0][3], sc);
+    q[2] = cvt4_e4m3((uint32_t)xv[1][0], (uint32_t)xv[1][1], sc);
+    q[3] = cvt4_e4m3((uint32_t)xv[1][2], (uint32_t)xv[1][3], sc);
+  }
+  if (e1 == 0xFFu) {
+    q[4] = q[5] = q[6] = q[7] = 0x7F7F7F7Fu;
+  } else {
+    const float sc = e8m0_to_float(e1);
+    q[4] = cvt4_e4m3((uint32_t)xv[2][0], (uint32_t)xv[2][1], sc);
+    q[5] = cvt4_e4m3((uint32_t)xv[2][2], (uint32_t)xv[2][3], sc);
+    q[6] = cvt4_e4m3((uint32_t)xv[3][0], (uint32_t)xv[3][1], sc);
+    q[7] = cvt4_e4m3((uint32_t)xv[3][2], (uint32_t)xv[3][3], sc);
+  }
+  b = (v8i){(int)q[0], (int)q[1], (int)q[2], (int)q[3], (int)q[4], (int)q[5], (int)q[6], (int)q[7]};
+  // the MFMA takes block g's scale from this lane: g = 0 and 3 computed it (e0 of block 0, e1
+  // of block 3); block 1 sits in e0 of g = 2 and block 2 in e1 of g = 1 (lane ^ 48)
+  const uint32_t give = g == 1 ? e1 : e0;
+  const uint32_t got = (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 48) << 2, (int)give);
+  sb = g == 0 ? e0 : (g == 3 ? e1 : got);
+}
+
 template <int AFMT, int BFMT>
 __device__ __forceinline__ v4f mfma16(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, AFMT, BFMT, 0, sa, 0, sb);

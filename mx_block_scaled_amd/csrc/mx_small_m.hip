@@ -257,11 +257,6 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
 // partials of a column group in part order by the last of them to arrive (a counter per
 // column group in the workspace, left at zero by that workgroup; no workgroup ever waits).
 
-__device__ __forceinline__ uint32_t lane_xor16(uint32_t v) {
-  // ds_swizzle, bit-mask mode: lane i of each 32-lane half reads lane i ^ 16
-  return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
-}
-
 constexpr int kSkMaxParts = 8;
 constexpr int kSkMaxM = 64;     // up to four 16-row activation tiles
 
@@ -330,41 +325,7 @@ __global__ __launch_bounds__(512) void k_linear_decode_sk(const uint16_t* __rest
     v8i b[MT];
     uint32_t sb[MT];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      uint32_t m0 = amax8_bf16(xv[t][0]), m1 = amax8_bf16(xv[t][2]);
-      const uint32_t m0b = amax8_bf16(xv[t][1]), m1b = amax8_bf16(xv[t][3]);
-      m0 = m0 > m0b ? m0 : m0b;
-      m1 = m1 > m1b ? m1 : m1b;
-      const uint32_t o0 = lane_xor16(m0), o1 = lane_xor16(m1);
-      m0 = m0 > o0 ? m0 : o0;    // block g / 2
-      m1 = m1 > o1 ? m1 : o1;    // block 2 + g / 2
-      const uint32_t e0 = scale_byte_from_amax<0>(m0), e1 = scale_byte_from_amax<0>(m1);
-      uint32_t q[8];
-      if (e0 == 0xFFu) {
-        q[0] = q[1] = q[2] = q[3] = 0x7F7F7F7Fu;   // block holds Inf/NaN: NaN codes
-      } else {
-        const float sc = e8m0_to_float(e0);
-        q[0] = cvt4_e4m3((uint32_t)xv[t][0][0], (uint32_t)xv[t][0][1], sc);
-        q[1] = cvt4_e4m3((uint32_t)xv[t][0][2], (uint32_t)xv[t][0][3], sc);
-        q[2] = cvt4_e4m3((uint32_t)xv[t][1][0], (uint32_t)xv[t][1][1], sc);
-        q[3] = cvt4_e4m3((uint32_t)xv[t][1][2], (uint32_t)xv[t][1][3], sc);
-      }
-      if (e1 == 0xFFu) {
-        q[4] = q[5] = q[6] = q[7] = 0x7F7F7F7Fu;
-      } else {
-        const float sc = e8m0_to_float(e1);
-        q[4] = cvt4_e4m3((uint32_t)xv[t][2][0], (uint32_t)xv[t][2][1], sc);
-        q[5] = cvt4_e4m3((uint32_t)xv[t][2][2], (uint32_t)xv[t][2][3], sc);
-        q[6] = cvt4_e4m3((uint32_t)xv[t][3][0], (uint32_t)xv[t][3][1], sc);
-        q[7] = cvt4_e4m3((uint32_t)xv[t][3][2], (uint32_t)xv[t][3][3], sc);
-      }
-      b[t] = (v8i){(int)q[0], (int)q[1], (int)q[2], (int)q[3], (int)q[4], (int)q[5], (int)q[6], (int)q[7]};
-      // the MFMA takes block g's scale from this lane: g = 0 and 3 computed it (e0 of block 0,
-      // e1 of block 3); block 1 sits in e0 of g = 2 and block 2 in e1 of g = 1 (lane ^ 48)
-      const uint32_t give = g == 1 ? e1 : e0;
-      const uint32_t got = (uint32_t)__builtin_amdgcn_ds_bpermute((lane ^ 48) << 2, (int)give);
-      sb[t] = g == 0 ? e0 : (g == 3 ? e1 : got);
-    }
+    for (int t = 0; t < MT; ++t) quantize_tile_operand_e4m3(xv[t], lane, b[t], sb[t]);
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll

@@ -155,14 +155,16 @@ def test_decode_split_k_graph_replay():
         torch.cuda.synchronize()
 
 
+@pytest.mark.parametrize("bi", [False, True])
 @pytest.mark.parametrize("M", [1, 8, 16, 32, 50, 64, 100])
-def test_fused_quantizers_bit_exact_through_identity_weight(M):
+def test_fused_quantizers_bit_exact_through_identity_weight(M, bi):
     """With W = I (E4M3 1.0 on the diagonal, scale 2^0) every output is one dequantized
     activation, exact in fp32 and in bf16, so the layer's output equals the oracle's
     dequantize(quantize(x)) bit for bit: a bit-level check of the quantizer each path fuses
     (small-M kernel at M = 1 and 8, split-K decode kernel at 16, 32, 50 and 64, quantizer launch
-    + tiled GEMM at 100).  Inputs hold outlier channels, all-zero blocks, values that saturate at 448
-    after scaling, bf16 subnormals and exact rounding ties."""
+    + tiled GEMM at 100; in batch-invariant mode the quantizer launch + generic or tiled GEMM).  Inputs hold outlier
+    channels, all-zero blocks, values that saturate at 448 after scaling, bf16 subnormals and
+    exact rounding ties."""
     K = N = 2048
     g = np.random.default_rng(M + 77)
     x = g.standard_normal((M, K)).astype(np.float32)
@@ -175,8 +177,12 @@ def test_fused_quantizers_bit_exact_through_identity_weight(M):
     x_bits = synth.bf16_bits(x)
     w = np.eye(N, K, dtype=np.float32)
     layer, wq, ws = _layer(synth.bf16_bits(w), 0, None)
-    banner("identity weight, bit-exact quantizer", M, N, K)
-    y = host_bf16_bits(layer(bf16_dev(x_bits)))
+    banner("identity weight, bit-exact quantizer", M, N, K, "batch-invariant" if bi else "")
+    mxfp8.set_batch_invariant(bi)
+    try:
+        y = host_bf16_bits(layer(bf16_dev(x_bits)))
+    finally:
+        mxfp8.set_batch_invariant(False)
     xq, xs = orc.quantize(x_bits, orc.E4M3)
     expect = orc.f64_to_bf16(orc.dequantize(xq, xs, orc.E4M3))
     # the layer's output is a sum started at +0, so a code of -0 comes out as +0

@@ -279,17 +279,21 @@ def test_tiled_kernel_many_tiles(K, fmt):
         mxfp8.set_tile_config(0, 0)
 
 
+@pytest.mark.parametrize("fmt", [0, 2])
 @pytest.mark.parametrize("K", [512, 4224, 544])
-def test_batch_invariant_mode(K):
+def test_batch_invariant_mode(K, fmt):
     """Batch-invariant mode: the first rows of a 300-row call (tiled kernel; K % 128 != 0:
-    generic kernel) are bit-identical to the same rows called alone at M = 1, 8, 17 and 32,
-    on both entries; the default mode is still checked against the oracle."""
-    g = np.random.default_rng(K)
+    generic kernel) are bit-identical to the same rows called alone at M = 1, 8, 16, 17, 31
+    and 32 (generic kernel, one and two activation tiles), on both entries, with E4M3 and E2M3
+    weights; the mode's result is checked against the oracle."""
+    g = np.random.default_rng(K + fmt)
     M, N = 300, 272
-    x = synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    xf = g.standard_normal((M, K)).astype(np.float32)
+    xf[:, g.choice(K, 4, replace=False)] *= 50.0                     # outlier channels
+    x = synth.bf16_bits(xf)
     w = synth.bf16_bits((g.standard_normal((N, K)) * 0.03).astype(np.float32))
     b = synth.bf16_bits((g.standard_normal(N) * 0.1).astype(np.float32))
-    layer, wq, ws = _layer(w, 0, b)
+    layer, wq, ws = _layer(w, fmt, b)
     xd = bf16_dev(x)
     xq, xs = mxfp8.quantize_act(xd)
     banner("batch invariant", K)
@@ -298,15 +302,15 @@ def test_batch_invariant_mode(K):
         y_all = layer(xd)
         yq_all = layer.apply_quantized(xq, xs)
         assert torch.equal(y_all.view(torch.int16), yq_all.view(torch.int16))
-        for m in (1, 8, 17, 32):
+        for m in (1, 8, 16, 17, 31, 32):
             y = layer(xd[:m].contiguous())
             yq = layer.apply_quantized(xq[:m].contiguous(), xs[:m].contiguous())
             assert torch.equal(y.view(torch.int16), y_all[:m].view(torch.int16)), m
             assert torch.equal(yq.view(torch.int16), y_all[:m].view(torch.int16)), m
     finally:
         mxfp8.set_batch_invariant(False)
-    ref, _, _ = orc.linear_ref(x, wq, ws, 0, b)
-    ok, rep = tolerance.check(host_bf16_bits(y_all), ref, name="batch-invariant-%d" % K)
+    ref, _, _ = orc.linear_ref(x, wq, ws, fmt, b)
+    ok, rep = tolerance.check(host_bf16_bits(y_all), ref, name="batch-invariant-%d-%d" % (K, fmt))
     assert ok, rep
 
 

@@ -75,7 +75,14 @@ def test_linear_validation(L):
     # above 64 rows, 32 tiles of 128 x 128: the quantized activations, then 8 K parts of fp32
     # sums of the tiled GEMM
     q = 65536 + 65 * 4096 + 65 * 128
-    assert L.mxfp8_workspace_bytes(65, 4096, 4096, 0) == (q + 255) // 256 * 256 + 8 * 65 * 4096 * 4
+    need65 = (q + 255) // 256 * 256 + 8 * 65 * 4096 * 4
+    assert L.mxfp8_workspace_bytes(65, 4096, 4096, 0) == need65
+    # one byte short of the split-K parts: rejected before any launch
+    assert L.mxfp8_linear(A, 65, 4096, B, 4096, 0, None, B, B, need65 - 1, None) == MX_EWORKSPACE
+    assert b"needed" in L.mxfp8_last_error()
+    # FP6 activations: the same split from 33 rows (no split-K decode kernel on that entry)
+    q6 = 65536 + 40 * 3072 + 40 * 128
+    assert L.mxfp8_workspace_bytes_fmt(40, 4096, 4096, 2, 2) == (q6 + 255) // 256 * 256 + 8 * 40 * 4096 * 4
     assert L.mxfp8_workspace_bytes(8, 4096, 4096, 0) == 65536 + 8 * 4096 + 8 * 128
     assert L.mxfp8_workspace_bytes(1, 4096, 4096, 0) == 65536 + 4096 + 128
     assert L.mxfp8_linear(A, 64, 512, B, 256, 0, None, B, B, ws - 1, None) == MX_EWORKSPACE

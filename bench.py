@@ -130,6 +130,9 @@ def main():
     # ------------------------------------------------------------ prefill workload
     M, N, K = 4096, 14336, 4096
     d = synth.make("prefill")
+    # SHA-256 of the generated bf16 inputs (bit patterns), so a run names its exact data
+    inputs_sha = {k: hashlib.sha256(np.ascontiguousarray(d[k]).tobytes()).hexdigest()[:16]
+                  for k in ("x", "w")}
     x0 = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
     w0 = torch.from_numpy(d["w"].view(np.int16)).view(torch.bfloat16).to(dev)
     wq, ws = mxfp8.quantize_weight(w0, "e4m3")
@@ -473,7 +476,7 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights quantized on the GPU)",
         "config": {"workload": "prefill MLP up-proj: x bf16 [4096,4096] x W mxfp8 [14336,4096] "
                                "-> y bf16 [4096,14336], act quant included",
-                   "M": M, "N": N, "K": K, "rotated_sets": R},
+                   "M": M, "N": N, "K": K, "rotated_sets": R, "inputs_sha256_16": inputs_sha},
         "roofline": roofline,
         "quantizer": {"us": round(quant_us, 2), "GB/s": round(quant_bytes / (quant_us * 1e-6) / 1e9, 1),
                       "hbm_frac": round(quant_bytes / (quant_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},

@@ -75,9 +75,13 @@ int mxfp8_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t ldx,
 /* Fused producer of a pre-quantized activation: RMS norm, then the quantization above (the
  * Mxfp8LinearKernel page's input_quant_key: a layer may take activations quantized outside
  * it, with row-major [M, K/32] E8M0 scales; the pages name no producer, and the norm here is
- * the usual RMS norm with a bf16 weight, each product rounded to bf16):
- *     r = 1 / sqrt(sum_k x_k^2 / K + eps)   (fp64),   y_k = bf16(bf16(x_k r) gamma_k),
- * then y is quantized exactly as mxfp8_quantize_act quantizes a bf16 input.
+ * the usual RMS norm with a bf16 weight computed in fp32, each fp32 quantity being the value
+ * nearest to its exact definition):
+ *     r32 = fp32(1 / sqrt(sum_k x_k^2 / K + eps)),   p_k = fp32(x_k r32),
+ *     t_k = bf16(p_k),                               y_k = bf16(t_k gamma_k),
+ * all roundings to nearest even; then y is quantized exactly as mxfp8_quantize_act quantizes
+ * a bf16 input.  The sum of squares is taken in fp64, so r32 is the correctly rounded value
+ * except for a row whose r lies within about 2^-45 (relative) of an fp32 rounding boundary.
  *   x_bf16 [16]  bf16 [M, ldx] (ldx >= K, ldx % 8 == 0)
  *   gamma  [16]  bf16 [K]
  *   eps          finite, >= 0

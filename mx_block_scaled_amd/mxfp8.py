@@ -89,21 +89,79 @@ def _fmt(fmt):
 def _u8(t, name):
     if t.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e8m0fnu):
         raise TypeError("%s must be uint8 / float8 bytes, got %s" % (name, t.dtype))
-    if not t.is_cuda or not t.is_contiguous():
-        raise ValueError("%s must be a contiguous CUDA tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
     return t.view(torch.uint8)
 
 
 def _bf16(t, name):
     if t.dtype != torch.bfloat16:
         raise TypeError("%s must be bfloat16, got %s" % (name, t.dtype))
-    if not t.is_cuda or not t.is_contiguous():
-        raise ValueError("%s must be a contiguous CUDA tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
     return t
+
+
+def _on_gpu(ref, **tensors):
+    """Every tensor handed to the library must be a CUDA tensor on ref's device.  Checked after
+    the shape checks, so those run (and raise) without a GPU too."""
+    for name, t in (("x", ref),) + tuple(tensors.items()):
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("%s must be a CUDA tensor" % name)
+        if t.device != ref.device:
+            raise ValueError("%s is on %s, the activations on %s" % (name, t.device, ref.device))
 
 
 def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _out(out, shape, ref):
+    """The caller's output tensor (bf16, contiguous, exactly ``shape``), or a new one on ref's
+    device.  The kernels write every element of it, so a wrong shape would be an out-of-bounds
+    write: it is rejected here."""
+    if out is None:
+        return torch.empty(shape, dtype=torch.bfloat16, device=ref.device)
+    _bf16(out, "out")
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError("out has shape %s, the layer writes %s"
+                         % (tuple(out.shape), tuple(shape)))
+    return out
+
+
+def _bias(bias, shape):
+    """None, or a contiguous bf16 tensor of exactly ``shape`` ([N], or [B, N] when batched)."""
+    if bias is None:
+        return None
+    _bf16(bias, "bias")
+    if tuple(bias.shape) != tuple(shape):
+        raise ValueError("bias has shape %s, need %s" % (tuple(bias.shape), tuple(shape)))
+    return bias
+
+
+def _packed(packed, N, K, f, batch=1):
+    """A prepacked weight buffer of exactly ``batch`` weights of N x K in format f."""
+    packed = _u8(packed, "packed")
+    need = batch * prepacked_bytes(N, K, f)
+    if need <= 0 or packed.numel() != need:
+        raise ValueError("packed holds %d bytes; %d prepacked weight(s) of N = %d, K = %d in "
+                         "format %d hold %d" % (packed.numel(), batch, N, K, f, need))
+    return packed
+
+
+def _workspace_arg(workspace, need):
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor (new_workspace)")
+    if workspace.numel() < need:
+        raise ValueError("workspace holds %d bytes, the call needs %d"
+                         % (workspace.numel(), need))
+    return workspace
+
+
+def _ptr(t):
+    return 0 if t is None else t.data_ptr()
 
 
 def set_tile_config(fn=0, fm=0):
@@ -135,12 +193,20 @@ def new_workspace(nbytes, device="cuda"):
     return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _rows(x, name):
+    """x [..., K] -> (x as [M, K], leading shape, K)."""
+    if x.dim() < 1:
+        raise ValueError("%s must have a last dimension K" % name)
+    K = x.shape[-1]
+    return x.reshape(-1, K), x.shape[:-1], K
+
+
 def quantize_act(x):
     """bf16 x [..., K] -> (xq uint8 [M, K] E4M3, xs uint8 [M, K/32] E8M0), M = prod(lead)."""
     x = _bf16(x, "x")
-    K = x.shape[-1]
-    x2 = x.reshape(-1, K)
+    x2, _, K = _rows(x, "x")
     M = x2.shape[0]
+    _on_gpu(x)
     xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     xs = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
     _check(lib().mxfp8_quantize_act(x2.data_ptr(), M, K, K, xq.data_ptr(), xs.data_ptr(),
@@ -154,25 +220,27 @@ def rmsnorm_quantize_act(x, gamma, eps=1e-6, return_y=False):
     rows y [M, K] when return_y."""
     x = _bf16(x, "x")
     gamma = _bf16(gamma, "gamma")
-    K = x.shape[-1]
+    x2, _, K = _rows(x, "x")
     if tuple(gamma.shape) != (K,):
         raise ValueError("gamma must be [K]")
-    x2 = x.reshape(-1, K)
     M = x2.shape[0]
+    _on_gpu(x, gamma=gamma)
     xq = torch.empty((M, K), dtype=torch.uint8, device=x.device)
     xs = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
     y = torch.empty((M, K), dtype=torch.bfloat16, device=x.device) if return_y else None
     _check(lib().mxfp8_rmsnorm_quantize_act(x2.data_ptr(), M, K, K, gamma.data_ptr(), float(eps),
-                                            xq.data_ptr(), xs.data_ptr(),
-                                            0 if y is None else y.data_ptr(), _stream(x)))
+                                            xq.data_ptr(), xs.data_ptr(), _ptr(y), _stream(x)))
     return (xq, xs, y) if return_y else (xq, xs)
 
 
 def quantize_weight(w, fmt="e4m3"):
     """bf16 W [N, K] -> (wq [N, K] E4M3 or [N, 3K/4] packed FP6, ws [N, K/32] E8M0)."""
     w = _bf16(w, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
     N, K = w.shape
     f = _fmt(fmt)
+    _on_gpu(w)
     wq = torch.empty((N, K if f == 0 else K // 4 * 3), dtype=torch.uint8, device=w.device)
     ws = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
     _check(lib().mxfp8_quantize_weight(w.data_ptr(), N, K, K, f, wq.data_ptr(), ws.data_ptr(),
@@ -180,18 +248,30 @@ def quantize_weight(w, fmt="e4m3"):
     return wq, ws
 
 
+def _weight_scales(ws):
+    if ws.dtype not in (torch.uint8, torch.float8_e8m0fnu):
+        raise TypeError("ws must be uint8 / float8_e8m0fnu")
+    if ws.dim() != 2 or ws.stride(-1) != 1:
+        raise ValueError("ws must be 2-D with contiguous rows")
+    return ws.view(torch.uint8)
+
+
 def prepack_weight(wq, ws, fmt="e4m3", K=None):
     """Quantized weight (wq [N, row bytes], ws [>=N, >=K/32]) -> prepacked uint8 buffer."""
     f = _fmt(fmt)
     wq = _u8(wq, "wq")
-    if ws.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not ws.is_cuda:
-        raise TypeError("ws must be uint8 / float8_e8m0fnu on the GPU")
-    ws = ws.view(torch.uint8)
-    if ws.stride(-1) != 1:
-        raise ValueError("ws rows must be contiguous")
+    ws = _weight_scales(ws)
+    if wq.dim() != 2:
+        raise ValueError("wq must be [N, row bytes]")
     N = wq.shape[0]
     if K is None:
         K = wq.shape[1] if f == 0 else wq.shape[1] // 3 * 4
+    if wq.shape[1] < (K if f == 0 else K // 4 * 3):
+        raise ValueError("wq rows hold %d bytes, K = %d needs more" % (wq.shape[1], K))
+    if ws.shape[0] < N or ws.shape[1] < K // 32:
+        raise ValueError("ws %s is smaller than [N, K/32] = [%d, %d]"
+                         % (tuple(ws.shape), N, K // 32))
+    _on_gpu(wq, ws=ws)
     out = torch.empty(prepacked_bytes(N, K, f), dtype=torch.uint8, device=wq.device)
     _check(lib().mxfp8_prepack_weight(wq.data_ptr(), wq.stride(0), ws.data_ptr(), ws.stride(0),
                                       N, K, f, out.data_ptr(), _stream(wq)))
@@ -203,11 +283,11 @@ def prepack_weight_shuffled16(w16, ws, N, K):
     w16 = _u8(w16, "w16")
     if w16.numel() != N * K:
         raise ValueError("w16 must hold N * K = %d bytes" % (N * K))
-    if ws.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not ws.is_cuda:
-        raise TypeError("ws must be uint8 / float8_e8m0fnu on the GPU")
-    ws = ws.view(torch.uint8)
-    if ws.stride(-1) != 1:
-        raise ValueError("ws rows must be contiguous")
+    ws = _weight_scales(ws)
+    if ws.shape[0] < N or ws.shape[1] < K // 32:
+        raise ValueError("ws %s is smaller than [N, K/32] = [%d, %d]"
+                         % (tuple(ws.shape), N, K // 32))
+    _on_gpu(w16, ws=ws)
     out = torch.empty(prepacked_bytes(N, K, 0), dtype=torch.uint8, device=w16.device)
     _check(lib().mxfp8_prepack_weight_shuffled16(w16.data_ptr(), ws.data_ptr(), ws.stride(0), N, K,
                                                  out.data_ptr(), _stream(w16)))
@@ -216,7 +296,8 @@ def prepack_weight_shuffled16(w16, ws, N, K):
 
 def unpack_weight_shuffled16(packed, N, K):
     """Prepacked E4M3 weight -> (w16 uint8 [N * K] in the aiter (16, 16) order, ws [N, K/32])."""
-    packed = _u8(packed, "packed")
+    packed = _packed(packed, N, K, 0)
+    _on_gpu(packed)
     w16 = torch.empty(N * K, dtype=torch.uint8, device=packed.device)
     ws = torch.empty((N, K // 32), dtype=torch.uint8, device=packed.device)
     _check(lib().mxfp8_unpack_weight_shuffled16(packed.data_ptr(), N, K, w16.data_ptr(),
@@ -225,8 +306,10 @@ def unpack_weight_shuffled16(packed, N, K):
 
 
 def unpack_weight(packed, N, K, fmt="e4m3"):
+    """Prepacked weight -> (wq [N, K] E4M3 or [N, 3K/4] FP6, ws [N, K/32]): the exact inverse."""
     f = _fmt(fmt)
-    packed = _u8(packed, "packed")
+    packed = _packed(packed, N, K, f)
+    _on_gpu(packed)
     wq = torch.empty((N, K if f == 0 else K // 4 * 3), dtype=torch.uint8, device=packed.device)
     ws = torch.empty((N, K // 32), dtype=torch.uint8, device=packed.device)
     _check(lib().mxfp8_unpack_weight(packed.data_ptr(), N, K, f, wq.data_ptr(), ws.data_ptr(),
@@ -246,42 +329,76 @@ def _workspace(device, stream, nbytes):
     return t
 
 
+def _act_row_bytes(K, afmt):
+    return K if afmt == 0 else K // 4 * 3
+
+
+def _prequant_acts(xq, xs, K, a, lead=()):
+    """Checks pre-quantized activations: xq [*lead, M, row bytes of K in format a], xs
+    [*lead, M, K/32] (the aiter_flydsl page asserts exactly this scale shape)."""
+    xq = _u8(xq, "xq")
+    xs = _u8(xs, "xs")
+    nl = len(lead)
+    if xq.dim() != nl + 2:
+        raise ValueError("xq must be %d-D" % (nl + 2))
+    M = xq.shape[nl]
+    if tuple(xq.shape) != tuple(lead) + (M, _act_row_bytes(K, a)) or \
+            tuple(xs.shape) != tuple(lead) + (M, K // 32):
+        raise ValueError("activation codes %s / scales %s do not match K = %d in format %d: "
+                         "need %s and %s row-major"
+                         % (tuple(xq.shape), tuple(xs.shape), K, a,
+                            tuple(lead) + (M, _act_row_bytes(K, a)), tuple(lead) + (M, K // 32)))
+    return xq, xs, M
+
+
+def linear_fmt(x, packed, N, fmt, afmt, bias=None, out=None, workspace=None):
+    """linear() with the activations quantized to afmt (FP6 afmt needs an FP6 weight fmt)."""
+    x = _bf16(x, "x")
+    f, a = _fmt(fmt), _fmt(afmt)
+    x2, lead, K = _rows(x, "x")
+    M = x2.shape[0]
+    packed = _packed(packed, N, K, f)
+    bias = _bias(bias, (N,))
+    y = _out(out, (M, N) if out is None or out.dim() == 2 else tuple(lead) + (N,), x)
+    need = workspace_bytes_fmt(M, N, K, f, a)
+    if workspace is not None:
+        workspace = _workspace_arg(workspace, need)
+    _on_gpu(x, packed=packed, bias=bias, out=y, workspace=workspace)
+    st = _stream(x)
+    ws = workspace if workspace is not None else _workspace(x.device, st.value, need)
+    _check(lib().mxfp8_linear_fmt(x2.data_ptr(), M, K, packed.data_ptr(), N, f, a, _ptr(bias),
+                                  y.data_ptr(), ws.data_ptr(), ws.numel(), st))
+    return y.reshape(*lead, N)
+
+
 def linear(x, packed, N, fmt="e4m3", bias=None, out=None, workspace=None):
     """y = MX-quantized x [..., K] times the prepacked weight, (+ bias), bf16 [..., N].
 
-    ``workspace``: a uint8 device tensor of at least workspace_bytes(M, N, K, fmt) bytes from
-    new_workspace (zero-filled); by default one is kept per device and stream."""
-    x = _bf16(x, "x")
-    f = _fmt(fmt)
-    lead, K = x.shape[:-1], x.shape[-1]
-    x2 = x.reshape(-1, K)
-    M = x2.shape[0]
-    packed = _u8(packed, "packed")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    b = 0 if bias is None else _bf16(bias, "bias").data_ptr()
-    st = _stream(x)
-    need = workspace_bytes(M, N, K, f)
-    ws = workspace if workspace is not None else _workspace(x.device, st.value, need)
-    _check(lib().mxfp8_linear(x2.data_ptr(), M, K, packed.data_ptr(), N, f, b, y.data_ptr(),
-                              ws.data_ptr(), ws.numel(), st))
-    return y.reshape(*lead, N)
+    ``out``: optional bf16 tensor of shape [M, N] or [..., N].  ``workspace``: a uint8 device
+    tensor of at least workspace_bytes(M, N, K, fmt) bytes from new_workspace (zero-filled); by
+    default one is kept per device and stream."""
+    return linear_fmt(x, packed, N, fmt, "e4m3", bias, out, workspace)
+
+
+def linear_prequant_fmt(xq, xs, packed, N, K, fmt, afmt, bias=None, out=None):
+    """linear_prequant() with activations in format afmt: xq [M, K] E4M3 or [M, 3K/4] FP6."""
+    f, a = _fmt(fmt), _fmt(afmt)
+    xq, xs, M = _prequant_acts(xq, xs, K, a)
+    packed = _packed(packed, N, K, f)
+    bias = _bias(bias, (N,))
+    y = _out(out, (M, N), xq)
+    _on_gpu(xq, xs=xs, packed=packed, bias=bias, out=y)
+    _check(lib().mxfp8_linear_prequant_fmt(xq.data_ptr(), xs.data_ptr(), M, K, a,
+                                           packed.data_ptr(), N, f, _ptr(bias), y.data_ptr(),
+                                           _stream(xq)))
+    return y
 
 
 def linear_prequant(xq, xs, packed, N, fmt="e4m3", bias=None, out=None, lead_shape=None):
     """Same layer from pre-quantized activations: xq [M, K] E4M3, xs [M, K/32] row-major."""
-    xq = _u8(xq, "xq")
-    xs = _u8(xs, "xs")
-    f = _fmt(fmt)
-    M, K = xq.shape
-    if tuple(xs.shape) != (M, K // 32):
-        # the aiter_flydsl page asserts exactly this scale shape before its GEMM
-        raise ValueError("activation scale %s for %s: need (M, K/32) row-major"
-                         % (tuple(xs.shape), tuple(xq.shape)))
-    packed = _u8(packed, "packed")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
-    b = 0 if bias is None else _bf16(bias, "bias").data_ptr()
-    _check(lib().mxfp8_linear_prequant(xq.data_ptr(), xs.data_ptr(), M, K, packed.data_ptr(),
-                                       N, f, b, y.data_ptr(), _stream(xq)))
+    if xq.dim() != 2:
+        raise ValueError("xq must be [M, K]")
+    y = linear_prequant_fmt(xq, xs, packed, N, xq.shape[1], fmt, "e4m3", bias, out)
     return y if lead_shape is None else y.reshape(*lead_shape, N)
 
 
@@ -290,46 +407,36 @@ def linear_batched(x, packed, N, fmt="e4m3", bias=None, out=None, workspace=None
     prepack_weight outputs), bias bf16 [B, N] or None -> y bf16 [B, M, N]."""
     x = _bf16(x, "x")
     f = _fmt(fmt)
+    if x.dim() != 3:
+        raise ValueError("x must be [B, M, K]")
     B, M, K = x.shape
-    packed = _u8(packed, "packed")
-    if packed.numel() != B * prepacked_bytes(N, K, f):
-        raise ValueError("packed must hold B prepacked weights")
-    y = out if out is not None else torch.empty((B, M, N), dtype=torch.bfloat16, device=x.device)
-    b = 0
-    if bias is not None:
-        bias = _bf16(bias, "bias")
-        if tuple(bias.shape) != (B, N):
-            raise ValueError("bias must be [B, N]")
-        b = bias.data_ptr()
-    st = _stream(x)
+    packed = _packed(packed, N, K, f, batch=B)
+    bias = _bias(bias, (B, N))
+    y = _out(out, (B, M, N), x)
     need = workspace_bytes(B * M, N, K, f)
+    if workspace is not None:
+        workspace = _workspace_arg(workspace, need)
+    _on_gpu(x, packed=packed, bias=bias, out=y, workspace=workspace)
+    st = _stream(x)
     ws = workspace if workspace is not None else _workspace(x.device, st.value, need)
-    _check(lib().mxfp8_linear_batched(x.data_ptr(), B, M, K, packed.data_ptr(), N, f, b,
+    _check(lib().mxfp8_linear_batched(x.data_ptr(), B, M, K, packed.data_ptr(), N, f, _ptr(bias),
                                       y.data_ptr(), ws.data_ptr(), ws.numel(), st))
     return y
 
 
 def linear_prequant_batched(xq, xs, packed, N, fmt="e4m3", bias=None, out=None):
     """xq E4M3 [B, M, K], xs E8M0 [B, M, K/32] -> y bf16 [B, M, N] (weights as linear_batched)."""
-    xq = _u8(xq, "xq")
-    xs = _u8(xs, "xs")
     f = _fmt(fmt)
-    B, M, K = xq.shape
-    if tuple(xs.shape) != (B, M, K // 32):
-        raise ValueError("activation scale %s for %s: need (B, M, K/32)"
-                         % (tuple(xs.shape), tuple(xq.shape)))
-    packed = _u8(packed, "packed")
-    if packed.numel() != B * prepacked_bytes(N, K, f):
-        raise ValueError("packed must hold B prepacked weights")
-    y = out if out is not None else torch.empty((B, M, N), dtype=torch.bfloat16, device=xq.device)
-    b = 0
-    if bias is not None:
-        bias = _bf16(bias, "bias")
-        if tuple(bias.shape) != (B, N):
-            raise ValueError("bias must be [B, N]")
-        b = bias.data_ptr()
+    if xq.dim() != 3:
+        raise ValueError("xq must be [B, M, K]")
+    B, K = xq.shape[0], xq.shape[2]
+    xq, xs, M = _prequant_acts(xq, xs, K, 0, lead=(B,))
+    packed = _packed(packed, N, K, f, batch=B)
+    bias = _bias(bias, (B, N))
+    y = _out(out, (B, M, N), xq)
+    _on_gpu(xq, xs=xs, packed=packed, bias=bias, out=y)
     _check(lib().mxfp8_linear_prequant_batched(xq.data_ptr(), xs.data_ptr(), B, M, K,
-                                               packed.data_ptr(), N, f, b, y.data_ptr(),
+                                               packed.data_ptr(), N, f, _ptr(bias), y.data_ptr(),
                                                _stream(xq)))
     return y
 
@@ -337,10 +444,6 @@ def linear_prequant_batched(xq, xs, packed, N, fmt="e4m3", bias=None, out=None):
 # ---------------------------------------------------------------- MXFP6 activations
 # (mxfp6 page, MxFp6LinearLayerConfig.activation_quant_key): activations quantized to E2M3 or
 # E3M2 (packed four codes per three bytes), with FP6 weights; afmt "e4m3" gives the layer above.
-
-def _act_row_bytes(K, afmt):
-    return K if afmt == 0 else K // 4 * 3
-
 
 def workspace_bytes_fmt(M, N, K, fmt, afmt):
     return int(lib().mxfp8_workspace_bytes_fmt(M, N, K, _fmt(fmt), _fmt(afmt)))
@@ -350,50 +453,14 @@ def quantize_act_fmt(x, afmt):
     """bf16 x [..., K] -> (xq uint8 [M, K] E4M3 or [M, 3K/4] packed FP6, xs uint8 [M, K/32])."""
     x = _bf16(x, "x")
     a = _fmt(afmt)
-    K = x.shape[-1]
-    x2 = x.reshape(-1, K)
+    x2, _, K = _rows(x, "x")
     M = x2.shape[0]
+    _on_gpu(x)
     xq = torch.empty((M, _act_row_bytes(K, a)), dtype=torch.uint8, device=x.device)
     xs = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
     _check(lib().mxfp8_quantize_act_fmt(x2.data_ptr(), M, K, K, a, xq.data_ptr(), xs.data_ptr(),
                                         _stream(x)))
     return xq, xs
-
-
-def linear_fmt(x, packed, N, fmt, afmt, bias=None, out=None, workspace=None):
-    """linear() with the activations quantized to afmt (FP6 afmt needs an FP6 weight fmt)."""
-    x = _bf16(x, "x")
-    f, a = _fmt(fmt), _fmt(afmt)
-    lead, K = x.shape[:-1], x.shape[-1]
-    x2 = x.reshape(-1, K)
-    M = x2.shape[0]
-    packed = _u8(packed, "packed")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
-    b = 0 if bias is None else _bf16(bias, "bias").data_ptr()
-    st = _stream(x)
-    need = workspace_bytes_fmt(M, N, K, f, a)
-    ws = workspace if workspace is not None else _workspace(x.device, st.value, need)
-    _check(lib().mxfp8_linear_fmt(x2.data_ptr(), M, K, packed.data_ptr(), N, f, a, b,
-                                  y.data_ptr(), ws.data_ptr(), ws.numel(), st))
-    return y.reshape(*lead, N)
-
-
-def linear_prequant_fmt(xq, xs, packed, N, K, fmt, afmt, bias=None, out=None):
-    """linear_prequant() with activations in format afmt: xq [M, K] E4M3 or [M, 3K/4] FP6."""
-    xq = _u8(xq, "xq")
-    xs = _u8(xs, "xs")
-    f, a = _fmt(fmt), _fmt(afmt)
-    M = xq.shape[0]
-    if tuple(xq.shape) != (M, _act_row_bytes(K, a)) or tuple(xs.shape) != (M, K // 32):
-        raise ValueError("xq %s / xs %s do not match K = %d in format %d"
-                         % (tuple(xq.shape), tuple(xs.shape), K, a))
-    packed = _u8(packed, "packed")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
-    b = 0 if bias is None else _bf16(bias, "bias").data_ptr()
-    _check(lib().mxfp8_linear_prequant_fmt(xq.data_ptr(), xs.data_ptr(), M, K, a,
-                                           packed.data_ptr(), N, f, b, y.data_ptr(),
-                                           _stream(xq)))
-    return y
 
 
 class MxLinear:

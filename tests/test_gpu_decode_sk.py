@@ -61,8 +61,6 @@ def _layer(w_bits, fmt, b_bits):
 @pytest.mark.parametrize("M,N,K", SHAPES)
 @pytest.mark.parametrize("fmt", [0, 2, 3])
 def test_decode_split_k_matches_oracle(M, N, K, fmt):
-    if fmt != 0 and (M, N, K) in [(32, 16384, 1024), (20, 1024, 8192)]:
-        pytest.skip("the FP6 formats are covered on the other shapes")
     x, w, b = _inputs(M, N, K, M * 7 + N + K + fmt)
     use_bias = (M + fmt) % 2 == 0
     layer, wq, ws = _layer(w, fmt, b if use_bias else None)

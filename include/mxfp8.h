@@ -164,6 +164,22 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, i
                  int fmt, const void* bias, void* y, void* workspace, int64_t ws_bytes,
                  void* stream);
 
+/* mxfp8_linear for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  Same arguments as mxfp8_linear minus
+ * the workspace, same kernels and results.  The library's own device array of
+ * MXFP8_NOALLOC_SCRATCH_BYTES (held on each GPU it runs on until the process ends) serves as
+ * the workspace; the call itself allocates and frees nothing.
+ *   - A call whose mxfp8_workspace_bytes(M, N, K, fmt) exceeds the array returns MX_EWORKSPACE
+ *     (before any HIP call); use mxfp8_linear with a workspace for such shapes.
+ *   - The first call on a device looks up the array's device address and enqueues one small
+ *     kernel that clears its counters (on `stream`; under capture it becomes part of the
+ *     graph, which is harmless since every call leaves them zero).
+ *   - All calls on one GPU share the array: calls that overlap on one GPU (several streams or
+ *     threads) race and must be serialized by the caller. */
+#define MXFP8_NOALLOC_SCRATCH_BYTES ((int64_t)64 << 20)
+int mxfp8_linear_noalloc(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N,
+                         int fmt, const void* bias, void* y, void* stream);
+
 /* The same layer from pre-quantized activations (aiter_flydsl page, apply_weights with a
  * QuantizedActivation; the scales must be row-major [M, K/32] E8M0 exactly, as its assert
  * requires):

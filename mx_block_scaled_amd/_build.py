@@ -12,7 +12,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxfp8.so")
-SOURCES = ["mx_api.cpp", "mx_quant.hip", "mx_prepack.hip", "mx_gemm.hip", "mx_small_m.hip"]
+SOURCES = ["mx_api.cpp", "mx_quant.hip", "mx_prepack.hip", "mx_gemm.hip", "mx_small_m.hip",
+           "mx_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

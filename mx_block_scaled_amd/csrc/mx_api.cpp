@@ -125,7 +125,72 @@ int check_fmt_pair(int fmt, int afmt) {
   return MX_OK;
 }
 
+int check_linear_common(int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
+                               const void* y) {
+  if (!valid_fmt(fmt)) return fail(MX_EINVAL, "unknown format %d", fmt);
+  int rc = check_mk(M, K);
+  if (rc) return rc;
+  if ((rc = check_nk(N, K))) return rc;
+  if (M > 0 && (!packed || !y)) return fail(MX_EINVAL, "null pointer (packed or y)");
+  if (M > 0 && (!aligned16(packed) || !aligned16(y)))
+    return fail(MX_EALIGN, "packed, y must be 16-byte aligned");
+  if (M * N >= ((int64_t)1 << 31)) return fail(MX_ESHAPE, "M x N exceeds the supported size");
+  return MX_OK;
+}
+
 }  // namespace
+
+namespace mx {
+
+int api_fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int api_ok() { return ok(); }
+
+int api_check_arch() { return check_arch(); }
+
+int linear_check(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
+                 const void* y, int64_t* need) {
+  *need = 0;
+  int rc = check_linear_common(M, K, packed, N, fmt, y);
+  if (rc) return rc;
+  if (M == 0) return MX_OK;
+  if (!x_bf16) return fail(MX_EINVAL, "null pointer (x)");
+  if (!aligned16(x_bf16)) return fail(MX_EALIGN, "x must be 16-byte aligned");
+  *need = linear_ws_bytes(M, N, K);
+  return MX_OK;
+}
+
+int linear_launch(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
+                  const void* bias, void* y, void* workspace, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  if (!mx::batch_invariant() && sk_shape(M, N, K))   // decode: K split across workgroups
+    return hip_status(mx::launch_linear_decode_sk((const uint16_t*)x_bf16, M, K,
+                                                  (const uint8_t*)packed, N, fmt,
+                                                  (const uint16_t*)bias, (uint16_t*)y, workspace, s),
+                      "linear (decode, split K) launch");
+  if (!mx::batch_invariant() && mx::small_m_fused(M, K))   // decode: quantizer fused in
+    return hip_status(mx::launch_linear_small_m(x_bf16, nullptr, false, M, K,
+                                                (const uint8_t*)packed, N, fmt,
+                                                (const uint16_t*)bias, (uint16_t*)y, s),
+                      "linear (small M) launch");
+  uint8_t* xq = (uint8_t*)workspace + mx::kWorkspacePrefix;
+  uint8_t* xs = xq + ((M * K + 255) / 256) * 256;
+  float* part = !sk_shape(M, N, K) && mx::gemm_split_bytes(M, N, K)
+                    ? (float*)((uint8_t*)workspace + split_offset(M, K)) : nullptr;
+  hipError_t e = mx::launch_quantize_act((const uint16_t*)x_bf16, M, K, K, xq, xs, s);
+  if (e != hipSuccess) return hip_status(e, "quantize_act launch");
+  return hip_status(mx::launch_gemm(xq, xs, M, K, (const uint8_t*)packed, N, fmt,
+                                    (const uint16_t*)bias, (uint16_t*)y, s, 1, {}, 0, part),
+                    "gemm launch");
+}
+
+}  // namespace mx
 
 extern "C" {
 
@@ -243,51 +308,18 @@ int64_t mxfp8_workspace_bytes(int64_t M, int64_t N, int64_t K, int fmt) {
   return linear_ws_bytes(M, N, K);
 }
 
-static int check_linear_common(int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
-                               const void* y) {
-  if (!valid_fmt(fmt)) return fail(MX_EINVAL, "unknown format %d", fmt);
-  int rc = check_mk(M, K);
-  if (rc) return rc;
-  if ((rc = check_nk(N, K))) return rc;
-  if (M > 0 && (!packed || !y)) return fail(MX_EINVAL, "null pointer (packed or y)");
-  if (M > 0 && (!aligned16(packed) || !aligned16(y)))
-    return fail(MX_EALIGN, "packed, y must be 16-byte aligned");
-  if (M * N >= ((int64_t)1 << 31)) return fail(MX_ESHAPE, "M x N exceeds the supported size");
-  return MX_OK;
-}
 
 int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
                  const void* bias, void* y, void* workspace, int64_t ws_bytes, void* stream) {
-  int rc = check_linear_common(M, K, packed, N, fmt, y);
+  int64_t need = 0;
+  int rc = mx::linear_check(x_bf16, M, K, packed, N, fmt, y, &need);
   if (rc) return rc;
   if (M == 0) return ok();
-  if (!x_bf16) return fail(MX_EINVAL, "null pointer (x)");
-  if (!aligned16(x_bf16)) return fail(MX_EALIGN, "x must be 16-byte aligned");
-  const int64_t need = linear_ws_bytes(M, N, K);
   if (!workspace || ws_bytes < need)
     return fail(MX_EWORKSPACE, "workspace of %lld bytes given, %lld needed", (long long)ws_bytes, (long long)need);
   if (!aligned16(workspace)) return fail(MX_EALIGN, "workspace must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
-  hipStream_t s = (hipStream_t)stream;
-  if (!mx::batch_invariant() && sk_shape(M, N, K))   // decode: K split across workgroups
-    return hip_status(mx::launch_linear_decode_sk((const uint16_t*)x_bf16, M, K,
-                                                  (const uint8_t*)packed, N, fmt,
-                                                  (const uint16_t*)bias, (uint16_t*)y, workspace, s),
-                      "linear (decode, split K) launch");
-  if (!mx::batch_invariant() && mx::small_m_fused(M, K))   // decode: quantizer fused in
-    return hip_status(mx::launch_linear_small_m(x_bf16, nullptr, false, M, K,
-                                                (const uint8_t*)packed, N, fmt,
-                                                (const uint16_t*)bias, (uint16_t*)y, s),
-                      "linear (small M) launch");
-  uint8_t* xq = (uint8_t*)workspace + mx::kWorkspacePrefix;
-  uint8_t* xs = xq + ((M * K + 255) / 256) * 256;
-  float* part = !sk_shape(M, N, K) && mx::gemm_split_bytes(M, N, K)
-                    ? (float*)((uint8_t*)workspace + split_offset(M, K)) : nullptr;
-  hipError_t e = mx::launch_quantize_act((const uint16_t*)x_bf16, M, K, K, xq, xs, s);
-  if (e != hipSuccess) return hip_status(e, "quantize_act launch");
-  return hip_status(mx::launch_gemm(xq, xs, M, K, (const uint8_t*)packed, N, fmt,
-                                    (const uint16_t*)bias, (uint16_t*)y, s, 1, {}, 0, part),
-                    "gemm launch");
+  return mx::linear_launch(x_bf16, M, K, packed, N, fmt, bias, y, workspace, stream);
 }
 
 int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K, const void* packed,

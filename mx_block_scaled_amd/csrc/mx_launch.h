@@ -87,4 +87,15 @@ hipError_t launch_linear_small_m(const void* x, const uint8_t* xs, bool quantize
                                  const uint16_t* bias, uint16_t* y, hipStream_t s,
                                  int batch = 1, BatchStrides bs = {});
 
+// The C-ABI front's own pieces, shared with the allocation-free entry point: the thread-local
+// error message (api_fail sets it and returns code), the per-device gfx950 check, and
+// mxfp8_linear split into its argument checks (need = workspace bytes) and its launches.
+int api_fail(int code, const char* fmt, ...);
+int api_ok();
+int api_check_arch();
+int linear_check(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
+                 const void* y, int64_t* need);
+int linear_launch(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
+                  const void* bias, void* y, void* workspace, void* stream);
+
 }  // namespace mx

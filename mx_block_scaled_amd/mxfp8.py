@@ -21,7 +21,8 @@ __all__ = [
     "linear", "linear_prequant", "MxLinear", "set_tile_config", "set_batch_invariant",
     "prepack_weight_shuffled16", "unpack_weight_shuffled16", "linear_batched",
     "linear_prequant_batched", "quantize_act_fmt", "workspace_bytes_fmt", "linear_fmt",
-    "linear_prequant_fmt", "rmsnorm_quantize_act", "new_workspace",
+    "linear_prequant_fmt", "rmsnorm_quantize_act", "new_workspace", "linear_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
 ]
 
 FMT = {"e4m3": 0, "e2m3": 2, "e3m2": 3}
@@ -69,6 +70,7 @@ def lib():
             "mxfp8_linear_fmt": (I, [P, I64, I64, P, I64, I, I, P, P, P, I64, P]),
             "mxfp8_linear_prequant_fmt": (I, [P, P, I64, I64, I, P, I64, I, P, P, P]),
             "mxfp8_rmsnorm_quantize_act": (I, [P, I64, I64, I64, P, ctypes.c_float, P, P, P, P]),
+            "mxfp8_linear_noalloc": (I, [P, I64, I64, P, I64, I, P, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -378,6 +380,27 @@ def linear(x, packed, N, fmt="e4m3", bias=None, out=None, workspace=None):
     tensor of at least workspace_bytes(M, N, K, fmt) bytes from new_workspace (zero-filled); by
     default one is kept per device and stream."""
     return linear_fmt(x, packed, N, fmt, "e4m3", bias, out, workspace)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def linear_noalloc(x, packed, N, fmt="e4m3", bias=None, out=None):
+    """linear() without a workspace: the library's static per-GPU scratch array serves as one
+    (mxfp8_linear_noalloc), so the call allocates nothing on the library side.  Pass ``out`` to
+    allocate nothing at all.  Shapes whose workspace exceeds NOALLOC_SCRATCH_BYTES are refused;
+    calls that overlap on one GPU race on the shared array."""
+    x = _bf16(x, "x")
+    f = _fmt(fmt)
+    x2, lead, K = _rows(x, "x")
+    M = x2.shape[0]
+    packed = _packed(packed, N, K, f)
+    bias = _bias(bias, (N,))
+    y = _out(out, (M, N) if out is None or out.dim() == 2 else tuple(lead) + (N,), x)
+    _on_gpu(x, packed=packed, bias=bias, out=y)
+    _check(lib().mxfp8_linear_noalloc(x2.data_ptr(), M, K, packed.data_ptr(), N, f, _ptr(bias),
+                                      y.data_ptr(), _stream(x)))
+    return y.reshape(*lead, N)
 
 
 def linear_prequant_fmt(xq, xs, packed, N, K, fmt, afmt, bias=None, out=None):

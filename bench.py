@@ -9,36 +9,50 @@ TFLOP/s, with activation quantization inside the timed step.  Inputs are residen
 the clock starts; R copies of the inputs/weights/outputs are rotated so the working set exceeds
 the 256 MiB Infinity Cache.
 
+Order of a run: the chip is first brought to its steady clock (steps for --settle-ms of GPU
+time); the GEMM and quantizer are timed alone (roofline); then W warmup steps and exactly K
+timed steps (wall clock between two synchronizations, HIP events alongside), which give
+`value`; then the step protocol: 5 loops of >= 100 steps timed with HIP events (median, min).
+
 Also measured and printed in the same JSON line:
-  roofline      the GEMM kernel alone (pre-quantized entry), timed with HIP events on the
-                stream it runs on: achieved TFLOP/s against the 5.0 PFLOP/s dense FP8 peak;
-                traffic from the committed rocprofv3 counter summary while the kernel source
-                still matches it, else null;
+  roofline      the GEMM kernel alone (pre-quantized entry), 5 loops of >= 100 launches timed
+                with HIP events on the stream it runs on (median): achieved TFLOP/s against
+                the 5.0 PFLOP/s dense FP8 peak, and against the attainable peak that the MFMA
+                loop of libmxpeaks measures on the same chip; traffic from the committed
+                rocprofv3 counter summary while the kernel source still matches it, else null;
+  clock         the shader clock the chip runs at under back-to-back GEMMs and steps: a one-wave
+                probe on a second stream counts shader-clock cycles against the 100 MHz
+                counter while the calls run;
+  attainable    the MFMA-loop peaks (FP8 x FP8, FP8 x FP6, FP6 x FP6) and the HBM stream-read
+                rate of 1 GiB, measured in this run;
   decode        the decode workload (x [M, 4096], M in {1, 8, 32}, weight [4096, 4096], bias),
                 one fused call each, replayed from a HIP graph over 32 rotated weight copies:
-                time per call, algorithmic bytes / time against 8 TB/s; the same for M = 64
-                and 128 (prefill chunks too small to fill the GPU with output tiles, where K
-                is split across workgroups: the split-K decode kernel at 64 rows, the tiled
-                GEMM at 128), and every M again in batch-invariant mode;
+                time per call, algorithmic bytes / time against 8 TB/s and against a plain
+                read of the same weight bytes replayed the same way (the stream floor); the
+                same for M = 64 and 128 (prefill chunks), and every M in batch-invariant mode;
   other_workloads  outlier activations on the pre-quantized entry (2048 x 6144 x 4096, GEMM
                 only), MXFP6 weights (E2M3 and E3M2, 512 x 8192 x 8192, activation quantization
                 included) with MXFP8 activations and with MXFP6 activations of the same format
                 (both MFMA operands FP6), each over enough rotated sets to exceed the Infinity
-                Cache; the fused RMS norm + MXFP8 quantizer (producer of pre-quantized
-                activations) on the prefill activations against a torch RMS norm followed by
-                the standalone quantizer; and the
-                latency of one tiny call (16 x 256 x 512) from a HIP graph;
-  cpu_baseline  the CPU oracle on a bounded sample of the prefill workload (host cores),
-                run in a separate process (oracle/cpu_bench.py).
+                Cache; the fused RMS norm + MXFP8 quantizer on the prefill activations against a
+                torch RMS norm followed by the standalone quantizer; the latency of one tiny
+                call (16 x 256 x 512) from a HIP graph; the batched layer;
+  cpu_baseline  the CPU oracle on bounded samples of the prefill workload (host cores), run in
+                separate processes (oracle/cpu_bench.py): the whole layer (value), and the
+                quantizer (GB/s) and fp64 GEMM (GFLOP/s) apart, on all cores and on one thread.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --only peaks            (MFMA-loop peaks, stream reads 16 MiB .. 1 GiB)
        python bench.py --only gemm --steps K   (the GEMM alone, for rocprofv3 --pmc passes)
+       python bench.py --only decode --steps K (the decode calls, for rocprofv3 --pmc passes)
        python bench.py --only copy             (1 GiB device copy x 3: counter calibration)
 """
 import argparse
+import ctypes
 import hashlib
 import json
 import os
+import statistics
 import subprocess
 import sys
 import time
@@ -71,6 +85,139 @@ def _traffic(kernel_key, n_launch_units=1):
     return t.get("bytes_per_launch")
 
 
+def _peaks_lib():
+    path = os.path.join(ROOT, "mx_block_scaled_amd", "libmxpeaks.so")
+    if not os.path.exists(path):
+        raise RuntimeError("libmxpeaks.so is not built; run __graft_entry__.build()")
+    L = ctypes.CDLL(path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.mxpk_mfma_loop.restype, L.mxpk_mfma_loop.argtypes = I, [I, I, I, I, P, P, P]
+    L.mxpk_mfma_chains.restype, L.mxpk_mfma_chains.argtypes = I, []
+    L.mxpk_stream_read.restype, L.mxpk_stream_read.argtypes = I, [P, I64, I, I, P, P]
+    L.mxpk_clock_probe.restype, L.mxpk_clock_probe.argtypes = I, [I64, P, P]
+    return L
+
+
+def clock_under(L, fn, calls, probe_ms):
+    """Shader clock (MHz) while fn(i) runs ``calls`` times back to back: a one-wave probe on a
+    second stream waits ``probe_ms`` inside that stretch and counts the shader-clock cycles
+    (s_memtime) against the 100 MHz counter (s_memrealtime)."""
+    import torch
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    side = torch.cuda.Stream()
+    head = max(1, calls // 5)
+    for i in range(head):
+        fn(i)
+    assert L.mxpk_clock_probe(int(probe_ms * 1e5), out.data_ptr(), side.cuda_stream) == 0
+    for i in range(head, calls):
+        fn(i)
+    torch.cuda.synchronize()
+    cyc, ticks = out.cpu().tolist()
+    return round(cyc / (ticks / 100.0), 1) if ticks > 0 else None
+
+
+def event_loops(fn, loops=5, iters=100, warm=10):
+    """Times ``iters`` back-to-back calls of fn(i) with HIP events on the current stream,
+    ``loops`` times: (median, min) microseconds per call."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warm):
+        fn(i)
+    per = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(loops):
+        e0.record(stream)
+        for i in range(iters):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        per.append(e0.elapsed_time(e1) * 1e3 / iters)
+    return statistics.median(per), min(per)
+
+
+def mfma_peak(L, afmt, bfmt, blocks, iters=20000):
+    """(TFLOP/s, shader clock in MHz) of the MFMA loop: blocks x 4 waves x iters x chains
+    scaled 16x16x128 MFMAs; the clock from block 0's s_memtime / s_memrealtime stamps."""
+    import torch
+    out = torch.zeros(4, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    flop = blocks * 4.0 * iters * L.mxpk_mfma_chains() * 2 * 16 * 16 * 128
+
+    def run(_):
+        assert L.mxpk_mfma_loop(afmt, bfmt, blocks, iters, out.data_ptr(), clk.data_ptr(), st) == 0
+
+    med, _ = event_loops(run, loops=3, iters=1, warm=1)
+    c = clk.cpu().tolist()
+    mhz = c[0] / (c[1] / 100.0) if c[1] > 0 else None
+    return flop / (med * 1e-6) / 1e12, mhz
+
+
+def stream_read_us(L, nbytes, sets=None, reps=20, configs=None):
+    """Best microseconds per plain read of nbytes over the (unroll, blocks) configs, replayed
+    from a HIP graph over enough distinct buffers (>= 2 x the Infinity Cache in all) that the
+    reads come from HBM: the same method the decode calls are timed with."""
+    import torch
+    nbytes = (nbytes + 15) // 16 * 16
+    n16 = nbytes // 16
+    n = sets or max(1, -(-2 * MALL_BYTES // nbytes))
+    if configs is None:
+        configs = [(u, max(1, min(16384, -(-n16 // (256 * u * k))))) for u in (4, 8, 16)
+                   for k in (1, 2, 4)]
+    bufs = [torch.full((nbytes,), j + 1, dtype=torch.uint8, device="cuda") for j in range(n)]
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    per_graph = max(n, 8)
+    best = None
+    for unroll, blocks in configs:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            for j in range(per_graph):
+                assert L.mxpk_stream_read(bufs[j % n].data_ptr(), nbytes, blocks, unroll,
+                                          out.data_ptr(), s.cuda_stream) == 0
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for j in range(per_graph):
+                L.mxpk_stream_read(bufs[j % n].data_ptr(), nbytes, blocks, unroll,
+                                   out.data_ptr(), s.cuda_stream)
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / (reps * per_graph)
+        del g
+        if best is None or us < best[0]:
+            best = (us, unroll, blocks)
+    del bufs
+    torch.cuda.empty_cache()
+    return best
+
+
+def measure_peaks(full=False):
+    """Attainable peaks of the running chip: MFMA loops (4 and 8 waves per SIMD, the better
+    one) and plain HBM reads (the best launch shape)."""
+    L = _peaks_lib()
+    res = {"mfma_TFLOPs": {}, "mfma_clock_MHz": {}}
+    for name, af, bf in (("fp8xfp8", 0, 0), ("fp8xfp6", 0, 2), ("fp6xfp6", 2, 2)):
+        best = max((mfma_peak(L, af, bf, blocks) for blocks in (1024, 2048)),
+                   key=lambda r: r[0])
+        res["mfma_TFLOPs"][name] = round(best[0], 1)
+        res["mfma_clock_MHz"][name] = round(best[1], 1) if best[1] else None
+    sizes = [16 << 20, 64 << 20, 256 << 20, 1 << 30] if full else [1 << 30]
+    res["stream_read"] = {}
+    for b in sizes:
+        us, unroll, blocks = stream_read_us(L, b)
+        res["stream_read"]["%dMiB" % (b >> 20)] = {"us": round(us, 2),
+                                                    "GB/s": round(b / us / 1e3, 1),
+                                                    "unroll": unroll, "blocks": blocks}
+    res["hbm_GBs"] = res["stream_read"]["1024MiB"]["GB/s"]
+    return res, L
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,8 +227,13 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the outlier, MXFP6 and tiny workloads")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["all", "gemm", "copy", "decode"], default="all",
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="CPU time of the whole-layer oracle sample (the split parts take "
+                         "a quarter of it each)")
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="GPU time of untimed steps run first, so the chip reaches its steady "
+                         "clock before anything is timed")
+    ap.add_argument("--only", choices=["all", "gemm", "copy", "decode", "peaks"], default="all",
                     help="counter runs: 'gemm' launches only the prefill GEMM (pre-quantized "
                          "entry) --steps times; 'decode' runs the decode calls (M = 1, 8, 32) "
                          "--steps times each over the rotated weights, without a graph; 'copy' "
@@ -99,6 +251,11 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.only == "peaks":
+        res, _ = measure_peaks(full=True)
+        print(json.dumps(res))
+        return
 
     if args.only == "copy":
         src = torch.full((1 << 30,), 3, dtype=torch.uint8, device=dev)
@@ -158,60 +315,101 @@ def main():
     ps_ = [packed0] + [packed0.clone() for _ in range(R - 1)]
     ys_ = [torch.empty((M, N), dtype=torch.bfloat16, device=dev) for _ in range(R)]
     wsb = torch.zeros(mxfp8.workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    flop = 2.0 * M * N * K
 
     def step(i):
         j = i % R
         mxfp8.linear(xs_[j], ps_[j], N, "e4m3", out=ys_[j], workspace=wsb)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    flop = 2.0 * M * N * K
-    value = flop / (ms_per_step * 1e-3) / 1e12
+    # bring the chip to its steady clock: untimed steps for --settle-ms of GPU time
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for i in range(20):
+            step(n_settle + i)
+        n_settle += 20
+        torch.cuda.synchronize()
 
     # ------------------------------------------------------------ GEMM kernel alone (roofline)
     xq_, xsc_ = [], []
     for j in range(R):
-        q, s = mxfp8.quantize_act(xs_[j])
+        q, sc = mxfp8.quantize_act(xs_[j])
         xq_.append(q)
-        xsc_.append(s)
-    stream = torch.cuda.current_stream(dev)
-    n_gemm = max(args.steps, 50)
-    for j in range(5):
-        mxfp8.linear_prequant(xq_[j % R], xsc_[j % R], ps_[j % R], N, "e4m3", out=ys_[j % R])
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(n_gemm):
-        j = i % R
-        mxfp8.linear_prequant(xq_[j], xsc_[j], ps_[j], N, "e4m3", out=ys_[j])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    gemm_us = e0.elapsed_time(e1) * 1e3 / n_gemm
+        xsc_.append(sc)
+    gemm_us, gemm_us_min = event_loops(
+        lambda i: mxfp8.linear_prequant(xq_[i % R], xsc_[i % R], ps_[i % R], N, "e4m3",
+                                        out=ys_[i % R]))
     achieved = flop / (gemm_us * 1e-6) / 1e12
-    # quantizer alone
+    quant_us, quant_us_min = event_loops(lambda i: mxfp8.quantize_act(xs_[i % R]))
+    del xq_, xsc_
+    quant_bytes = M * K * 2 + M * K + M * K // 32
+
+    # ------------------------------------------------------------ the timed steps (value)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     e0.record(stream)
-    for i in range(n_gemm):
-        j = i % R
-        mxfp8.quantize_act(xs_[j])
+    for i in range(args.steps):
+        step(i)
     e1.record(stream)
     torch.cuda.synchronize()
-    quant_us = e0.elapsed_time(e1) * 1e3 / n_gemm
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step_events = e0.elapsed_time(e1) / args.steps
+    value = flop / (ms_per_step * 1e-3) / 1e12
+
+    # step protocol: 5 loops of >= 100 steps, HIP events
+    step_us, step_us_min = event_loops(step, loops=5, iters=max(100, args.steps))
+
+    # ------------------------------------------------------------ attainable peaks
+    attainable = None
+    try:
+        attainable, peaks_lib = measure_peaks(full=False)
+    except Exception as e:          # report, never fail the bench line for it
+        attainable, peaks_lib = {"error": str(e)[:200]}, None
+    att_fp8 = (attainable.get("mfma_TFLOPs") or {}).get("fp8xfp8")
+    att_hbm = attainable.get("hbm_GBs")
+    # achieved shader clock under the GEMM and under the whole step (a one-wave probe on a
+    # second stream, in a separate stretch of calls after the timed loops)
+    clock = None
+    if peaks_lib is not None:
+        xq1, xs1 = mxfp8.quantize_act(xs_[0])
+        clock = {
+            "gemm_MHz": clock_under(peaks_lib, lambda i: mxfp8.linear_prequant(
+                xq1, xs1, ps_[i % R], N, "e4m3", out=ys_[i % R]), 500, 60),
+            "step_MHz": clock_under(peaks_lib, step, 500, 60),
+            "mfma_loop_MHz": (attainable.get("mfma_clock_MHz") or {}).get("fp8xfp8"),
+            "source": "s_memtime / s_memrealtime of a one-wave probe on a second stream, "
+                      "60 ms inside 500 back-to-back calls"}
+        del xq1, xs1
+
     roofline = {
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
         "traffic": _traffic("gemm_prefill"),
-        "kernel": "k_gemm (pre-quantized entry), %dx%dx%d" % (M, N, K),
-        "kernel_us": round(gemm_us, 2),
+        "kernel": "k_gemm_tile (pre-quantized entry), %dx%dx%d" % (M, N, K),
+        "kernel_us": round(gemm_us, 2), "kernel_us_min": round(gemm_us_min, 2),
+        "timing": "HIP events on the launch stream, median of 5 loops of 100 launches",
         "algorithmic_flop_per_launch": flop,
+        "attainable_peak": att_fp8,
+        "frac_attainable": round(achieved / att_fp8, 4) if att_fp8 else None,
     }
-    quant_bytes = M * K * 2 + M * K + M * K // 32
-    del xq_, xsc_
+    quant_gbs = quant_bytes / (quant_us * 1e-6) / 1e9
+    quantizer = {"us": round(quant_us, 2), "us_min": round(quant_us_min, 2),
+                 "GB/s": round(quant_gbs, 1), "hbm_frac": round(quant_gbs / PEAK_HBM_GBS, 4),
+                 "hbm_frac_attainable": round(quant_gbs / att_hbm, 4) if att_hbm else None}
+    step_protocol = {
+        "us_median": round(step_us, 2), "us_min": round(step_us_min, 2),
+        "TFLOP/s_median": round(flop / step_us / 1e6, 1),
+        "TFLOP/s_best": round(flop / step_us_min / 1e6, 1),
+        "loops": 5, "steps_per_loop": max(100, args.steps),
+        "gemm_plus_quantizer_us": round(gemm_us + quant_us, 2),
+        "TFLOP/s_from_gemm_plus_quantizer": round(flop / (gemm_us + quant_us) / 1e6, 1),
+        "timed_steps_us_events": round(ms_per_step_events * 1e3, 2),
+        "settle_steps": n_settle}
 
     # ------------------------------------------------------------ decode (HBM-bound)
     decode = None
@@ -226,6 +424,14 @@ def main():
         pk = mxfp8.prepack_weight(wq, ws, "e4m3")
         bias = torch.from_numpy(dd["bias"].view(np.int16)).view(torch.bfloat16).to(dev)
         RD = 32
+        # the stream floor: a plain read of the same weight bytes, 32 rotated copies, replayed
+        # from a HIP graph exactly as the decode calls are
+        floor_us = None
+        if peaks_lib is not None:
+            floor_us, fu, fb = stream_read_us(peaks_lib, pk.numel(), sets=RD)
+            decode["stream_floor"] = {"bytes": pk.numel(), "us_per_read": round(floor_us, 3),
+                                      "GB/s": round(pk.numel() / floor_us / 1e3, 1),
+                                      "unroll": fu, "blocks": fb}
         pks = [pk] + [pk.clone() for _ in range(RD - 1)]
         for Md in (1, 8, 32, 64, 128):
             xd = torch.from_numpy(dd["x"][:Md].view(np.int16)).view(torch.bfloat16).to(dev)
@@ -255,7 +461,9 @@ def main():
             decode["M%d" % Md] = {
                 "us_per_call": round(us, 3), "TFLOP/s": round(2.0 * Md * Nd * Kd / (us * 1e-6) / 1e12, 3),
                 "algorithmic_bytes": bytes_alg, "GB/s": round(gbs, 1),
-                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                "hbm_frac_attainable": round(gbs / att_hbm, 4) if att_hbm else None,
+                "x_stream_floor": round(us / floor_us, 3) if floor_us else None}
             # the same calls in batch-invariant mode (no split-K kernels)
             mxfp8.set_batch_invariant(True)
             try:
@@ -456,17 +664,31 @@ def main():
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline and int(os.environ.get("RANK", "0")) == 0:
-        env = dict(os.environ)
-        env.pop("CUDA_VISIBLE_DEVICES", None)
-        r = subprocess.run([sys.executable, "-m", "oracle.cpu_bench", "--workload", "prefill",
-                            "--seconds", str(args.cpu_seconds)],
-                           cwd=ROOT, capture_output=True, text=True, env=env)
-        if r.returncode == 0:
-            c = json.loads(r.stdout.strip().splitlines()[-1])
-            cpu = {"value": c["value"], "unit": c["unit"], "cores": c["cores"],
-                   "kind": "oracle", "sample": c["sample"]}
+        def cpu_run(part, seconds, threads=None):
+            env = dict(os.environ)
+            env.pop("CUDA_VISIBLE_DEVICES", None)
+            if threads:
+                env["OMP_NUM_THREADS"] = str(threads)
+            r = subprocess.run([sys.executable, "-m", "oracle.cpu_bench", "--workload", "prefill",
+                                "--part", part, "--seconds", str(seconds)],
+                               cwd=ROOT, capture_output=True, text=True, env=env)
+            if r.returncode != 0:
+                return {"error": r.stderr[-300:]}
+            return json.loads(r.stdout.strip().splitlines()[-1])
+
+        c = cpu_run("layer", args.cpu_seconds)
+        if "error" in c:
+            cpu = c
         else:
-            cpu = {"error": r.stderr[-500:]}
+            cpu = {"value": c["value"], "unit": c["unit"], "cores": c["cores"],
+                   "kind": "oracle", "sample": c["sample"], "cpu_model": c.get("cpu_model")}
+            part_s = max(1.0, args.cpu_seconds / 4)
+            for part, key in (("quant", "quantizer"), ("gemm", "fp64_gemm")):
+                for th, tag in ((None, "all_cores"), (1, "one_thread")):
+                    r = cpu_run(part, part_s, th)
+                    cpu["%s_%s" % (key, tag)] = (
+                        r if "error" in r else {"value": round(r["value"], 3), "unit": r["unit"],
+                                                "cores": r["cores"], "sample": r["sample"]})
 
     out = {
         "metric": "MXFP8 linear TFLOP/s (incl. act quant) and % MFMA/HBM roofline, prefill & decode",
@@ -478,8 +700,10 @@ def main():
                                "-> y bf16 [4096,14336], act quant included",
                    "M": M, "N": N, "K": K, "rotated_sets": R, "inputs_sha256_16": inputs_sha},
         "roofline": roofline,
-        "quantizer": {"us": round(quant_us, 2), "GB/s": round(quant_bytes / (quant_us * 1e-6) / 1e9, 1),
-                      "hbm_frac": round(quant_bytes / (quant_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "quantizer": quantizer,
+        "step_protocol": step_protocol,
+        "clock": clock,
+        "attainable": attainable,
         "decode": decode,
         "other_workloads": others,
         "cpu_baseline": cpu,

@@ -1,0 +1,189 @@
+// mx_peaks.hip — microbenchmarks behind the attainable-peak denominators of bench.py (a library
+// of its own, libmxpeaks.so; the layer library does not contain it):
+//
+//  * mxpk_mfma_loop: every wave of the grid issues chains of independent scaled MFMAs
+//    (16x16x128, A / B operand formats as given) with no memory traffic in the loop, so the
+//    time is the matrix units' own rate on the running chip.
+//  * mxpk_clock_probe: one wave that waits a given time and reports the shader-clock cycles
+//    that passed, i.e. the clock the chip runs at while other work fills it.
+//  * mxpk_stream_read: a read of n bytes (16-byte loads, a few in flight per lane) whose words
+//    are folded into a value that is stored only in a case that never occurs, so the loads
+//    cannot be dropped and nothing is written.
+//
+// All are plain launches on the caller's stream; timing is the caller's (HIP events).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v6i __attribute__((ext_vector_type(6)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kChains = 8;   // independent accumulators per wave
+
+// shader-clock counter and the constant 100 MHz counter (scalar memory-time reads)
+__device__ __forceinline__ uint64_t shader_clock() {
+  uint64_t v = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_memtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v));
+#endif
+  return v;
+}
+__device__ __forceinline__ uint64_t real_clock() {
+  uint64_t v = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v));
+#endif
+  return v;
+}
+
+// operand register image: 32 bytes for FP8, 24 for FP6
+template <int F> struct Reg { typedef v8i type; };
+template <> struct Reg<2> { typedef v6i type; };
+
+// in-place scaled MFMA (D == C), so the accumulators stay put between iterations; the VGPR
+// constraints exist only in the device pass
+#if defined(__HIP_DEVICE_COMPILE__)
+#define MXPK_MFMA(FMT)                                                                        \
+  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]" \
+               FMT : "+v"(acc[c]) : "v"(a), "v"(b), "v"(sa), "v"(sb))
+#else
+#define MXPK_MFMA(FMT) (void)0
+#endif
+
+// clk (optional): lane 0 of wave 0 of block 0 stores the shader-clock cycles (s_memtime) and
+// the 100 MHz real-time ticks (s_memrealtime) its loop took, so the caller gets the clock the
+// chip ran the loop at
+template <int AF, int BF>
+__global__ void __launch_bounds__(256) k_mfma_loop(int iters, float* out, uint64_t* clk) {
+  const int t = threadIdx.x;
+  const uint64_t c0 = shader_clock();
+  const uint64_t r0 = real_clock();
+  // operands that the compiler cannot fold: small codes derived from the lane
+  typename Reg<AF>::type a;
+  typename Reg<BF>::type b;
+#pragma unroll
+  for (int i = 0; i < (AF == 0 ? 8 : 6); ++i) a[i] = (int)(0x01010101u * (uint32_t)((t + i) & 7));
+#pragma unroll
+  for (int i = 0; i < (BF == 0 ? 8 : 6); ++i) b[i] = (int)(0x01010101u * (uint32_t)((t * 3 + i) & 7));
+  [[maybe_unused]] const int sa = 127 + (t >> 10), sb = 127;   // E8M0 1.0 (t < 256)
+  v4f acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = (v4f){0.f, 0.f, 0.f, 0.f};
+  // the assembly MFMAs are invisible to the compiler's hazard checks: let the VALU writes of
+  // the operands retire first
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#endif
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+      if constexpr (AF == 0 && BF == 0) MXPK_MFMA("");
+      else if constexpr (AF == 0) MXPK_MFMA(" blgp:2");
+      else MXPK_MFMA(" cbsz:2 blgp:2");
+    }
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#endif
+  const uint64_t c1 = shader_clock();
+  const uint64_t r1 = real_clock();
+  if (clk && blockIdx.x == 0 && t == 0) {
+    clk[0] = c1 - c0;
+    clk[1] = r1 - r0;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  if (s == -1.0f) out[0] = s;    // never true for these operands; keeps the loop alive
+}
+
+// n16 16-byte words; each lane takes U words per pass, a pass covering the grid
+template <int U>
+__global__ void __launch_bounds__(256) k_stream_read(const uint4* __restrict__ p, int64_t n16,
+                                                     uint32_t* out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (U - 1) * stride < n16; i += U * stride) {
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u && out) out[0] = acc;   // data-dependent store that never happens
+}
+
+// one wave that waits until `ticks` of the 100 MHz counter have passed (bounded by time, so
+// it always ends), then stores the shader-clock cycles and ticks that elapsed: run beside
+// other work on a second stream, it gives the clock the chip ran that work at
+__global__ void __launch_bounds__(64) k_clock_probe(uint64_t ticks, uint64_t* out) {
+  const uint64_t c0 = shader_clock(), r0 = real_clock();
+  uint64_t r = r0;
+  while (r - r0 < ticks) {
+    __builtin_amdgcn_s_sleep(8);
+    r = real_clock();
+  }
+  const uint64_t c1 = shader_clock();
+  if (threadIdx.x == 0) {
+    out[0] = c1 - c0;
+    out[1] = r - r0;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// out: 2 uint64 (shader-clock cycles, 100 MHz ticks) over a wait of `ticks` ticks
+int mxpk_clock_probe(int64_t ticks, uint64_t* out, void* stream) {
+  if (ticks <= 0 || ticks > 1000000000 || !out) return -1;
+  hipLaunchKernelGGL(k_clock_probe, dim3(1), dim3(64), 0, (hipStream_t)stream, (uint64_t)ticks,
+                     out);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// flop per launch = blocks * 4 waves * iters * kChains * 2 * 16 * 16 * 128
+int mxpk_mfma_chains(void) { return kChains; }
+
+// clk: null, or 2 uint64 (shader-clock cycles, 100 MHz ticks) of block 0's loop
+int mxpk_mfma_loop(int afmt, int bfmt, int blocks, int iters, float* out, uint64_t* clk,
+                   void* stream) {
+  if (blocks <= 0 || iters <= 0 || !out) return -1;
+  hipStream_t s = (hipStream_t)stream;
+  if (afmt == 0 && bfmt == 0)
+    hipLaunchKernelGGL((k_mfma_loop<0, 0>), dim3(blocks), dim3(256), 0, s, iters, out, clk);
+  else if (afmt == 0 && bfmt == 2)
+    hipLaunchKernelGGL((k_mfma_loop<0, 2>), dim3(blocks), dim3(256), 0, s, iters, out, clk);
+  else if (afmt == 2 && bfmt == 2)
+    hipLaunchKernelGGL((k_mfma_loop<2, 2>), dim3(blocks), dim3(256), 0, s, iters, out, clk);
+  else
+    return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// read `bytes` (a multiple of 16) from p: `blocks` workgroups of 256 lanes, `unroll` (4, 8 or
+// 16) 16-byte loads in flight per lane
+int mxpk_stream_read(const void* p, int64_t bytes, int blocks, int unroll, uint32_t* out,
+                     void* stream) {
+  if (!p || bytes <= 0 || bytes % 16 != 0 || blocks <= 0) return -1;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t n16 = bytes / 16;
+  if (unroll == 4)
+    hipLaunchKernelGGL(k_stream_read<4>, dim3(blocks), dim3(256), 0, s, (const uint4*)p, n16, out);
+  else if (unroll == 8)
+    hipLaunchKernelGGL(k_stream_read<8>, dim3(blocks), dim3(256), 0, s, (const uint4*)p, n16, out);
+  else if (unroll == 16)
+    hipLaunchKernelGGL(k_stream_read<16>, dim3(blocks), dim3(256), 0, s, (const uint4*)p, n16, out);
+  else
+    return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+}  // extern "C"

@@ -202,7 +202,8 @@ def measure_peaks(full=False):
     one) and plain HBM reads (the best launch shape)."""
     L = _peaks_lib()
     res = {"mfma_TFLOPs": {}, "mfma_clock_MHz": {}}
-    for name, af, bf in (("fp8xfp8", 0, 0), ("fp8xfp6", 0, 2), ("fp6xfp6", 2, 2)):
+    for name, af, bf in (("fp8xfp8", 0, 0), ("fp8xfp6", 0, 2), ("fp6xfp6", 2, 2),
+                         ("fp8xfp8_32x32x64", 100, 100)):
         best = max((mfma_peak(L, af, bf, blocks) for blocks in (1024, 2048)),
                    key=lambda r: r[0])
         res["mfma_TFLOPs"][name] = round(best[0], 1)
@@ -216,6 +217,38 @@ def measure_peaks(full=False):
                                                     "unroll": unroll, "blocks": blocks}
     res["hbm_GBs"] = res["stream_read"]["1024MiB"]["GB/s"]
     return res, L
+
+
+def gemm_only(args, dev):
+    """--only gemm for the outlier and MXFP6 workloads: the GEMM alone (pre-quantized entry)
+    --steps times over enough rotated operand / output sets to exceed the Infinity Cache, for
+    rocprofv3 counter passes."""
+    import numpy as np
+    import torch
+    from mx_block_scaled_amd import mxfp8, synth
+
+    def bf16_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    name = {"outlier": "outlier"}.get(args.workload, "mxfp6")
+    d = synth.make(name)
+    M, N, K = d["M"], d["N"], d["K"]
+    wfmt = "e4m3" if args.workload == "outlier" else args.workload.split("_")[1]
+    afmt = wfmt if args.workload.startswith("w6a6") else "e4m3"
+    xq, xs = mxfp8.quantize_act_fmt(bf16_dev(d["x"]), afmt)
+    wq, ws = mxfp8.quantize_weight(bf16_dev(d["w"]), wfmt)
+    pk = mxfp8.prepack_weight(wq, ws, wfmt)
+    del wq, ws
+    set_bytes = xq.numel() + xs.numel() + pk.numel() + M * N * 2
+    R = max(2, -(-2 * MALL_BYTES // set_bytes))
+    sets = [(xq.clone(), xs.clone(), pk.clone(), torch.empty((M, N), dtype=torch.bfloat16, device=dev))
+            for _ in range(R)]
+    for i in range(args.steps):
+        a, b, p, y = sets[i % R]
+        mxfp8.linear_prequant_fmt(a, b, p, N, K, wfmt, afmt, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"gemm_launches": args.steps, "workload": args.workload, "rotated_sets": R,
+                      "M": M, "N": N, "K": K}))
 
 
 def main():
@@ -233,6 +266,10 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=500.0,
                     help="GPU time of untimed steps run first, so the chip reaches its steady "
                          "clock before anything is timed")
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "outlier", "mxfp6_e2m3", "mxfp6_e3m2", "w6a6_e2m3",
+                             "w6a6_e3m2"],
+                    help="with --only gemm: whose GEMM is launched (pre-quantized entry)")
     ap.add_argument("--only", choices=["all", "gemm", "copy", "decode", "peaks"], default="all",
                     help="counter runs: 'gemm' launches only the prefill GEMM (pre-quantized "
                          "entry) --steps times; 'decode' runs the decode calls (M = 1, 8, 32) "
@@ -282,6 +319,10 @@ def main():
                 mxfp8.linear(xd, pks[i % 32], Nd, "e4m3", bias, out=yd, workspace=wsd)
             torch.cuda.synchronize()
         print(json.dumps({"decode_calls_per_M": args.steps, "M": [1, 8, 32], "N": Nd, "K": Kd}))
+        return
+
+    if args.only == "gemm" and args.workload != "prefill":
+        gemm_only(args, dev)
         return
 
     # ------------------------------------------------------------ prefill workload

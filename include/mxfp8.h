@@ -249,15 +249,28 @@ int mxfp8_linear_prequant_fmt(const void* xq, const void* xs, int64_t M, int64_t
  * invariant).  on != 0: every M runs on kernels that add the K steps of an output in
  * sequence, so a row's result does not depend on how many rows the call has (the small-M
  * kernels, which split K over waves, are not used).  on == 0 (default): fastest kernel per
- * shape.  Process-wide; not for use while other threads are launching.  Returns MX_OK. */
+ * shape.  Returns MX_OK.
+ * Thread safety: the mode is one process-wide atomic flag, read by each call while it picks
+ * its kernels.  Calls made after this function returns (on any thread) use the new mode.  A
+ * call running on another thread while the mode changes may pick some of its kernels under
+ * either mode: its result is still correct (within the layer's tolerance) and it still needs
+ * only mxfp8_workspace_bytes of workspace, but it is batch invariant only if it started after
+ * mxfp8_set_batch_invariant(1) returned.  Already enqueued work is never affected. */
 int mxfp8_set_batch_invariant(int on);
 
 
-/* Tuning / testing hook: force the tile of the LDS-tiled GEMM used for large M (fn, fm =
- * 16-row weight fragments and 16-row activation groups per wave; the workgroup of 8 waves
- * covers 32 fn weight rows x 64 fm activation rows).  Compiled choices: (8,4) (7,4) (6,4)
- * (4,4) (4,2); (0,0) restores the automatic
- * choice.  Process-wide; not for use while other threads are launching.  MX_EINVAL otherwise. */
+/* Tuning / testing hook: force the tile of the LDS-tiled GEMM used for large M.
+ *   (fn, fm) in (8,4) (7,4) (6,4) (4,4) (4,2): the eight-wave kernel, fn, fm = 16-row weight
+ *     fragments and 16-row activation groups per wave; the workgroup covers 32 fn weight rows
+ *     x 64 fm activation rows;
+ *   (16,16) (17,16) (18,16) (19,16): the four-wave kernel (one wave per SIMD, 32x32x64 scaled
+ *     MFMAs, E4M3 weights and K % 512 == 0 only; other layers keep the automatic choice), with
+ *     workgroup tiles 256 x 256, 224 x 256, 192 x 256 and 256 x 128 (weight rows x activation
+ *     rows);
+ *   (0,0) restores the automatic choice.  MX_EINVAL for any other pair.
+ * A forced tile also turns off the split-K tiled path.  Thread safety as for
+ * mxfp8_set_batch_invariant: one process-wide atomic setting, read by each call when it
+ * launches; a call concurrent with a change runs with either setting (each correct). */
 int mxfp8_set_tile_config(int fn, int fm);
 
 #ifdef __cplusplus

@@ -48,8 +48,12 @@ template <> struct Reg<2> { typedef v6i type; };
 #define MXPK_MFMA(FMT)                                                                        \
   asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]" \
                FMT : "+v"(acc[c]) : "v"(a), "v"(b), "v"(sa), "v"(sb))
+#define MXPK_MFMA32()                                                                         \
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"  \
+               : "+a"(acc[c]) : "v"(a), "v"(b), "v"(sa), "v"(sb))
 #else
 #define MXPK_MFMA(FMT) (void)0
+#define MXPK_MFMA32() (void)0
 #endif
 
 // clk (optional): lane 0 of wave 0 of block 0 stores the shader-clock cycles (s_memtime) and
@@ -97,6 +101,46 @@ __global__ void __launch_bounds__(256) k_mfma_loop(int iters, float* out, uint64
 #pragma unroll
   for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
   if (s == -1.0f) out[0] = s;    // never true for these operands; keeps the loop alive
+}
+
+// the same loop with the 32x32x64 scaled MFMA (FP8 operands), accumulators in AGPRs
+__global__ void __launch_bounds__(256) k_mfma32_loop(int iters, float* out, uint64_t* clk) {
+  typedef float v16f __attribute__((ext_vector_type(16)));
+  const int t = threadIdx.x;
+  const uint64_t c0 = shader_clock();
+  const uint64_t r0 = real_clock();
+  v8i a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (int)(0x01010101u * (uint32_t)((t + i) & 7));
+    b[i] = (int)(0x01010101u * (uint32_t)((t * 3 + i) & 7));
+  }
+  [[maybe_unused]] const int sa = 127 + (t >> 10), sb = 127;
+  v16f acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = (v16f){};
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#endif
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) MXPK_MFMA32();
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#endif
+  const uint64_t c1 = shader_clock();
+  const uint64_t r1 = real_clock();
+  if (clk && blockIdx.x == 0 && t == 0) {
+    clk[0] = c1 - c0;
+    clk[1] = r1 - r0;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[c][e];
+  if (s == -1.0f) out[0] = s;
 }
 
 // n16 16-byte words; each lane takes U words per pass, a pass covering the grid
@@ -149,7 +193,8 @@ int mxpk_clock_probe(int64_t ticks, uint64_t* out, void* stream) {
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 
-// flop per launch = blocks * 4 waves * iters * kChains * 2 * 16 * 16 * 128
+// flop per launch = blocks * 4 waves * iters * kChains * 2 * 16 * 16 * 128 (the 32x32x64 loop
+// has 4 chains of twice the flop each: the same count)
 int mxpk_mfma_chains(void) { return kChains; }
 
 // clk: null, or 2 uint64 (shader-clock cycles, 100 MHz ticks) of block 0's loop
@@ -163,6 +208,8 @@ int mxpk_mfma_loop(int afmt, int bfmt, int blocks, int iters, float* out, uint64
     hipLaunchKernelGGL((k_mfma_loop<0, 2>), dim3(blocks), dim3(256), 0, s, iters, out, clk);
   else if (afmt == 2 && bfmt == 2)
     hipLaunchKernelGGL((k_mfma_loop<2, 2>), dim3(blocks), dim3(256), 0, s, iters, out, clk);
+  else if (afmt == 100 && bfmt == 100)   // 32x32x64, FP8 x FP8: 4 chains, 2x the flop each
+    hipLaunchKernelGGL(k_mfma32_loop, dim3(blocks), dim3(256), 0, s, iters, out, clk);
   else
     return -1;
   return hipGetLastError() == hipSuccess ? 0 : -6;

@@ -649,6 +649,383 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- 4-wave kernel (large tiles)
+// One wave per SIMD, 2 (n) x 2 (m) waves, each owning a 32 FNB x 32 FMB block of the output
+// as FNB x FMB tiles of the 32x32x64 scaled MFMA, accumulators held in the AGPRs (256 of them
+// for the 128 x 128 wave tile of the 256 x 256 workgroup tile).  Per 128-wide K step a wave
+// reads (32 FNB + 32 FMB) x 128 operand bytes from LDS for 2 FNB FMB MFMAs: half the LDS reads
+// per MFMA of the eight-wave kernel's 112 x 64 wave tiles, and 7 % fewer copied bytes per
+// output (workgroup tile 256 x 256 against 224 x 256).
+//
+// 32x32x64 operand layout (measured on gfx950 with one-hot inputs): lane l = (R = l % 32,
+// g = l / 32) holds row R's K bytes 32 h + 16 g + t (piece h = 0, 1, byte t < 16); the scale of
+// row R, 32-block b comes from lane R + 32 b (op-select picks its byte); accumulator element e
+// of lane l is C[8 (e / 4) + 4 (l / 32) + e % 4][l % 32].  A prepacked 16 x 128 fragment keeps
+// K bytes 64 h' + 16 g' + t of row r in lane (r, g') of half h', so the operand of K half s is
+// the 16-byte pieces (h' = s, g' = g) and (h' = s, g' = 2 + g): two LDS reads, 512 bytes apart.
+//
+// Pipeline: both stages of a step are copied global -> LDS one step ahead (direct-to-LDS, every
+// wave issuing a share, interleaved one copy per MFMA).  Within a step the second K half's
+// MFMAs are deferred past the next barrier: after it, a wave first issues the next step's
+// first-half operand reads, then runs the deferred MFMAs (their operands are already in
+// registers), so the matrix pipe is busy while the barrier resolves and the reads land.
+// Results equal the other kernels' within the usual fp32 reordering; every accumulator takes
+// its K steps in order.
+template <int WFMT, int WGN, int FNB, int FMB>
+struct W4Cfg {
+  static constexpr int NW = 4, WGM = NW / WGN;            // wave grid WGN (n) x WGM (m)
+  static constexpr int FB = frag_bytes(WFMT);
+  static constexpr int BN = 32 * FNB * WGN, BM = 32 * FMB * WGM;
+  static constexpr int A_BYTES = (BN / 16) * FB;
+  static constexpr int B_BYTES = BM * 128;
+  static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int A_CHUNKS = A_BYTES / 1024;
+  static constexpr int A_PW = (A_CHUNKS + NW - 1) / NW;   // surplus slots -> scratch
+  static constexpr int B_PW = B_BYTES / 1024 / NW;
+  static constexpr int D = A_PW + B_PW;                   // tile copies per wave per step
+  static constexpr int SA_PIECES = (BN / 16 + 3) / 4, SB_PIECES = BM / 16;
+  static constexpr int SA_PW = (SA_PIECES + NW - 1) / NW, SB_PW = (SB_PIECES + NW - 1) / NW;
+  static constexpr int SA_BYTES = SA_PIECES * 1024, SB_BYTES = SB_PIECES * 256;
+  static constexpr int SCALE_BYTES = SA_BYTES + SB_BYTES;
+  static constexpr int SCRATCH = 1024;
+  static constexpr int OUT_PITCH = (BN * 2 - 16 + 255) / 256 * 256 + 16;
+  static constexpr int LDS_MAIN = 2 * STAGE + 2 * SCALE_BYTES + SCRATCH;
+  static constexpr int LDS_BYTES = LDS_MAIN > BM * OUT_PITCH ? LDS_MAIN : BM * OUT_PITCH;
+  static_assert(WGN == 1 || WGN == 2 || WGN == 4, "wave grid");
+  static_assert(A_BYTES % 1024 == 0 && B_BYTES % (1024 * NW) == 0, "1 KiB copy chunks");
+  static_assert(LDS_BYTES <= 160 * 1024, "must fit the 160 KiB LDS");
+  static_assert(FNB * FMB * 16 <= 256, "accumulators must fit the AGPRs");
+};
+
+#define MX_MFMA32_ASM(OPSEL, FMT)                                                               \
+  asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %4 " OPSEL FMT          \
+               : "+a"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb))
+#define MX_MFMA32_Q(FMT)                                            \
+  do {                                                              \
+    if constexpr (Q == 0) MX_MFMA32_ASM(MX_MFMA_OPSEL_0, FMT);      \
+    else if constexpr (Q == 1) MX_MFMA32_ASM(MX_MFMA_OPSEL_1, FMT); \
+    else if constexpr (Q == 2) MX_MFMA32_ASM(MX_MFMA_OPSEL_2, FMT); \
+    else MX_MFMA32_ASM(MX_MFMA_OPSEL_3, FMT);                       \
+  } while (0)
+
+// 32x32x64 scaled MFMA, accumulating in place in AGPRs (A = weight format, B = E4M3)
+template <int WFMT, int Q, class TA>
+__device__ __forceinline__ void mfma32_inplace(v16f& acc, const TA& a, const v8i& b, uint32_t sa,
+                                               uint32_t sb) {
+  static_assert(Q >= 0 && Q < 4, "op-select byte");
+  static_assert(std::is_same<TA, typename AReg<WFMT>::type>::value, "operand register image");
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (WFMT == 0) MX_MFMA32_Q("");
+  else if constexpr (WFMT == 2) MX_MFMA32_Q(" cbsz:2");
+  else MX_MFMA32_Q(" cbsz:3");
+#endif
+}
+
+template <int WFMT, int WGN, int FNB, int FMB>
+__global__ __launch_bounds__(256, 1) void k_gemm_w4(const uint8_t* __restrict__ xq,
+                                                    const uint8_t* __restrict__ xs, int M, int K,
+                                                    const uint8_t* __restrict__ packed, int N,
+                                                    const uint16_t* __restrict__ bias,
+                                                    uint16_t* __restrict__ y, int tiles_m,
+                                                    int tiles_n, int group_m, BatchStrides bs) {
+  using C = W4Cfg<WFMT, WGN, FNB, FMB>;
+  typedef typename AReg<WFMT>::type AR;
+  MX_BATCH_OFFSET(blockIdx.y);
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_BYTES];
+  uint8_t* const slds = lds + 2 * C::STAGE;                  // two group-scale buffers
+  uint8_t* const scratch = slds + 2 * C::SCALE_BYTES;        // surplus copy slots land here
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave % WGN, wm = wave / WGN;
+  const int R = lane & 31, gq = lane >> 5, r = lane & 15;
+
+  // ---- tile of this workgroup: each XCD a contiguous range, in groups of group_m m-tiles
+  const int T = tiles_m * tiles_n;
+  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const int t = xcd * (T >> 3) + (xcd < (T & 7) ? xcd : (T & 7)) + slot;
+  const int gsz = group_m * tiles_n;
+  const int first_m = (t / gsz) * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int tm = first_m + (t % gsz) % gm;
+  const int tn = (t % gsz) / gm;
+  const int n0 = tn * C::BN, m0 = tm * C::BM;
+
+  const int NG = N >> 4, KB = K >> 5, KT = K >> 7;
+  const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * C::FB);
+
+  // ---- copy sources: 32-bit lane offsets from uniform bases (as in k_gemm_tile)
+  uint32_t a_off[C::A_PW];
+#pragma unroll
+  for (int i = 0; i < C::A_PW; ++i) {
+    const int c = min(wave + C::NW * i, C::A_CHUNKS - 1);
+    if (C::FB % 1024 == 0) {
+      const int f = c * 1024 / C::FB;
+      a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (c * 1024 - f * C::FB));
+    } else {
+      const int off = c * 1024 + lane * 16;
+      const int f = off / C::FB;
+      a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (off - f * C::FB));
+    }
+  }
+  const uint32_t a_lane = C::FB % 1024 == 0 ? (uint32_t)lane * 16 : 0u;
+  uint32_t b_off[C::B_PW];
+#pragma unroll
+  for (int i = 0; i < C::B_PW; ++i) {
+    const int row = 8 * (wave + C::NW * i) + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    b_off[i] = (uint32_t)(min(m0 + row, M - 1) * K + chunk * 16);
+  }
+  // the p-th tile copy of step kt into stage `stage` (p < D: weight chunks, then activations)
+  auto copy_one = [&](int kt, int stage, int p) __attribute__((always_inline)) {
+    uint8_t* base = lds + stage * C::STAGE;
+    if (p < C::A_PW) {
+      const int c = wave + C::NW * p;
+      dma16(packed + (uint32_t)(kt * NG * C::FB + a_off[p] + a_lane),
+            c < C::A_CHUNKS ? base + c * 1024 : scratch);
+    } else {
+      const int i = p - C::A_PW;
+      dma16(xq + (uint32_t)(kt * 128 + b_off[i]), base + C::A_BYTES + (wave + C::NW * i) * 1024);
+    }
+  };
+  // scale copies of group kt4 into buffer sbuf: weight words (16 B per lane, four fragments
+  // per instruction) and activation rows (4 B per lane, 16 rows per instruction)
+  uint32_t sa_src[C::SA_PW];
+#pragma unroll
+  for (int i = 0; i < C::SA_PW; ++i) {
+    const int c = min(wave + C::NW * i, C::SA_PIECES - 1);
+    sa_src[i] = (uint32_t)(min((n0 >> 4) + 4 * c + (lane >> 4), NG - 1) * 256 + (lane & 15) * 16);
+  }
+  uint32_t sb_src[C::SB_PW];
+#pragma unroll
+  for (int i = 0; i < C::SB_PW; ++i) {
+    const int c = min(wave + C::NW * i, C::SB_PIECES - 1);
+    sb_src[i] = (uint32_t)(min(m0 + 16 * c + (lane >> 2), M - 1) * KB + (lane & 3) * 4);
+  }
+  auto copy_scales = [&](int kt4, int sbuf) __attribute__((always_inline)) {
+    uint8_t* base = slds + sbuf * C::SCALE_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::SA_PW; ++i) {
+      const int c = wave + C::NW * i;
+      dma16((const uint8_t*)wsc + (uint32_t)(kt4 * NG * 256 + sa_src[i]),
+            c < C::SA_PIECES ? base + c * 1024 : scratch);
+    }
+#pragma unroll
+    for (int i = 0; i < C::SB_PW; ++i) {
+      const int c = wave + C::NW * i;
+      dma4(xs + (uint32_t)(sb_src[i] + 16 * kt4), c < C::SB_PIECES ? base + C::SA_BYTES + c * 256 : scratch);
+    }
+  };
+  // this lane's scale words of group kt4: weight block i, K half s -> row R of the block,
+  // 32-block 2 s + gq of each step (byte kt % 4); activations likewise, gathered from the
+  // row's 16 bytes (byte 4 q + 2 s + gq -> byte q)
+  const uint32_t cs0 = (uint32_t)gq, cs1 = (uint32_t)(2 + gq);
+  const uint32_t psel0 = cs0 | ((4 + cs0) << 8) | (0x0Cu << 16) | (0x0Cu << 24);
+  const uint32_t psel1 = cs1 | ((4 + cs1) << 8) | (0x0Cu << 16) | (0x0Cu << 24);
+  auto read_scales = [&](int sbuf, uint32_t (*sa)[2], uint32_t (*sb)[2]) __attribute__((always_inline)) {
+    const uint8_t* base = slds + sbuf * C::SCALE_BYTES;
+#pragma unroll
+    for (int i = 0; i < FNB; ++i) {
+      const int ngl = 2 * (wn * FNB + i) + (R >> 4);
+      sa[i][0] = *(const uint32_t*)(base + ngl * 256 + (r + 16 * gq) * 4);
+      sa[i][1] = *(const uint32_t*)(base + ngl * 256 + (r + 16 * (2 + gq)) * 4);
+    }
+#pragma unroll
+    for (int j = 0; j < FMB; ++j) {
+      const v4i w = *(const v4i*)(base + C::SA_BYTES + (wm * 32 * FMB + 32 * j + R) * 16);
+      const uint32_t lo0 = __builtin_amdgcn_perm((uint32_t)w[1], (uint32_t)w[0], psel0);
+      const uint32_t hi0 = __builtin_amdgcn_perm((uint32_t)w[3], (uint32_t)w[2], psel0);
+      const uint32_t lo1 = __builtin_amdgcn_perm((uint32_t)w[1], (uint32_t)w[0], psel1);
+      const uint32_t hi1 = __builtin_amdgcn_perm((uint32_t)w[3], (uint32_t)w[2], psel1);
+      sb[j][0] = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u);
+      sb[j][1] = __builtin_amdgcn_perm(hi1, lo1, 0x05040100u);
+    }
+  };
+
+  // ---- operand reads from LDS (K half s of the step in stage `stage`)
+  // weight block i: fragments 2 (wn FNB + i) and + 1; lane reads fragment row R of it
+  const uint32_t a_rd = (uint32_t)((2 * wn * FNB + (R >> 4)) * C::FB);
+  const uint32_t b_rd = (uint32_t)((wm * 32 * FMB + R) * 128);
+  const uint32_t sw = (uint32_t)swz(R);
+  auto load_a = [&](const uint8_t* st, int i, int s) __attribute__((always_inline)) {
+    const uint8_t* f = st + a_rd + i * 2 * C::FB;
+    if constexpr (WFMT == 0) {
+      const v4i lo = *(const v4i*)(f + s * 1024 + (r + 16 * gq) * 16);
+      const v4i hi = *(const v4i*)(f + s * 1024 + 512 + (r + 16 * gq) * 16);
+      return (AR){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    } else {   // FP6: 32-block 2 s + gq of row R: 16 bytes, then 8
+      const v4i lo = *(const v4i*)(f + (r + 16 * (2 * s + gq)) * 16);
+      const v2i hi = *(const v2i*)(f + 1024 + (r + 16 * (2 * s + gq)) * 8);
+      return (AR){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1]};
+    }
+  };
+  auto load_b = [&](const uint8_t* st, int j, int s) __attribute__((always_inline)) {
+    const uint8_t* row = st + C::A_BYTES + b_rd + j * 32 * 128;
+    const v4i lo = *(const v4i*)(row + (((uint32_t)(4 * s + gq) ^ sw) << 4));
+    const v4i hi = *(const v4i*)(row + (((uint32_t)(4 * s + 2 + gq) ^ sw) << 4));
+    return (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+
+  v16f acc[FNB][FMB];
+#pragma unroll
+  for (int i = 0; i < FNB; ++i)
+#pragma unroll
+    for (int j = 0; j < FMB; ++j) acc[i][j] = (v16f){};
+
+  uint32_t sa[FNB][2] = {}, sb[FMB][2] = {};   // this group's scale words
+  uint32_t ta[FNB] = {}, tb[FMB] = {};         // the deferred half's, across a group boundary
+  AR ay[FNB];                            // second-half operands, used after the next barrier
+  v8i by[FMB];
+  const int KT4 = KT >> 2;               // whole groups (K % 512 == 0)
+
+  // prologue: group 0's scales and step 0's tiles
+  copy_scales(0, 0);
+#pragma unroll
+  for (int p = 0; p < C::D; ++p) copy_one(0, 0, p);
+
+  // One K step.  After the barrier the wave issues this step's first-half operand reads, then
+  // runs the deferred second half of step kt - 1 (its operands are already in registers) with
+  // one copy for step kt + 1 after each MFMA; then this step's first half, with the second-half
+  // operand reads issued after its first MFMAs.  (Spreading the operand reads one or two per
+  // MFMA measured slower: 209 against 195 us on the prefill GEMM.)  FIRST (step 0) has no
+  // deferred half.  Copies past the last step re-fetch the last step (or group of scales) into
+  // the free buffer, unused, so every step issues the same operations and nothing in the loop
+  // depends on kt at run time.
+  auto step = [&](int kt, auto qc, auto firstc) __attribute__((always_inline)) {
+    constexpr int Q = decltype(qc)::value;
+    constexpr bool FIRST = decltype(firstc)::value;
+    constexpr int QD = (Q + 3) & 3;      // op-select byte of the deferred half (step kt - 1)
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm_barrier<0>();                // step kt's tiles (and its group's scales) landed;
+                                         // every wave is done with stage (kt + 1) % 2
+    const uint8_t* st = lds + (kt & 1) * C::STAGE;
+    if constexpr (Q == 0) {
+#pragma unroll
+      for (int i = 0; i < FNB; ++i) ta[i] = sa[i][1];
+#pragma unroll
+      for (int j = 0; j < FMB; ++j) tb[j] = sb[j][1];
+      read_scales((kt >> 2) & 1, sa, sb);
+    }
+    // first-half operands of this step
+    AR ax[FNB];
+    v8i bx[FMB];
+#pragma unroll
+    for (int j = 0; j < FMB; ++j) bx[j] = load_b(st, j, 0);
+#pragma unroll
+    for (int i = 0; i < FNB; ++i) ax[i] = load_a(st, i, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    const int kn = min(kt + 1, KT - 1);
+    if constexpr (Q == 0) copy_scales(min((kt >> 2) + 1, KT4 - 1), ((kt >> 2) + 1) & 1);
+    int p = 0;
+#pragma unroll
+    for (int i = 0; i < FNB; ++i) {
+#pragma unroll
+      for (int j = 0; j < FMB; ++j) {
+        if constexpr (!FIRST) {
+          if constexpr (Q == 0) mfma32_inplace<WFMT, QD>(acc[i][j], ay[i], by[j], ta[i], tb[j]);
+          else mfma32_inplace<WFMT, QD>(acc[i][j], ay[i], by[j], sa[i][1], sb[j][1]);
+        }
+        if (p < C::D) copy_one(kn, (kt + 1) & 1, p);
+        ++p;
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (; p < C::D; ++p) copy_one(kn, (kt + 1) & 1, p);
+    // scale words written by VALU above: two wait states before the assembly MFMAs read them
+    if constexpr (Q == 0) asm volatile("s_nop 2" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    int u = 0;
+#pragma unroll
+    for (int i = 0; i < FNB; ++i) {
+#pragma unroll
+      for (int j = 0; j < FMB; ++j) {
+        mfma32_inplace<WFMT, Q>(acc[i][j], ax[i], bx[j], sa[i][0], sb[j][0]);
+        ++u;
+        if (u == 2) {
+#pragma unroll
+          for (int jj = 0; jj < FMB; ++jj) by[jj] = load_b(st, jj, 1);
+        } else if (u == 3) {
+#pragma unroll
+          for (int ii = 0; ii < FNB; ++ii) ay[ii] = load_a(st, ii, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  step(0, I0(), T_());
+  step(1, I1(), F_());
+  step(2, I2(), F_());
+  step(3, I3(), F_());
+  for (int kt4 = 1; kt4 < KT4; ++kt4) {
+    step(4 * kt4 + 0, I0(), F_());
+    step(4 * kt4 + 1, I1(), F_());
+    step(4 * kt4 + 2, I2(), F_());
+    step(4 * kt4 + 3, I3(), F_());
+  }
+  // the last step's second half
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): its operands are in registers
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < FNB; ++i)
+#pragma unroll
+    for (int j = 0; j < FMB; ++j) mfma32_inplace<WFMT, 3>(acc[i][j], ay[i], by[j], sa[i][1], sb[j][1]);
+  // every copy landed and every wave done before LDS is reused for the output; the nops give
+  // the last (assembly) MFMAs their result latency before the accumulators are read
+  wait_vm_barrier<0>();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 15\n s_nop 15\n s_nop 15\n s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- epilogue: bias, bf16, through LDS as a [BM][BN] tile, then 16-byte coalesced stores.
+  // Lane holds, for u < 4, n = 32 (wn FNB + i) + 8 u + 4 gq + (0..3) of row m = 32 (wm FMB + j) + R
+#pragma unroll
+  for (int i = 0; i < FNB; ++i) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int nl = 32 * (wn * FNB + i) + 8 * u + 4 * gq;
+      float bv[4] = {0.f, 0.f, 0.f, 0.f};
+      if (bias && n0 + nl < N) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bv[e] = bf16_to_float(bias[n0 + nl + e]);
+      }
+#pragma unroll
+      for (int j = 0; j < FMB; ++j) {
+        const int ml = 32 * (wm * FMB + j) + R;
+        const v2i o = {(int)pack_bf16x2(acc[i][j][4 * u + 0] + bv[0], acc[i][j][4 * u + 1] + bv[1]),
+                       (int)pack_bf16x2(acc[i][j][4 * u + 2] + bv[2], acc[i][j][4 * u + 3] + bv[3])};
+        *(v2i*)(lds + ml * C::OUT_PITCH + nl * 2) = o;
+      }
+    }
+  }
+  __syncthreads();
+  constexpr int ROW_PIECES = C::BN * 2 / 16;
+#pragma unroll 4
+  for (int q = tid; q < C::BM * ROW_PIECES; q += C::NW * 64) {
+    const int ml = q / ROW_PIECES, cp = q - ml * ROW_PIECES;
+    const int m = m0 + ml, n = n0 + cp * 8;
+    if (m < M && n < N)
+      __builtin_nontemporal_store(*(const v4i*)(lds + ml * C::OUT_PITCH + cp * 16), (v4i*)(y + (int64_t)m * N + n));
+  }
+}
+
+template <int WFMT, int WGN, int FNB, int FMB>
+static void launch_w4(const uint8_t* xq, const uint8_t* xs, int M, int K, const uint8_t* packed,
+                      int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s,
+                      int batch, const BatchStrides& bs) {
+  using C = W4Cfg<WFMT, WGN, FNB, FMB>;
+  const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
+  hipLaunchKernelGGL((k_gemm_w4<WFMT, WGN, FNB, FMB>), dim3((unsigned)(tm * tn), (unsigned)batch), dim3(256),
+                     0, s, xq, xs, M, K, packed, N, bias, y, tm, tn, group_m, bs);
+}
+
+
 template <int WFMT, int XFMT, int FN, int FM, int S>
 static void launch_tile(const uint8_t* xq, const uint8_t* xs, int M, int K, const uint8_t* packed,
                         int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s,
@@ -713,14 +1090,15 @@ int64_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
 // counts the tiles of all its layers.
 struct TileChoice { int fn, fm; };
 // compiled tiles (fn, fm) -> workgroup tile 32 fn x 64 fm, two LDS stages
-static std::atomic<int> g_force_tile{0};   // fn * 16 + fm, 0 = automatic
-void force_tile(int fn, int fm) { g_force_tile.store(fn * 16 + fm); }
+static std::atomic<int> g_force_tile{0};   // fn * 256 + fm, 0 = automatic
+void force_tile(int fn, int fm) { g_force_tile.store(fn * 256 + fm); }
 static std::atomic<bool> g_batch_invariant{false};
 void set_batch_invariant(bool on) { g_batch_invariant.store(on); }
 bool batch_invariant() { return g_batch_invariant.load(std::memory_order_relaxed); }
-static TileChoice choose_tile(int M, int N, int batch) {
+static TileChoice choose_tile(int M, int N, int batch, bool w4_ok) {
   const int f = g_force_tile.load(std::memory_order_relaxed);
-  if (f) return TileChoice{f / 16, f % 16};
+  // a forced four-wave tile (fm == 16) applies only where that kernel does
+  if (f && (f % 256 != 16 || w4_ok)) return TileChoice{f / 256, f % 256};
   static const TileChoice opts[] = {{8, 4}, {7, 4}, {6, 4}, {4, 4}, {4, 2}};
   double best = 1e30;
   TileChoice pick = opts[0];
@@ -751,7 +1129,19 @@ static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int 
     hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)blocks), dim3(256), 0, s, part, parts, MN, N, bias, y);
     return hipGetLastError();
   }
-  const TileChoice c = choose_tile(M, N, batch);
+  const TileChoice c = choose_tile(M, N, batch, WFMT == 0 && XFMT == 0 && K % 512 == 0);
+  if constexpr (WFMT == 0 && XFMT == 0) {
+    // the four-wave kernel, by the tile override only (tuning and tests): measured slower than
+    // the eight-wave kernel on the prefill and outlier shapes (195 - 210 against 183 - 191 us;
+    // 56 - 60 against 54 us)
+    if (c.fm == 16) {
+      if (c.fn == 16) launch_w4<0, 2, 4, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+      else if (c.fn == 17) launch_w4<0, 1, 7, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+      else if (c.fn == 18) launch_w4<0, 1, 6, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+      else launch_w4<0, 2, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+      return hipGetLastError();
+    }
+  }
   if (c.fn == 8 && c.fm == 4) launch_tile<WFMT, XFMT, 8, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else if (c.fn == 7 && c.fm == 4) launch_tile<WFMT, XFMT, 7, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
   else if (c.fn == 6 && c.fm == 4) launch_tile<WFMT, XFMT, 6, 4, 2>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);

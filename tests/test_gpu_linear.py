@@ -198,6 +198,30 @@ def test_tiled_kernel_every_tile(fn, fm, fmt):
         mxfp8.set_tile_config(0, 0)
 
 
+# The four-wave kernel (32x32x64 scaled MFMAs, accumulators in the AGPRs; E4M3 weights,
+# K % 512 == 0), each of its tiles (forced: 256 x 256 and 256 x 128 on a 2 x 2 wave grid,
+# 224 x 256 and 192 x 256 on a 1 x 4 wave grid): ragged M and N tails, one tile smaller than
+# the workgroup tile, several tiles over the XCD ranges, with and without bias.
+W4_SHAPES = [(300, 592, 1024), (96, 256, 512), (520, 1040, 2048), (1024, 2048, 4096), (257, 272, 1536)]
+
+
+@pytest.mark.parametrize("tile", [(16, 16), (17, 16), (18, 16), (19, 16)])
+@pytest.mark.parametrize("M,N,K", W4_SHAPES)
+def test_four_wave_kernel(M, N, K, tile):
+    g = np.random.default_rng(M + N + K)
+    xf = g.standard_normal((M, K)).astype(np.float32)
+    xf[:, g.choice(K, 5, replace=False)] *= 40.0                     # outlier channels
+    x = synth.bf16_bits(xf)
+    w = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    b = synth.bf16_bits((g.standard_normal(N) * 0.01).astype(np.float32)) if M % 2 == 0 else None
+    banner("four-wave tile", tile, M, N, K, "bias" if b is not None else "no bias")
+    mxfp8.set_tile_config(*tile)
+    try:
+        _full_check(x, w, 0, b, name="w4-%d-%d-%d-%d" % (M, N, K, tile[0]))
+    finally:
+        mxfp8.set_tile_config(0, 0)
+
+
 # Small-M (decode) paths.  M <= 16: one launch with the activation quantizer fused into the
 # GEMM and K split over the 8 waves of a workgroup; K values give idle waves (K = 384), partial
 # 4-step groups (K = 640, 1152, 3968) and a wave with two groups, the second partial (K = 4224).

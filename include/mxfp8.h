@@ -260,9 +260,13 @@ int mxfp8_set_batch_invariant(int on);
 
 
 /* Tuning / testing hook: force the tile of the LDS-tiled GEMM used for large M.
- *   (fn, fm) in (8,4) (7,4) (6,4) (4,4) (4,2): the eight-wave kernel, fn, fm = 16-row weight
- *     fragments and 16-row activation groups per wave; the workgroup covers 32 fn weight rows
- *     x 64 fm activation rows;
+ *   (fn, fm) in (8,4) (7,4) (6,4) (4,4) (4,2): the eight-wave kernel with all waves in step,
+ *     fn, fm = 16-row weight fragments and 16-row activation groups per wave; the workgroup
+ *     covers 32 fn weight rows x 64 fm activation rows;
+ *   (7,36) (6,36) (4,36): the eight-wave ping-pong kernel (two groups of four waves taking
+ *     turns between MFMAs and operand reads; E4M3 weights and activations and K % 512 == 0
+ *     only, other layers keep the automatic choice) with the tile of (fn, 4).  The automatic
+ *     choice runs it wherever it picks one of these tiles and the layer qualifies;
  *   (16,16) (17,16) (18,16) (19,16): the four-wave kernel (one wave per SIMD, 32x32x64 scaled
  *     MFMAs, E4M3 weights and K % 512 == 0 only; other layers keep the automatic choice), with
  *     workgroup tiles 256 x 256, 224 x 256, 192 x 256 and 256 x 128 (weight rows x activation

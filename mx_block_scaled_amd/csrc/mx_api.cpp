@@ -495,7 +495,7 @@ int mxfp8_set_batch_invariant(int on) {
 }
 
 int mxfp8_set_tile_config(int fn, int fm) {
-  static const int ok_cfg[][2] = {{0, 0}, {8, 4}, {7, 4}, {6, 4}, {4, 4}, {4, 2}, {16, 16}, {17, 16}, {18, 16}, {19, 16}};
+  static const int ok_cfg[][2] = {{0, 0}, {8, 4}, {7, 4}, {6, 4}, {4, 4}, {4, 2}, {16, 16}, {17, 16}, {18, 16}, {19, 16}, {4, 36}, {6, 36}, {7, 36}};
   for (const auto& c : ok_cfg)
     if (c[0] == fn && c[1] == fm) {
       mx::force_tile(fn, fm);

@@ -287,6 +287,46 @@ __device__ __forceinline__ void wait_vm_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Epilogue of the eight-wave kernels: bias, bf16 rounding, through LDS as a row-major [BM][BN]
+// tile (rows padded by 16 B so the 8-byte writes of a wave hit distinct banks), then 16-byte
+// coalesced stores.  Lane holds n = 16 (wn FN + i) + 4 g + (0..3) of activation row
+// wm 16 FM + 16 j + r.  The caller has finished with the LDS stages (all copies landed, all
+// waves past a barrier) and given the last MFMAs their result latency.
+template <class C, int FN, int FM>
+__device__ __forceinline__ void store_tile(uint8_t* lds, const v4f (&acc)[FN][FM],
+                                           const uint16_t* __restrict__ bias,
+                                           uint16_t* __restrict__ y, int M, int N, int m0, int n0,
+                                           int wn, int wm, int r, int g, int tid) {
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    const int nl = wn * 16 * FN + 16 * i + 4 * g;
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias && n0 + nl < N) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) bv[e] = bf16_to_float(bias[n0 + nl + e]);
+    }
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      const int ml = wm * 16 * FM + 16 * j + r;
+      const v2i o = {(int)pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]),
+                     (int)pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3])};
+      *(v2i*)(lds + ml * C::OUT_PITCH + nl * 2) = o;
+    }
+  }
+  __syncthreads();
+  // non-temporal stores: the output streams out instead of displacing the operand panels that
+  // the running tiles still read from the caches (about 8 % on the prefill GEMM with operands
+  // and outputs rotated over more memory than the Infinity Cache holds)
+  constexpr int ROW_PIECES = C::BN * 2 / 16;          // 16-byte pieces per tile row
+#pragma unroll 4
+  for (int p = tid; p < C::BM * ROW_PIECES; p += C::NW * 64) {
+    const int ml = p / ROW_PIECES, cp = p - ml * ROW_PIECES;
+    const int m = m0 + ml, n = n0 + cp * 8;
+    if (m < M && n < N)
+      __builtin_nontemporal_store(*(const v4i*)(lds + ml * C::OUT_PITCH + cp * 16), (v4i*)(y + (int64_t)m * N + n));
+  }
+}
+
 template <int WFMT, int XFMT, int FN, int FM, int S>
 __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict__ xq,
                                                       const uint8_t* __restrict__ xs, int M, int K,
@@ -616,37 +656,332 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     return;
   }
 
-  // ---- epilogue: bias, bf16 rounding, through LDS as a row-major [BM][BN] tile (rows padded
-  // by 16 B so the 8-byte writes of a wave hit distinct banks), then 16-byte coalesced stores.
-  // Lane holds n = 16 (wn FN + i) + 4 g + (0..3) of activation row wm 16 FM + 16 j + r.
+  store_tile<C, FN, FM>(lds, acc, bias, y, M, N, m0, n0, wn, wm, r, g, tid);
+}
+
+// ---------------------------------------------------------------- ping-pong kernel
+// The eight waves of k_gemm_tile's geometry as two groups of four, one wave of each group per
+// SIMD (waves w and w + 4 share a SIMD): group 0 (waves 0-3) owns the tile's activation rows
+// 0 .. BM/2 - 1, group 1 the rest, each group's four waves splitting its rows 2 (n) x 2 (m).  The
+// groups run half a K step apart: in each phase one group issues all MFMAs of a K step from
+// registers while the other reads its next step's operands from LDS into registers and issues
+// copies; a workgroup barrier ends each phase.  A SIMD's matrix pipe is then fed by one wave at
+// a time and never waits on LDS latency, and each wave's memory work runs under its partner's
+// MFMAs (the all-waves-in-step kernel spends a fifth of its wave time waiting at the barrier and
+// on the first operand reads of each step).
+//
+// Phases, for K step k: in phase 2k group 0 computes step k and group 1 reads it; in phase
+// 2k + 1 group 1 computes step k and group 0 reads step k + 1.  LDS holds three weight stages
+// and two activation stages (step k in weight stage k % 3, activation stage k % 2) and one
+// buffer of group scales.  The copies go out from the computing waves, one after every few
+// MFMAs, so that the L1 (64 B/clk per CU, about 18 clocks per 1 KiB copy) never backs up and
+// a read phase is LDS reads alone: in phase 2k group 0 copies its activation rows and its
+// share of the weight tile of step k + 2, in phase 2k + 1 group 1 its activation rows of step
+// k + 2 and its weight share of step k + 3, each into a stage whose readers are done, each
+// with at least two and a half phases to land.  A wave waits for its copies of a phase by the
+// end of its next phase but one; the barriers then publish them.  Past the last step the last
+// step is copied again, unused, so that every wait count is a constant.  Group 0 copies the
+// scales of the next four-step group in a read phase once both groups have read the current
+// one.  K % 512 == 0 (whole scale groups); results equal k_gemm_tile's bit for bit (the same
+// MFMAs, each accumulator taking the K steps in order).
+template <int WFMT, int XFMT, int FN, int FM>
+struct PPCfg {
+  using C = TileCfg<WFMT, XFMT, FN, FM, 2>;
+  static constexpr int GW = 4;                                           // waves per group
+  static constexpr int A_PW0 = (C::A_CHUNKS + 2 * GW - 1) / (2 * GW);    // weight chunks per wave
+  static constexpr int A_PW1 = (C::A_CHUNKS - GW * A_PW0 + GW - 1) / GW; // (surplus -> scratch)
+  static constexpr int A_PWM = A_PW0 > A_PW1 ? A_PW0 : A_PW1;
+  static constexpr int B_PW = C::B_BYTES / 1024 / (2 * GW);              // activation chunks per wave
+  static constexpr int SA_PW = (C::SA_PIECES + GW - 1) / GW, SB_PW = (C::SB_PIECES + GW - 1) / GW;
+  static constexpr int OFF_B = 3 * C::A_BYTES;
+  static constexpr int OFF_S = OFF_B + 2 * C::B_BYTES;
+  static constexpr int OFF_SCR = OFF_S + C::SCALE_BYTES;
+  static constexpr int LDS_MAIN = OFF_SCR + 1024;
+  static constexpr int LDS_BYTES = LDS_MAIN > C::BM * C::OUT_PITCH ? LDS_MAIN : C::BM * C::OUT_PITCH;
+  static_assert(LDS_BYTES <= 160 * 1024, "must fit the 160 KiB LDS");
+  static_assert(C::B_BYTES % (2048 * GW) == 0, "each group copies its own activation rows");
+  static_assert(GW * (A_PW0 + A_PW1) >= C::A_CHUNKS, "weight chunk split");
+  static_assert(B_PW + A_PWM + SA_PW + SB_PW <= 63, "vmcnt is a 6-bit counter");
+};
+
+// s_waitcnt vmcnt(VM) lgkmcnt(0) (VM = 63: no vector-memory wait), then the workgroup barrier;
+// the empty assembly statements keep the compiler from moving LDS accesses across it
+template <int VM>
+__device__ __forceinline__ void pp_wait_barrier() {
+  static_assert(VM >= 0 && VM <= 63, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | (0 << 8) | ((VM >> 4) << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int WFMT, int XFMT, int FN, int FM>
+__global__ __launch_bounds__(512, 2) void k_gemm_pp(const uint8_t* __restrict__ xq,
+                                                    const uint8_t* __restrict__ xs, int M, int K,
+                                                    const uint8_t* __restrict__ packed, int N,
+                                                    const uint16_t* __restrict__ bias,
+                                                    uint16_t* __restrict__ y, int tiles_m,
+                                                    int tiles_n, int group_m, BatchStrides bs) {
+  using C = TileCfg<WFMT, XFMT, FN, FM, 2>;
+  using P = PPCfg<WFMT, XFMT, FN, FM>;
+  constexpr int GW = P::GW;
+  MX_BATCH_OFFSET(blockIdx.y);
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[P::LDS_BYTES];
+  uint8_t* const lds_b = lds + P::OFF_B;
+  uint8_t* const slds = lds + P::OFF_S;
+  uint8_t* const scratch = lds + P::OFF_SCR;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+  const int r = lane & 15, g = lane >> 4;
+  const bool g1 = wave >= GW;                             // wave-uniform
+  const int w4 = wave & (GW - 1);
+
+  // tile of this workgroup: as k_gemm_tile (XCD-contiguous ranges, group_m row tiles per group)
+  const int T = tiles_m * tiles_n;
+  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const int t = xcd * (T >> 3) + (xcd < (T & 7) ? xcd : (T & 7)) + slot;
+  const int gsz = group_m * tiles_n;
+  const int first_m = (t / gsz) * group_m;
+  const int gm = min(tiles_m - first_m, group_m);
+  const int tm = first_m + (t % gsz) % gm;
+  const int tn = (t % gsz) / gm;
+  const int n0 = tn * C::BN, m0 = tm * C::BM;
+
+  const int NG = N >> 4, KB = K >> 5, KT = K >> 7, G = KT >> 2;
+  const int LDX = KT * C::XB;
+  const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * C::FB);
+
+  // copy sources (32-bit offsets from uniform bases, as in k_gemm_tile).  Weight chunks: group 0
+  // wave w takes chunks w, w + 4, .. below 4 A_PW0, group 1 wave 4 + w the chunks 4 A_PW0 + w, ..
+  // (surplus slots to the scratch area).  Activation chunks (8 rows each): each group its rows.
+  const int a_c0 = g1 ? GW * P::A_PW0 : 0;
+  const int a_cend = g1 ? C::A_CHUNKS : GW * P::A_PW0;
+  uint32_t a_off[P::A_PWM];
 #pragma unroll
-  for (int i = 0; i < FN; ++i) {
-    const int nl = wn * 16 * FN + 16 * i + 4 * g;
-    float bv[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias && n0 + nl < N) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) bv[e] = bf16_to_float(bias[n0 + nl + e]);
+  for (int i = 0; i < P::A_PWM; ++i) {
+    const int c = min(a_c0 + w4 + GW * i, C::A_CHUNKS - 1);
+    if (C::FB % 1024 == 0) {
+      const int f = c * 1024 / C::FB;
+      a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (c * 1024 - f * C::FB));
+    } else {
+      const int off = c * 1024 + lane * 16;
+      const int f = off / C::FB;
+      a_off[i] = (uint32_t)(min((n0 >> 4) + f, NG - 1) * C::FB + (off - f * C::FB));
     }
+  }
+  const uint32_t a_lane = C::FB % 1024 == 0 ? (uint32_t)lane * 16 : 0u;
+  const int cb0 = g1 ? C::B_BYTES / 2048 : 0;             // first activation chunk of the group
+  uint32_t b_off[P::B_PW];
+  bool b_on[P::B_PW];
+#pragma unroll
+  for (int i = 0; i < P::B_PW; ++i) {
+    const int row = 8 * (cb0 + w4 + GW * i) + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    b_on[i] = chunk < C::XB / 16;
+    b_off[i] = (uint32_t)(min(m0 + row, M - 1) * LDX + min(chunk, C::XB / 16 - 1) * 16);
+  }
+  // copy i of this wave's weight share of step kt into weight stage `stage`
+  auto copy_a = [&](int i, int kt, int stage) __attribute__((always_inline)) {
+    const int c = a_c0 + w4 + GW * i;   // wave-uniform
+    dma16(packed + (uint32_t)(kt * NG * C::FB + a_off[i] + a_lane),
+          c < a_cend ? lds + stage * C::A_BYTES + c * 1024 : scratch);
+  };
+  // copy i of this wave's activation rows of step kt into activation stage `stage`
+  auto copy_b = [&](int i, int kt, int stage) __attribute__((always_inline)) {
+    if (XFMT == 0 || b_on[i])
+      dma16(xq + (uint32_t)(kt * C::XB + b_off[i]), lds_b + stage * C::B_BYTES + (cb0 + w4 + GW * i) * 1024);
+  };
+  // scale copies (group 0): weight words 4 fragments per 16-byte copy, activation rows 16 per
+  // 4-byte copy, as k_gemm_tile
+  uint32_t sa_src[P::SA_PW], sb_src[P::SB_PW];
+#pragma unroll
+  for (int i = 0; i < P::SA_PW; ++i) {
+    const int c = min(w4 + GW * i, C::SA_PIECES - 1);
+    sa_src[i] = (uint32_t)(min((n0 >> 4) + 4 * c + (lane >> 4), NG - 1) * 256 + (lane & 15) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < P::SB_PW; ++i) {
+    const int c = min(w4 + GW * i, C::SB_PIECES - 1);
+    sb_src[i] = (uint32_t)(min(m0 + 16 * c + (lane >> 2), M - 1) * KB);
+  }
+  const int q4 = (lane & 3) * 4;
+  auto issue_scales = [&](int kt4) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < P::SA_PW; ++i) {
+      const int c = w4 + GW * i;
+      dma16((const uint8_t*)wsc + (uint32_t)(kt4 * NG * 256 + sa_src[i]),
+            c < C::SA_PIECES ? slds + c * 1024 : scratch);
+    }
+#pragma unroll
+    for (int i = 0; i < P::SB_PW; ++i) {
+      const int c = w4 + GW * i;
+      dma4(xs + (uint32_t)(sb_src[i] + 16 * kt4 + q4), c < C::SB_PIECES ? slds + C::SA_BYTES + c * 256 : scratch);
+    }
+  };
+
+  typedef typename AReg<WFMT>::type AR;
+  typedef typename AReg<XFMT>::type BR;
+  AR a[FN];
+  BR b[FM];
+  uint32_t sa[FN], sb[FM];
+  const uint32_t psel = (uint32_t)g | ((uint32_t)(4 + g) << 8) | ((uint32_t)g << 16) | ((uint32_t)(4 + g) << 24);
+  auto read_scales = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) sa[i] = *(const uint32_t*)(slds + (wn * FN + i) * 256 + lane * 4);
 #pragma unroll
     for (int j = 0; j < FM; ++j) {
-      const int ml = wm * 16 * FM + 16 * j + r;
-      const v2i o = {(int)pack_bf16x2(acc[i][j][0] + bv[0], acc[i][j][1] + bv[1]),
-                     (int)pack_bf16x2(acc[i][j][2] + bv[2], acc[i][j][3] + bv[3])};
-      *(v2i*)(lds + ml * C::OUT_PITCH + nl * 2) = o;
+      const v4i w = *(const v4i*)(slds + C::SA_BYTES + (wm * 16 * FM + 16 * j + r) * 16);
+      const uint32_t t01 = __builtin_amdgcn_perm((uint32_t)w[1], (uint32_t)w[0], psel);
+      const uint32_t t23 = __builtin_amdgcn_perm((uint32_t)w[3], (uint32_t)w[2], psel);
+      sb[j] = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+    }
+  };
+  const uint32_t b_lo = (uint32_t)((wm * 16 * FM + r) * 128 + ((g ^ swz(r)) << 4));
+  const uint32_t b_hi = (uint32_t)((wm * 16 * FM + r) * 128 + (((4 + g) ^ swz(r)) << 4));
+  const bool godd = (g & 1) != 0;
+  const int c_full = (3 * g + 1) >> 1, c_half = godd ? c_full - 1 : c_full + 1;
+  const uint32_t bx_off = (uint32_t)((wm * 16 * FM + r) * 128 + ((c_full ^ swz(r)) << 4));
+  const uint32_t by_off = (uint32_t)((wm * 16 * FM + r) * 128 + ((c_half ^ swz(r)) << 4) + (godd ? 8 : 0));
+  // all operands of one K step into registers
+  auto read_ops = [&](int astage, int bstage) __attribute__((always_inline)) {
+    const uint8_t* base = lds + astage * C::A_BYTES;
+    const uint8_t* bl = lds_b + bstage * C::B_BYTES;
+#pragma unroll
+    for (int j = 0; j < FM; ++j)
+      b[j] = lds_b_operand<XFMT>(bl + (XFMT == 0 ? b_lo : bx_off) + j * 2048,
+                                 bl + (XFMT == 0 ? b_hi : by_off) + j * 2048, godd);
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      const uint8_t* fa = base + (wn * FN + i) * C::FB;
+      const v4i lo = *(const v4i*)(fa + lane * 16);
+      if constexpr (WFMT == 0) {
+        const v4i hi = *(const v4i*)(fa + 1024 + lane * 16);
+        a[i] = (AR){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      } else {
+        const v2i hi = *(const v2i*)(fa + 1024 + lane * 8);
+        a[i] = (AR){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1]};
+      }
+    }
+  };
+
+  v4f acc[FN][FM];
+#pragma unroll
+  for (int i = 0; i < FN; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+  // one K step's MFMAs with ND copies interleaved: copy c (copy(c) issues it) after MFMA
+  // number 1 + c * SPACE, spread over the step
+  auto compute = [&](auto qc, auto nd, auto&& copy) __attribute__((always_inline)) {
+    constexpr int Q = decltype(qc)::value;
+    constexpr int ND = decltype(nd)::value;
+    constexpr int SPACE = (FN * FM - 1) / (ND > 1 ? ND : 1) > 0 ? (FN * FM - 1) / (ND > 1 ? ND : 1) : 1;
+    // the scale words were written by VALU code before the last barrier; two wait states
+    asm volatile("s_nop 1" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+      for (int j = 0; j < FM; ++j) {
+        mfma_inplace<WFMT, XFMT, Q>(acc[i][j], a[i], b[j], sa[i], sb[j]);
+        const int mm = i * FM + j;   // a constant once unrolled
+        if ((mm - 1) % SPACE == 0 && (mm - 1) / SPACE < ND && mm >= 1) {
+          __builtin_amdgcn_sched_barrier(0);
+          copy((mm - 1) / SPACE);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+  };
+  const std::integral_constant<int, P::B_PW + P::A_PW0> nd0;
+  const std::integral_constant<int, P::B_PW + P::A_PW1> nd1;
+  const int KL = KT - 1;
+
+  // prologue: steps 0 and 1, group 1's weight share of step 2 and scale group 0
+  if (!g1) {
+    issue_scales(0);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int i = 0; i < P::B_PW; ++i) copy_b(i, min(st, KL), st);
+#pragma unroll
+      for (int i = 0; i < P::A_PW0; ++i) copy_a(i, min(st, KL), st);
+    }
+  } else {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int i = 0; i < P::B_PW; ++i) copy_b(i, min(st, KL), st);
+    }
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+#pragma unroll
+      for (int i = 0; i < P::A_PW1; ++i) copy_a(i, min(st, KL), st);
     }
   }
-  __syncthreads();
-  // non-temporal stores: the output streams out instead of displacing the operand panels that
-  // the running tiles still read from the caches (about 8 % on the prefill GEMM with operands
-  // and outputs rotated over more memory than the Infinity Cache holds)
-  constexpr int ROW_PIECES = C::BN * 2 / 16;          // 16-byte pieces per tile row
-#pragma unroll 4
-  for (int p = tid; p < C::BM * ROW_PIECES; p += C::NW * 64) {
-    const int ml = p / ROW_PIECES, cp = p - ml * ROW_PIECES;
-    const int m = m0 + ml, n = n0 + cp * 8;
-    if (m < M && n < N)
-      __builtin_nontemporal_store(*(const v4i*)(lds + ml * C::OUT_PITCH + cp * 16), (v4i*)(y + (int64_t)m * N + n));
+  pp_wait_barrier<0>();
+  // Each group runs its own loop (the branch is wave-uniform); both pass the same barriers, two
+  // per K step, so the phases line up across the groups.
+  if (!g1) {
+    read_ops(0, 0);                       // phase -1: read step 0
+    read_scales();
+    pp_wait_barrier<63>();
+    // phase 2 kt: compute step kt, copying group 0's activation rows and weight share of step
+    // kt + 2; phase 2 kt + 1: read step kt + 1 (at a group's last step with the next group's
+    // scales) and, at a group's first step, copy the next group's scales
+    auto step = [&](int kt, auto qc) __attribute__((always_inline)) {
+      constexpr int Q = decltype(qc)::value;
+      const int k2 = min(kt + 2, KL);
+      compute(qc, nd0, [&](int c) __attribute__((always_inline)) {
+        if (c < P::B_PW) copy_b(c, k2, kt & 1);
+        else copy_a(c - P::B_PW, k2, (kt + 2) % 3);
+      });
+      pp_wait_barrier<P::B_PW + P::A_PW0>();   // copies of two phases ago (step kt + 1)
+      if (kt + 1 < KT) {
+        read_ops((kt + 1) % 3, (kt + 1) & 1);
+        if (Q == 3) read_scales();
+      }
+      if (Q == 0 && (kt >> 2) + 1 < G) issue_scales((kt >> 2) + 1);
+      pp_wait_barrier<63>();
+    };
+    for (int kt = 0; kt < KT; kt += 4) {
+      step(kt + 0, std::integral_constant<int, 0>());
+      step(kt + 1, std::integral_constant<int, 1>());
+      step(kt + 2, std::integral_constant<int, 2>());
+      step(kt + 3, std::integral_constant<int, 3>());
+    }
+  } else {
+    pp_wait_barrier<63>();                // phase -1: nothing to read yet
+    // phase 2 kt: read step kt (at a group's first step with its scales); phase 2 kt + 1:
+    // compute step kt, copying group 1's activation rows of step kt + 2 and its weight share of
+    // step kt + 3
+    auto step = [&](int kt, auto qc) __attribute__((always_inline)) {
+      constexpr int Q = decltype(qc)::value;
+      read_ops(kt % 3, kt & 1);
+      if (Q == 0) read_scales();
+      pp_wait_barrier<P::B_PW + P::A_PW1>();   // copies of three phases ago (weight of kt + 1)
+      const int k2 = min(kt + 2, KL), k3 = min(kt + 3, KL);
+      compute(qc, nd1, [&](int c) __attribute__((always_inline)) {
+        if (c < P::B_PW) copy_b(c, k2, kt & 1);
+        else copy_a(c - P::B_PW, k3, kt % 3);
+      });
+      pp_wait_barrier<P::B_PW + P::A_PW1>();   // copies of two phases ago (activations of kt + 1)
+    };
+    for (int kt = 0; kt < KT; kt += 4) {
+      step(kt + 0, std::integral_constant<int, 0>());
+      step(kt + 1, std::integral_constant<int, 1>());
+      step(kt + 2, std::integral_constant<int, 2>());
+      step(kt + 3, std::integral_constant<int, 3>());
+    }
   }
+  // every copy landed and every wave done with the stages before LDS takes the output tile; the
+  // nops give the last MFMAs (assembly, so untracked by the compiler's hazard checks) their
+  // result latency before VALU code reads the accumulators
+  pp_wait_barrier<0>();
+  asm volatile("s_nop 15\n s_nop 15\n s_nop 15" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  store_tile<C, FN, FM>(lds, acc, bias, y, M, N, m0, n0, wn, wm, r, g, tid);
 }
 
 // ---------------------------------------------------------------- 4-wave kernel (large tiles)
@@ -1026,6 +1361,16 @@ static void launch_w4(const uint8_t* xq, const uint8_t* xs, int M, int K, const 
 }
 
 
+template <int WFMT, int XFMT, int FN, int FM>
+static void launch_pp(const uint8_t* xq, const uint8_t* xs, int M, int K, const uint8_t* packed,
+                      int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s,
+                      int batch, const BatchStrides& bs) {
+  using C = TileCfg<WFMT, XFMT, FN, FM, 2>;
+  const int tm = (M + C::BM - 1) / C::BM, tn = (N + C::BN - 1) / C::BN;
+  hipLaunchKernelGGL((k_gemm_pp<WFMT, XFMT, FN, FM>), dim3((unsigned)(tm * tn), (unsigned)batch),
+                     dim3(512), 0, s, xq, xs, M, K, packed, N, bias, y, tm, tn, group_m, bs);
+}
+
 template <int WFMT, int XFMT, int FN, int FM, int S>
 static void launch_tile(const uint8_t* xq, const uint8_t* xs, int M, int K, const uint8_t* packed,
                         int N, const uint16_t* bias, uint16_t* y, int group_m, hipStream_t s,
@@ -1098,7 +1443,7 @@ bool batch_invariant() { return g_batch_invariant.load(std::memory_order_relaxed
 static TileChoice choose_tile(int M, int N, int batch, bool w4_ok) {
   const int f = g_force_tile.load(std::memory_order_relaxed);
   // a forced four-wave tile (fm == 16) applies only where that kernel does
-  if (f && (f % 256 != 16 || w4_ok)) return TileChoice{f / 256, f % 256};
+  if (f && ((f % 256 != 16 && f % 256 != 36) || w4_ok)) return TileChoice{f / 256, f % 256};
   static const TileChoice opts[] = {{8, 4}, {7, 4}, {6, 4}, {4, 4}, {4, 2}};
   double best = 1e30;
   TileChoice pick = opts[0];
@@ -1131,6 +1476,17 @@ static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int 
   }
   const TileChoice c = choose_tile(M, N, batch, WFMT == 0 && XFMT == 0 && K % 512 == 0);
   if constexpr (WFMT == 0 && XFMT == 0) {
+    // the ping-pong kernel wherever it applies (E4M3 operands, whole scale groups): chosen
+    // tiles 224 x 256, 192 x 256 and 128 x 256, or forced as (fn, 36); a forced (fn, 4) keeps
+    // the all-waves-in-step kernel
+    const int f = g_force_tile.load(std::memory_order_relaxed);
+    const bool pp_tile = c.fm == 36 || (f == 0 && c.fm == 4 && (c.fn == 7 || c.fn == 6 || c.fn == 4));
+    if (pp_tile && K % 512 == 0) {
+      if (c.fn == 6) launch_pp<0, 0, 6, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+      else if (c.fn == 4) launch_pp<0, 0, 4, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+      else launch_pp<0, 0, 7, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);
+      return hipGetLastError();
+    }
     // the four-wave kernel, by the tile override only (tuning and tests): measured slower than
     // the eight-wave kernel on the prefill and outlier shapes (195 - 210 against 183 - 191 us;
     // 56 - 60 against 54 us)

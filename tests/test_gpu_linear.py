@@ -222,6 +222,31 @@ def test_four_wave_kernel(M, N, K, tile):
         mxfp8.set_tile_config(0, 0)
 
 
+# The ping-pong kernel (two groups of four waves taking turns between MFMAs and operand reads;
+# E4M3 weights and activations, K % 512 == 0), each of its tiles (forced: 224 x 256, 192 x 256
+# and 128 x 256): against the oracle, and bit-equal to the all-waves-in-step kernel of the same
+# tile, which issues the same MFMAs in the same order per accumulator.
+@pytest.mark.parametrize("tile", [(7, 36), (6, 36), (4, 36)])
+@pytest.mark.parametrize("M,N,K", W4_SHAPES)
+def test_ping_pong_kernel(M, N, K, tile):
+    g = np.random.default_rng(M * 3 + N + K + tile[0])
+    xf = g.standard_normal((M, K)).astype(np.float32)
+    xf[:, g.choice(K, 5, replace=False)] *= 40.0                     # outlier channels
+    x = synth.bf16_bits(xf)
+    w = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    b = synth.bf16_bits((g.standard_normal(N) * 0.01).astype(np.float32)) if M % 2 == 0 else None
+    banner("ping-pong tile", tile, M, N, K, "bias" if b is not None else "no bias")
+    mxfp8.set_tile_config(*tile)
+    try:
+        y, layer = _full_check(x, w, 0, b, name="pp-%d-%d-%d-%d" % (M, N, K, tile[0]))
+        mxfp8.set_tile_config(tile[0], 4)
+        y2 = layer(bf16_dev(x))
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    finally:
+        mxfp8.set_tile_config(0, 0)
+
+
 # Small-M (decode) paths.  M <= 16: one launch with the activation quantizer fused into the
 # GEMM and K split over the 8 waves of a workgroup; K values give idle waves (K = 384), partial
 # 4-step groups (K = 640, 1152, 3968) and a wave with two groups, the second partial (K = 4224).

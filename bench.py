@@ -431,7 +431,7 @@ def main():
         "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_FP8_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP8_TFLOPS, 4),
         "traffic": _traffic("gemm_prefill"),
-        "kernel": "k_gemm_tile (pre-quantized entry), %dx%dx%d" % (M, N, K),
+        "kernel": "k_gemm_pp<0, 0, 7, 4> (pre-quantized entry), %dx%dx%d" % (M, N, K),
         "kernel_us": round(gemm_us, 2), "kernel_us_min": round(gemm_us_min, 2),
         "timing": "HIP events on the launch stream, median of 5 loops of 100 launches",
         "algorithmic_flop_per_launch": flop,

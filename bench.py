@@ -95,7 +95,39 @@ def _peaks_lib():
     L.mxpk_mfma_chains.restype, L.mxpk_mfma_chains.argtypes = I, []
     L.mxpk_stream_read.restype, L.mxpk_stream_read.argtypes = I, [P, I64, I, I, P, P]
     L.mxpk_clock_probe.restype, L.mxpk_clock_probe.argtypes = I, [I64, P, P]
+    L.mxpk_lds_read.restype, L.mxpk_lds_read.argtypes = I, [I, I, I, I, P, P, P]
+    L.mxpk_l1_copy.restype, L.mxpk_l1_copy.argtypes = I, [I, P, I, I, I, P, P, P]
     return L
+
+
+def cu_rates(L):
+    """Per-CU data rates of one workgroup per CU (256 workgroups), in bytes per shader clock of
+    block 0's loop: LDS reads (16- and 8-byte lanes, 4 / 8 / 16 waves) and global -> CU copies
+    from an L2-resident 256 KiB window (16-byte direct-to-LDS, 16-byte into registers, 4-byte
+    direct-to-LDS; 16 waves)."""
+    import torch
+    st = torch.cuda.current_stream().cuda_stream
+    out = torch.zeros(4, dtype=torch.int32, device="cuda")
+    clk = torch.zeros(2, dtype=torch.int64, device="cuda")
+    res = {"lds_read_B_per_clk": {}, "l1_copy_B_per_clk": {}}
+    iters = 2000
+    for width in (16, 8):
+        for threads in (256, 512, 1024):
+            for _ in range(2):
+                assert L.mxpk_lds_read(width, threads, 256, iters, out.data_ptr(), clk.data_ptr(), st) == 0
+            torch.cuda.synchronize()
+            cyc = clk.cpu().tolist()[0]
+            key = "b%d_%dwaves" % (width * 8, threads // 64)
+            res["lds_read_B_per_clk"][key] = round(threads * iters * 8 * width / cyc, 1) if cyc else None
+    src = torch.full((512 << 10,), 1, dtype=torch.uint8, device="cuda")
+    for mode, name, width in ((0, "lds_dma_16B", 16), (1, "vgpr_16B", 16), (2, "lds_dma_4B", 4)):
+        for _ in range(2):
+            assert L.mxpk_l1_copy(mode, src.data_ptr(), 1024, 256, iters, out.data_ptr(), clk.data_ptr(), st) == 0
+        torch.cuda.synchronize()
+        cyc = clk.cpu().tolist()[0]
+        res["l1_copy_B_per_clk"][name + "_16waves"] = round(1024 * iters * 8 * width / cyc, 1) if cyc else None
+    del src
+    return res
 
 
 def clock_under(L, fn, calls, probe_ms):
@@ -199,7 +231,7 @@ def stream_read_us(L, nbytes, sets=None, reps=20, configs=None):
 
 def measure_peaks(full=False):
     """Attainable peaks of the running chip: MFMA loops (4 and 8 waves per SIMD, the better
-    one) and plain HBM reads (the best launch shape)."""
+    one), plain HBM reads (the best launch shape) and the per-CU LDS and L1 rates."""
     L = _peaks_lib()
     res = {"mfma_TFLOPs": {}, "mfma_clock_MHz": {}}
     for name, af, bf in (("fp8xfp8", 0, 0), ("fp8xfp6", 0, 2), ("fp6xfp6", 2, 2),
@@ -216,6 +248,7 @@ def measure_peaks(full=False):
                                                     "GB/s": round(b / us / 1e3, 1),
                                                     "unroll": unroll, "blocks": blocks}
     res["hbm_GBs"] = res["stream_read"]["1024MiB"]["GB/s"]
+    res["per_CU"] = cu_rates(L)
     return res, L
 
 

@@ -9,6 +9,11 @@
 //  * mxpk_stream_read: a read of n bytes (16-byte loads, a few in flight per lane) whose words
 //    are folded into a value that is stored only in a case that never occurs, so the loads
 //    cannot be dropped and nothing is written.
+//  * mxpk_lds_read: LDS read bandwidth of one workgroup per CU: every wave keeps eight 16-byte
+//    (or 8-byte) reads per lane in flight from conflict-free addresses of a 64 KiB buffer.
+//  * mxpk_l1_copy: global -> CU bandwidth of one workgroup per CU reading a 256 KiB window that
+//    stays in the L2: 16-byte direct-to-LDS loads, 16-byte loads into registers, or 4-byte
+//    direct-to-LDS loads, eight per wave in flight.
 //
 // All are plain launches on the caller's stream; timing is the caller's (HIP events).
 #include <hip/hip_runtime.h>
@@ -181,6 +186,71 @@ __global__ void __launch_bounds__(64) k_clock_probe(uint64_t ticks, uint64_t* ou
   }
 }
 
+// LDS reads: W = 16 (ds_read_b128) or 8 (ds_read_b64); each wave reads 1 KiB windows of a 64 KiB
+// buffer, eight in flight, then waits; clk: block 0's shader-clock cycles over the loop
+template <int W>
+__global__ void __launch_bounds__(1024) k_lds_read(int iters, int* out, uint64_t* clk) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[65536];
+  const int t = threadIdx.x, wv = t >> 6, l = t & 63;
+  for (int i = t; i < 65536 / 4; i += blockDim.x) ((int*)lds)[i] = i * 2654435761u;
+  __syncthreads();
+  const uint64_t c0 = shader_clock();
+  int acc = 0;
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t base = (uint32_t)(uintptr_t)lds;
+  for (int it = 0; it < iters; ++it) {
+    int v[8][4];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t off = base + ((wv * 8 + u + it) & 63) * 1024 + l * W;   // < 64 KiB
+      if (W == 16) asm volatile("ds_read_b128 %0, %1" : "=v"(*(__attribute__((ext_vector_type(4))) int*)v[u]) : "v"(off));
+      else asm volatile("ds_read_b64 %0, %1" : "=v"(*(__attribute__((ext_vector_type(2))) int*)v[u]) : "v"(off));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ (W == 16 ? v[u][2] ^ v[u][3] : 0);
+  }
+#endif
+  __syncthreads();
+  const uint64_t c1 = shader_clock();
+  if (blockIdx.x == 0 && t == 0 && clk) clk[0] = c1 - c0;
+  if (acc == 0x12345 && out) out[0] = acc;   // data-dependent store that never happens
+}
+
+// global -> CU copies from a 256 KiB window: MODE 0 = 16-byte direct-to-LDS, 1 = 16-byte loads
+// into registers, 2 = 4-byte direct-to-LDS; eight per wave in flight, then a wait
+template <int MODE>
+__global__ void __launch_bounds__(1024) k_l1_copy(const uint8_t* __restrict__ src, int iters,
+                                                 int* out, uint64_t* clk) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[65536];
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int nw = blockDim.x >> 6, slots = 64 / nw;   // 1 KiB LDS slots per wave
+  __syncthreads();
+  const uint64_t c0 = shader_clock();
+  typedef int v4i_t __attribute__((ext_vector_type(4)));
+  v4i_t acc = {0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t off = (uint32_t)((((it * 8 + u) * nw + w + blockIdx.x * 7) & 255) * 1024);
+      void __attribute__((address_space(3)))* dst =
+          (void __attribute__((address_space(3)))*)(lds + (w * slots + (u % slots)) * 1024);
+      if (MODE == 0)
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src + off + l * 16), dst, 16, 0, 0);
+      else if (MODE == 1)
+        acc ^= *(const v4i_t*)(src + off + l * 16);
+      else
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(src + off + l * 4), dst, 4, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0x70 | (0xF << 8));   // vmcnt(0)
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const uint64_t c1 = shader_clock();
+  if (blockIdx.x == 0 && t == 0 && clk) clk[0] = c1 - c0;
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w ^ lds[t]) == 0x12345 && out) out[0] = 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -230,6 +300,36 @@ int mxpk_stream_read(const void* p, int64_t bytes, int blocks, int unroll, uint3
     hipLaunchKernelGGL(k_stream_read<16>, dim3(blocks), dim3(256), 0, s, (const uint4*)p, n16, out);
   else
     return -1;
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// LDS read bandwidth: width 16 or 8 bytes per lane, threads per workgroup a multiple of 64 up
+// to 1024; bytes read per workgroup = threads x iters x 8 x width; clk: block 0's cycles
+int mxpk_lds_read(int width, int threads, int blocks, int iters, int* out, uint64_t* clk,
+                  void* stream) {
+  if ((width != 16 && width != 8) || threads < 64 || threads > 1024 || threads % 64 || blocks <= 0 ||
+      iters <= 0)
+    return -1;
+  hipStream_t s = (hipStream_t)stream;
+  if (width == 16)
+    hipLaunchKernelGGL(k_lds_read<16>, dim3(blocks), dim3(threads), 0, s, iters, out, clk);
+  else
+    hipLaunchKernelGGL(k_lds_read<8>, dim3(blocks), dim3(threads), 0, s, iters, out, clk);
+  return hipGetLastError() == hipSuccess ? 0 : -6;
+}
+
+// global -> CU copy bandwidth from a 256 KiB window of src (src must hold 256 KiB): mode 0 / 1 /
+// 2 as k_l1_copy; threads 256, 512 or 1024; bytes per workgroup = threads x iters x 8 x (16 or 4)
+int mxpk_l1_copy(int mode, const void* src, int threads, int blocks, int iters, int* out,
+                 uint64_t* clk, void* stream) {
+  if (mode < 0 || mode > 2 || !src || (threads != 256 && threads != 512 && threads != 1024) ||
+      blocks <= 0 || iters <= 0)
+    return -1;
+  hipStream_t s = (hipStream_t)stream;
+  const uint8_t* p = (const uint8_t*)src;
+  if (mode == 0) hipLaunchKernelGGL(k_l1_copy<0>, dim3(blocks), dim3(threads), 0, s, p, iters, out, clk);
+  else if (mode == 1) hipLaunchKernelGGL(k_l1_copy<1>, dim3(blocks), dim3(threads), 0, s, p, iters, out, clk);
+  else hipLaunchKernelGGL(k_l1_copy<2>, dim3(blocks), dim3(threads), 0, s, p, iters, out, clk);
   return hipGetLastError() == hipSuccess ? 0 : -6;
 }
 

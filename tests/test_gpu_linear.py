@@ -394,6 +394,34 @@ def test_batched(M, N, K):
     assert ok, rep
 
 
+@pytest.mark.parametrize("tile", [(7, 36), (6, 36), (7, 4)])
+def test_batched_forced_tiles(tile):
+    """The batched layer on the ping-pong kernel's tiles (grid y = batch) and on the
+    all-waves-in-step kernel's: every batch equals a separate call bit for bit."""
+    Bn, M, N, K = 3, 300, 592, 1024
+    g = np.random.default_rng(tile[0] * 100 + tile[1])
+    xs_ = [synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32)) for _ in range(Bn)]
+    ws_ = [synth.bf16_bits((g.standard_normal((N, K)) * 0.03).astype(np.float32)) for _ in range(Bn)]
+    bs_ = [synth.bf16_bits((g.standard_normal(N) * 0.1).astype(np.float32)) for _ in range(Bn)]
+    banner("batched forced tile", tile, Bn, M, N, K)
+    layers = [_layer(ws_[b], 0, bs_[b]) for b in range(Bn)]
+    packed = torch.cat([l[0].packed for l in layers])
+    bias = torch.stack([bf16_dev(bb) for bb in bs_])
+    x = torch.stack([bf16_dev(xx) for xx in xs_])
+    mxfp8.set_tile_config(*tile)
+    try:
+        y = mxfp8.linear_batched(x, packed, N, 0, bias)
+        for b in range(Bn):
+            y1 = layers[b][0](x[b])
+            torch.cuda.synchronize()
+            assert torch.equal(y[b].view(torch.int16), y1.view(torch.int16)), b
+    finally:
+        mxfp8.set_tile_config(0, 0)
+    ref, _, _ = orc.linear_ref(xs_[2], layers[2][1], layers[2][2], 0, bs_[2])
+    ok, rep = tolerance.check(host_bf16_bits(y[2]), ref, name="batched-tile-%d-%d" % tile)
+    assert ok, rep
+
+
 @pytest.mark.parametrize("M", [5, 24, 300])
 def test_bias_at_odd_offset(M):
     """A bias that starts 2 bytes past an 8-byte boundary (a slice of a larger tensor): the

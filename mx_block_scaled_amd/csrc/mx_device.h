@@ -119,6 +119,42 @@ __device__ __forceinline__ uint32_t amax8_bf16(const v4i& v) {
   return m;
 }
 
+// The same as amax8_bf16 with the maxima taken two 16-bit fields at a time (v_pk_max_u16):
+// |bf16| bit patterns compare as unsigned integers in the order of the magnitudes.
+__device__ __forceinline__ uint32_t amax8_bf16_pk(const v4i& v) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 h[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t u = (uint32_t)v[i] & 0x7FFF7FFFu;
+    __builtin_memcpy(&h[i], &u, 4);
+  }
+  const u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(h[0], h[1]),
+                                            __builtin_elementwise_max(h[2], h[3]));
+  return m[0] > m[1] ? (uint32_t)m[0] : (uint32_t)m[1];
+}
+
+// Eight E4M3 codes (two dwords) of the bf16 values of a 16-byte piece, divided by `scale`,
+// RNE, saturated: cvt4_e4m3 twice.  The first convert of each dword writes its low half and
+// the second its high half, so the register's previous contents never reach the result.
+__device__ __forceinline__ v2i cvt8_e4m3(const v4i& v, float scale) {
+  uint32_t u[2];
+#pragma unroll
+  for (int d = 0; d < 2; ++d) {
+    const uint32_t lo = (uint32_t)v[2 * d], hi = (uint32_t)v[2 * d + 1];
+    v2bf a, b;
+    __builtin_memcpy(&a, &lo, 4);
+    __builtin_memcpy(&b, &hi, 4);
+    v2s r = __builtin_nondeterministic_value(r);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, a, scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, b, scale, true);
+    __builtin_memcpy(&u[d], &r, 4);
+    const uint32_t t = ((u[d] & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u;
+    u[d] -= t >> 7;
+  }
+  return (v2i){(int)u[0], (int)u[1]};
+}
+
 // ds_swizzle, bit-mask mode: lane i of each 32-lane half reads lane i ^ 16
 __device__ __forceinline__ uint32_t lane_xor16(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);

@@ -170,17 +170,13 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
       for (int m = 0; m < 16; ++m) {
         if (m < M) {
           const v4i v = xr[m][0][0];
-          const uint32_t e = scale_byte_from_amax<0>(quad_max_u32(amax8_bf16(v)));
-          v2i q;
-          if (e == 0xFFu) {
-            q = (v2i){0x7F7F7F7F, 0x7F7F7F7F};   // block holds Inf/NaN: NaN codes
-          } else {
-            const float sc = e8m0_to_float(e);
-            q = (v2i){(int)cvt4_e4m3((uint32_t)v[0], (uint32_t)v[1], sc),
-                      (int)cvt4_e4m3((uint32_t)v[2], (uint32_t)v[3], sc)};
-          }
+          const uint32_t e = scale_byte_from_amax<0>(quad_max_u32(amax8_bf16_pk(v)));
+          // converted whatever e is (branch-free); a block holding Inf/NaN gets NaN codes
+          v2i q = cvt8_e4m3(v, e8m0_to_float(e));
+          if (e == 0xFFu) q = (v2i){0x7F7F7F7F, 0x7F7F7F7F};
           *(v2i*)(xw + m * kRowPitch + 8 * lane) = q;
-          if ((lane & 3) == 0) sl[wave][m * 16 + (lane >> 2)] = (uint8_t)e;
+          // the four lanes of the block store the same byte
+          sl[wave][m * 16 + (lane >> 2)] = (uint8_t)e;
         }
       }
       // the LDS image is written and read by this wave only: LDS operations of a wave complete

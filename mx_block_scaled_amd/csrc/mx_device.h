@@ -50,6 +50,12 @@ __device__ __forceinline__ float e8m0_to_float(uint32_t byte) {
   return __uint_as_float(byte ? (byte << 23) : 0x00400000u);
 }
 
+// The same value as e8m0_to_float for bytes 0 .. 254 in one instruction: 2^-127 (an fp32
+// subnormal, kept since the kernels run with fp32 subnormals on) times 2^byte.
+__device__ __forceinline__ float e8m0_to_float_ldexp(uint32_t byte) {
+  return __builtin_ldexpf(__uint_as_float(0x00400000u), (int)byte);
+}
+
 // Four E4M3 codes (bytes of the result) from four bf16 values packed in two dwords, divided
 // by `scale` (a power of two), round-to-nearest-even, saturated at +-448.
 __device__ __forceinline__ uint32_t cvt4_e4m3(uint32_t bf_lo, uint32_t bf_hi, float scale) {

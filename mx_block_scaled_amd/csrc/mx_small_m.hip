@@ -172,7 +172,7 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
           const v4i v = xr[m][0][0];
           const uint32_t e = scale_byte_from_amax<0>(quad_max_u32(amax8_bf16_pk(v)));
           // converted whatever e is (branch-free); a block holding Inf/NaN gets NaN codes
-          v2i q = cvt8_e4m3(v, e8m0_to_float(e));
+          v2i q = cvt8_e4m3(v, e8m0_to_float_ldexp(e));
           if (e == 0xFFu) q = (v2i){0x7F7F7F7F, 0x7F7F7F7F};
           *(v2i*)(xw + m * kRowPitch + 8 * lane) = q;
           // the four lanes of the block store the same byte

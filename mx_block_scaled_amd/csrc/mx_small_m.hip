@@ -12,8 +12,11 @@
 //    order is fixed, so results do not depend on timing), then bias, one bf16 rounding, store.
 //  * the weight is read with non-temporal loads: each byte is used once per call, and the hint
 //    keeps it from displacing cached data (about 10 % per call at M = 1, 4096 x 4096).
-// Activations come either as bf16 (M <= 16: quantized inside the kernel, bit-identical to
-// k_quantize_act) or pre-quantized (E4M3 xq + row-major E8M0 xs, M <= 32).
+// Activations come either as bf16 (quantized inside the kernel, bit-identical to
+// k_quantize_act) or pre-quantized (E4M3 xq + row-major E8M0 xs, M <= 32).  For the bf16 entry
+// k_linear_small_m_rs below (up to 16 rows with K <= 8192, 24 with K <= 4096) puts the
+// quantizer and the weight stream in different waves; this kernel keeps the other bf16 shapes
+// (M <= 16 with a larger K) and the pre-quantized entry.
 //
 // The fused quantizer works on the natural row-major layout, where it is cheapest: lane l
 // quantizes elements 8 l .. 8 l + 7 of a row's 512-wide group slice (a quad of lanes is one MX
@@ -21,9 +24,9 @@
 // are then read back from LDS in the operand layout.  Working directly in the operand layout
 // would quantize 16 rows per wave whatever M is.
 //
-// From 16 rows on (bf16 entry), k_linear_decode_sk below also splits K across workgroups, so
-// that each workgroup reads only a part of the activations; there the operand layout is the
-// cheaper place to quantize.
+// Above the role-split kernel's rows (bf16 entry), k_linear_decode_sk below also splits K
+// across workgroups, so that each workgroup reads and quantizes only a part of the
+// activations; there the operand layout is the cheaper place to quantize.
 #include "mx_device.h"
 #include "mx_launch.h"
 
@@ -233,6 +236,191 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
     if (m < M) {
       const v2i o = {(int)pack_bf16x2(s[0] + bv[0], s[1] + bv[1]),
                      (int)pack_bf16x2(s[2] + bv[2], s[3] + bv[3])};
+      *(v2i*)(y + (int64_t)m * N + n) = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Small M, bf16 entry, with the waves of a workgroup in two roles (M <= 16 MT, K <= KMAX).
+// A wave that issues a long run of loads stalls once the CU's memory pipeline is full, and a
+// wave issues in order: in k_linear_small_m each wave's quantizer therefore starts only after
+// its last weight load has gone out, 1-3 us into the call at M = 8 (per-wave clock stamps),
+// and the quantizer's VALU time then adds to the call instead of hiding under the weight
+// stream.  Here:
+//  * waves 0-7 load the activation rows and quantize them (row-major, as k_linear_small_m)
+//    into an LDS image of the whole [M, K] block of codes and scales (K groups q, q + 8, ..);
+//  * waves 8-11 issue the weight stream of all their K groups (w, w + 4, ..; up to KMAX / 2048
+//    groups each, all in registers) and wait at one barrier for the image;
+//  * then waves 8-11 run the MFMAs, B operands and scales read from the image;
+//  * their 4 partials are added in wave order, then bias, one bf16 rounding, store.
+// Same codes and scales as k_quantize_act, so the same operands as every other path; the sum
+// over K runs in a different order than k_linear_small_m's (within the tolerance of any split).
+constexpr int kRsWaves = 4;    // weight (MFMA) waves
+
+// NQ quantizer waves (4 or 8), MT 16-row activation tiles, code image for K <= KMAX
+template <int NQ, int MT, int KMAX>
+struct RsCfg {
+  static constexpr int ROWS = 16 * MT;
+  static constexpr int PITCH = KMAX + 16;                  // code row pitch (max); +16 B: banks
+  static constexpr int GMAX = KMAX / 512 / kRsWaves;       // weight groups per weight wave
+  static constexpr int QMAX = KMAX / 512 / NQ;             // K groups per quantizer wave
+  static constexpr int LDS = ROWS * PITCH + ROWS * (KMAX / 32) + kRsWaves * MT * 64 * 16;
+  static_assert(LDS <= 160 * 1024, "must fit the 160 KiB LDS");
+};
+
+// s_waitcnt lgkmcnt(0), then the workgroup barrier; the empty assembly statements keep the
+// compiler from moving LDS accesses across it
+__device__ __forceinline__ void rs_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), vmcnt / expcnt not waited for
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// QR: rows quantized, a power of two >= M (rows past M repeat row M - 1; they are never read),
+// so that the row loops have no branches
+template <int WFMT, int NQ, int MT, int KMAX, int QR>
+__global__ __launch_bounds__(64 * (NQ + kRsWaves)) void k_linear_small_m_rs(const uint16_t* __restrict__ x, int M,
+                                                           int K, const uint8_t* __restrict__ packed,
+                                                           int N, const uint16_t* __restrict__ bias,
+                                                           uint16_t* __restrict__ y, BatchStrides bs) {
+  using R = RsCfg<NQ, MT, KMAX>;
+  static_assert(QR >= 1 && QR <= R::ROWS, "quantized rows");
+  {  // batch blockIdx.y (byte strides; all zero when unbatched)
+    const int64_t b = blockIdx.y;
+    x = (const uint16_t*)((const uint8_t*)x + b * bs.x);
+    packed += b * bs.w;
+    y = (uint16_t*)((uint8_t*)y + b * bs.y);
+    if (bias) bias = (const uint16_t*)((const uint8_t*)bias + b * bs.bias);
+  }
+  constexpr int FB = frag_bytes(WFMT);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[R::LDS];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int NG = N >> 4, KT = K >> 7, KT4 = (KT + 3) >> 2, KB = K >> 5;
+  const int P = K + 16;                                   // code row pitch
+  uint8_t* const codes = lds;                             // [ROWS][P]
+  uint8_t* const scl = lds + R::ROWS * P;                 // [ROWS][KB]
+  v4f* const red = (v4f*)(lds + R::ROWS * R::PITCH + R::ROWS * (KMAX / 32));   // [4][MT][64]
+  const int ng = blockIdx.x;
+  const int n = 16 * ng + 4 * g;                          // first of this lane's 4 columns
+
+  v8i a[R::GMAX][4];
+  uint32_t sw[R::GMAX];
+  v2i braw = {0, 0};
+  const bool bias8 = bias != nullptr && ((uintptr_t)bias & 7) == 0;
+  if (wave < NQ) {
+    // quantizer waves: K groups q, q + NQ, ..; lane l takes row m's elements 512 kt4 + 8 l .. + 7
+    // (a quad of lanes is one MX block).  Every row load of every group goes out before any is
+    // used; columns past K (a last group of fewer than 4 steps) and groups past the end re-read
+    // valid elements, whose codes are not stored (whole quads: K % 128 == 0).
+    typedef const __attribute__((address_space(1))) v4i* gv4i_t;
+    const __attribute__((address_space(1))) uint8_t* xg = (const __attribute__((address_space(1))) uint8_t*)x;
+    v4i xr[R::QMAX][QR];
+#pragma unroll
+    for (int i = 0; i < R::QMAX; ++i) {
+      const int colc = min(512 * (wave + NQ * i) + 8 * lane, K - 8);
+#pragma unroll
+      for (int m = 0; m < QR; ++m) xr[i][m] = *(gv4i_t)(xg + (uint32_t)(2 * (min(m, M - 1) * K + colc)));
+    }
+#pragma unroll
+    for (int i = 0; i < R::QMAX; ++i) {
+      const int col = 512 * (wave + NQ * i) + 8 * lane;
+      const bool on = col < K;
+#pragma unroll
+      for (int m = 0; m < QR; ++m) {
+        const v4i v = xr[i][m];
+        const uint32_t e = scale_byte_from_amax<0>(quad_max_u32(amax8_bf16_pk(v)));
+        v2i q = cvt8_e4m3(v, e8m0_to_float_ldexp(e));
+        if (e == 0xFFu) q = (v2i){0x7F7F7F7F, 0x7F7F7F7F};   // Inf/NaN block: NaN codes
+        if (on) {
+          *(v2i*)(codes + m * P + col) = q;
+          scl[m * KB + (col >> 5)] = (uint8_t)e;          // the quad's four lanes, one byte
+        }
+      }
+    }
+  } else {
+    // weight waves: the scale words and fragments of every K group of this wave, non-temporal
+    // (read once per call); steps past the end re-read the last one, unused
+    const int w = wave - NQ;
+    const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * FB) + (int64_t)ng * 64 + lane;
+#pragma unroll
+    for (int i = 0; i < R::GMAX; ++i) {
+      const int kt4 = w + kRsWaves * i;
+      if (kt4 < KT4) {                                    // wave-uniform
+        sw[i] = wsc[(int64_t)kt4 * NG * 64];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kt = min(4 * kt4 + j, KT - 1);
+          const uint8_t* f = packed + ((int64_t)kt * NG + ng) * FB;
+          const v4i lo = __builtin_nontemporal_load((const v4i*)(f + lane * 16));
+          if (WFMT == 0) {
+            const v4i hi = __builtin_nontemporal_load((const v4i*)(f + 1024 + lane * 16));
+            a[i][j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          } else {
+            const v2i hi = __builtin_nontemporal_load((const v2i*)(f + 1024 + lane * 8));
+            a[i][j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+          }
+        }
+      }
+    }
+    if (w < MT && bias8) braw = *(const v2i*)(bias + n);
+  }
+  rs_lds_barrier();   // the code image is complete
+
+  if (wave >= NQ) {
+    const int w = wave - NQ;
+    int mrow[MT];     // rows past M read row M - 1: their outputs are not stored
+#pragma unroll
+    for (int t = 0; t < MT; ++t) mrow[t] = min(16 * t + r, M - 1);
+    v4f acc[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < R::GMAX; ++i) {
+      const int kt4 = w + kRsWaves * i;
+      if (kt4 < KT4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int kt = 4 * kt4 + j;
+          if (kt < KT) {                                  // wave-uniform
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+              const uint8_t* p = codes + mrow[t] * P + 128 * kt + 16 * g;
+              const v4i lo = *(const v4i*)p, hi = *(const v4i*)(p + 64);
+              const v8i b = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              const uint32_t sb = scl[mrow[t] * KB + 4 * kt + g];
+              acc[t] = mfma_wsel<WFMT>(j, a[i][j], b, acc[t], sw[i], sb);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < MT; ++t) red[(w * MT + t) * 64 + lane] = acc[t];
+  }
+  rs_lds_barrier();   // the partials are in
+  if (wave >= NQ && wave - NQ < MT) {
+    const int t = wave - NQ;
+    v4f s4 = red[t * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kRsWaves; ++w) s4 += red[(w * MT + t) * 64 + lane];
+    float bv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias8) {
+      bv[0] = bf16_to_float((uint32_t)braw[0] & 0xFFFFu);
+      bv[1] = bf16_to_float((uint32_t)braw[0] >> 16);
+      bv[2] = bf16_to_float((uint32_t)braw[1] & 0xFFFFu);
+      bv[3] = bf16_to_float((uint32_t)braw[1] >> 16);
+    } else if (bias) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bv[i] = bf16_to_float(bias[n + i]);
+    }
+    const int m = 16 * t + r;
+    if (m < M) {
+      const v2i o = {(int)pack_bf16x2(s4[0] + bv[0], s4[1] + bv[1]),
+                     (int)pack_bf16x2(s4[2] + bv[2], s4[3] + bv[3])};
       *(v2i*)(y + (int64_t)m * N + n) = o;
     }
   }
@@ -468,8 +656,48 @@ hipError_t launch_linear_decode_sk(const uint16_t* x, int64_t M, int64_t K, cons
   return hipGetLastError();
 }
 
-bool small_m_fused(int64_t M, int64_t K) { return M >= 1 && M <= 16 && K % 128 == 0; }
+// Up to 16 rows with K <= 8192, up to 24 with K <= 4096.  Every workgroup quantizes the whole
+// activation block, so from about 24 rows on the quantizer's VALU time, not the weight stream,
+// sets the call (4096 x 4096: 6.2 us at M = 16, 8.6 at 24, 10.3 at 32, where the split-K decode
+// kernel, which quantizes only its K part, takes 7.8 / 9.0 / 9.3 us).
+bool small_m_rs(int64_t M, int64_t K) {
+  return M >= 1 && K % 128 == 0 && ((M <= 16 && K <= 8192) || (M <= 24 && K <= 4096));
+}
+bool small_m_fused(int64_t M, int64_t K) {
+  return M >= 1 && K % 128 == 0 && (M <= 16 || small_m_rs(M, K));
+}
 bool small_m_quantized(int64_t M, int64_t K) { return M >= 1 && M <= 32 && K % 128 == 0; }
+
+// the role-split kernel with the smallest code image and row count that hold the call; four
+// quantizer waves for one or two rows (fewer waves in the workgroup), eight from three rows on
+template <int WFMT, int MT, int KMAX>
+static void launch_rs_k(const uint16_t* x, int M, int K, const uint8_t* packed, int N,
+                        const uint16_t* bias, uint16_t* y, hipStream_t s, dim3 grid,
+                        const BatchStrides& bs) {
+#define MX_RS(NQ, QR) hipLaunchKernelGGL((k_linear_small_m_rs<WFMT, NQ, MT, KMAX, QR>), grid, dim3(64 * (NQ + kRsWaves)), 0, s, x, M, K, packed, N, bias, y, bs)
+  if constexpr (MT == 1) {
+    if (M <= 1) MX_RS(4, 1);
+    else if (M <= 2) MX_RS(4, 2);
+    else if (M <= 4) MX_RS(8, 4);
+    else if (M <= 8) MX_RS(8, 8);
+    else if (M <= 12) MX_RS(8, 12);
+    else MX_RS(8, 16);
+  } else {
+    MX_RS(8, 24);
+  }
+#undef MX_RS
+}
+template <int WFMT, int MT>
+static void launch_rs(const uint16_t* x, int M, int K, const uint8_t* packed, int N,
+                      const uint16_t* bias, uint16_t* y, hipStream_t s, dim3 grid,
+                      const BatchStrides& bs) {
+  if constexpr (MT == 2) {
+    launch_rs_k<WFMT, MT, 4096>(x, M, K, packed, N, bias, y, s, grid, bs);
+  } else {
+    if (K <= 4096) launch_rs_k<WFMT, MT, 4096>(x, M, K, packed, N, bias, y, s, grid, bs);
+    else launch_rs_k<WFMT, MT, 8192>(x, M, K, packed, N, bias, y, s, grid, bs);
+  }
+}
 
 template <int WFMT>
 static void launch_small(const void* x, const uint8_t* xs, bool quantized, int M, int K,
@@ -477,7 +705,11 @@ static void launch_small(const void* x, const uint8_t* xs, bool quantized, int M
                          hipStream_t s, int batch, const BatchStrides& bs) {
   const dim3 grid((unsigned)(N / 16), (unsigned)batch), block(512);
   const bool xs16 = ((uintptr_t)xs & 15) == 0 && K % 512 == 0;   // then K / 32 % 16 == 0 too
-  if (!quantized)
+  if (!quantized && M <= 16 && K <= 8192)
+    launch_rs<WFMT, 1>((const uint16_t*)x, M, K, packed, N, bias, y, s, grid, bs);
+  else if (!quantized && M <= 24 && K <= 4096)
+    launch_rs<WFMT, 2>((const uint16_t*)x, M, K, packed, N, bias, y, s, grid, bs);
+  else if (!quantized)
     hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, false, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y, bs);
   else if (M <= 16 && xs16)
     hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, true, true>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y, bs);

@@ -69,7 +69,11 @@ def test_linear_validation(L):
     # decode shapes with K split across workgroups (16 <= M <= 64, N % 64 == 0): the prefix,
     # then the partial sums (4 K parts x N/64 column groups x (fragment, tile) pairs x 1 KiB)
     assert L.mxfp8_workspace_bytes(32, 4096, 4096, 0) == 65536 + 4 * 64 * 8 * 1024
-    assert L.mxfp8_workspace_bytes(16, 4096, 4096, 0) == 65536 + 4 * 64 * 4 * 1024
+    # 16 rows (K <= 8192) and 24 (K <= 4096) run on the role-split small-M kernel, which needs
+    # no workspace: the size covers batch-invariant mode's quantized activations (xq, xs)
+    assert L.mxfp8_workspace_bytes(16, 4096, 4096, 0) == 65536 + 16 * 4096 + 16 * 128
+    assert L.mxfp8_workspace_bytes(24, 4096, 4096, 0) == 65536 + 24 * 4096 + 24 * 128
+    assert L.mxfp8_workspace_bytes(25, 4096, 4096, 0) == 65536 + 4 * 64 * 8 * 1024
     assert L.mxfp8_workspace_bytes(48, 4096, 4096, 0) == 65536 + 4 * 64 * 12 * 1024
     assert L.mxfp8_workspace_bytes(64, 4096, 4096, 0) == 65536 + 4 * 64 * 16 * 1024
     # above 64 rows, 32 tiles of 128 x 128: the quantized activations, then 8 K parts of fp32

@@ -1,5 +1,6 @@
 """GPU parity of the decode path that splits K across workgroups (mxfp8_linear with bf16
-activations, 16 <= M <= 64, N % 64 == 0, K % 128 == 0).
+activations, N % 64 == 0, K % 128 == 0, 25 <= M <= 64; from 17 rows when K > 4096 and from 16
+when K > 8192, where the role-split small-M kernel does not hold the activation block).
 
 That kernel quantizes the activations itself, in the MFMA operand layout, and adds the K parts
 of a column group in a fixed order chosen by the last workgroup to finish (a counter in the
@@ -26,13 +27,14 @@ FMTS = {0: "e4m3", 2: "e2m3", 3: "e3m2"}
 
 # (M, N, K): K parts = min(ceil(256 / (N / 64)), max(1, K / 1024), 8)
 SHAPES = [
-    (16, 64, 128),      # one part, one K step: seven idle waves; one activation tile
-    (16, 4096, 4096),   # four parts of 8 K steps
+    (25, 64, 128),      # one part, one K step: seven idle waves; two activation tiles
+    (16, 1024, 16384),  # one activation tile, eight parts of 16 K steps
+    (28, 4096, 4096),   # four parts of 8 K steps
     (32, 4096, 4096),   # the decode workload's shape, two activation tiles
     (17, 4096, 4480),   # 35 K steps in four parts of 8 or 9
     (20, 1024, 8192),   # eight parts
     (32, 16384, 1024),  # 256 column groups: one part, no cross-workgroup sum
-    (24, 640, 2560),    # ten column groups, two parts of 10 K steps
+    (26, 640, 2560),    # ten column groups, two parts of 10 K steps on different XCDs
     (33, 4096, 4096),   # three activation tiles, the third with one row
     (48, 2048, 4096),   # three full tiles, eight parts
     (64, 4096, 4096),   # four tiles: each wave finishes two (fragment, tile) pairs
@@ -72,7 +74,7 @@ def test_decode_split_k_matches_oracle(M, N, K, fmt):
 
 
 def test_decode_split_k_inf_block():
-    M, N, K = 19, 2048, 4096
+    M, N, K = 27, 2048, 4096
     x, w, b = _inputs(M, N, K, 5)
     x[3, 1000] = 0x7F80                     # +Inf in row 3
     layer, wq, ws = _layer(w, 0, b)
@@ -154,13 +156,13 @@ def test_decode_split_k_graph_replay():
 
 
 @pytest.mark.parametrize("bi", [False, True])
-@pytest.mark.parametrize("M", [1, 8, 16, 32, 50, 64, 100])
+@pytest.mark.parametrize("M", [1, 2, 8, 12, 16, 20, 24, 32, 50, 64, 100])
 def test_fused_quantizers_bit_exact_through_identity_weight(M, bi):
     """With W = I (E4M3 1.0 on the diagonal, scale 2^0) every output is one dequantized
     activation, exact in fp32 and in bf16, so the layer's output equals the oracle's
     dequantize(quantize(x)) bit for bit: a bit-level check of the quantizer each path fuses
-    (small-M kernel at M = 1 and 8, split-K decode kernel at 16, 32, 50 and 64, quantizer launch
-    + tiled GEMM at 100; in batch-invariant mode the quantizer launch + generic or tiled GEMM).  Inputs hold outlier
+    (role-split small-M kernel at M = 1 .. 24 with each of its row counts, split-K decode kernel
+    at 32, 50 and 64, quantizer launch + tiled GEMM at 100; in batch-invariant mode the quantizer launch + generic or tiled GEMM).  Inputs hold outlier
     channels, all-zero blocks, values that saturate at 448 after scaling, bf16 subnormals and
     exact rounding ties."""
     K = N = 2048

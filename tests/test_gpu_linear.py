@@ -247,11 +247,12 @@ def test_ping_pong_kernel(M, N, K, tile):
         mxfp8.set_tile_config(0, 0)
 
 
-# Small-M (decode) paths.  M <= 16: one launch with the activation quantizer fused into the
-# GEMM and K split over the 8 waves of a workgroup; K values give idle waves (K = 384), partial
-# 4-step groups (K = 640, 1152, 3968) and a wave with two groups, the second partial (K = 4224).
-# 16 < M <= 32: the activation quantizer kernel, then the same small-M kernel on the quantized
-# activations (two 16-row tiles).
+# Small-M (decode) paths, one launch with the activation quantizer fused in.  bf16 entry up to
+# 16 rows with K <= 8192 and up to 24 with K <= 4096: the role-split kernel (quantizer waves
+# beside MFMA waves); other rows up to 64 (N % 64 == 0): the split-K decode kernel.  The
+# pre-quantized entry (M <= 32) runs the small-M kernel with K split over its 8 waves.  K values
+# give idle waves (K = 384), partial 4-step groups (K = 640, 1152, 3968) and a wave with two
+# groups, the second partial (K = 4224).
 SMALL = [(1, 16, 128), (5, 48, 384), (16, 272, 640), (15, 80, 4224), (17, 64, 512),
          (31, 80, 3968), (32, 32, 1152), (24, 48, 4096), (32, 4096, 4096)]
 
@@ -276,9 +277,9 @@ def test_small_m_fused(M, N, K, fmt):
     y, layer = _full_check(x, w, fmt, b, name="small-%d-%d-%d-%d" % (M, N, K, fmt))
     xq, xs = orc.quantize(x, orc.E4M3)
     y2 = layer.apply_quantized(u8_dev(xq), u8_dev(xs))
-    if _splits_k(M, N, K):
-        # the bf16 entry splits K across workgroups here and adds in another order: both
-        # entries against the oracle
+    if _entries_differ(M, N, K):
+        # the bf16 entry runs another kernel here and adds in another order: both entries
+        # against the oracle
         ref, _, _ = orc.linear_ref(x, *orc.quantize(w, fmt), fmt, b)
         ok, rep = tolerance.check(host_bf16_bits(y2), ref, name="small-prequant")
         assert ok, rep
@@ -289,9 +290,49 @@ def test_small_m_fused(M, N, K, fmt):
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
-def _splits_k(M, N, K):
-    """shapes on which mxfp8_linear runs the decode kernel that splits K across workgroups"""
-    return 16 <= M <= 64 and N % 64 == 0 and K % 128 == 0
+def _role_split(M, K):
+    """shapes on which mxfp8_linear runs the role-split small-M kernel"""
+    return K % 128 == 0 and ((1 <= M <= 16 and K <= 8192) or (1 <= M <= 24 and K <= 4096))
+
+
+def _entries_differ(M, N, K):
+    """shapes on which mxfp8_linear (bf16 entry) runs another kernel than the pre-quantized
+    entry's small-M kernel: the role-split kernel or the split-K decode kernel"""
+    return _role_split(M, K) or (16 <= M <= 64 and N % 64 == 0 and K % 128 == 0)
+
+
+# The role-split kernel on each of its row counts (1, 2, 4, 8, 12 and 16 rows with one tile, 24
+# with two), both code-image sizes (K <= 4096, K <= 8192), partial last K groups, quantizer and
+# weight waves with no K group, columns that are not a multiple of 64, and a full decode width.
+RS = [(1, 64, 128), (2, 80, 8192), (3, 48, 640), (7, 272, 4224), (11, 96, 1152),
+      (12, 64, 3968), (13, 4096, 4096), (16, 160, 8192), (17, 64, 4096), (21, 112, 640),
+      (24, 48, 2048)]
+
+
+@pytest.mark.parametrize("fmt", [0, 2, 3])
+@pytest.mark.parametrize("M,N,K", RS)
+def test_small_m_role_split(M, N, K, fmt):
+    assert _role_split(M, K)
+    x, w, b = _small_inputs(M, N, K, M * 17 + N + K + fmt)
+    banner("linear small-M role split", M, N, K, FMTS[fmt])
+    _full_check(x, w, fmt, b if (M + K) % 3 else None, name="rs-%d-%d-%d-%d" % (M, N, K, fmt))
+
+
+@pytest.mark.parametrize("M,K", [(9, 1024), (22, 2560)])
+def test_small_m_role_split_inf_block(M, K):
+    """A block holding Inf: its row of the output is NaN, as in the oracle; the other rows are
+    unaffected."""
+    N = 128
+    x, w, b = _small_inputs(M, N, K, M + K)
+    x[3, 100] = 0x7F80                      # +Inf in row 3
+    layer, wq, ws = _layer(w, 0, b)
+    banner("linear small-M role split, Inf block", M, N, K)
+    y = host_bf16_bits(layer(bf16_dev(x)))
+    ref, _, _ = orc.linear_ref(x, wq, ws, 0, b)
+    assert np.isnan(tolerance.bf16_to_f64(y)[3]).all() and np.isnan(ref[3]).all()
+    keep = np.arange(M) != 3
+    ok, rep = tolerance.check(y[keep], ref[keep], name="rs-inf")
+    assert ok, rep
 
 
 @pytest.mark.parametrize("M", [1, 8, 32])
@@ -301,7 +342,7 @@ def test_decode_prequant_matches_fused(M):
     y = layer(bf16_dev(d["x"]))
     xq, xs = orc.quantize(d["x"], orc.E4M3)
     y2 = layer.apply_quantized(u8_dev(xq), u8_dev(xs))
-    if _splits_k(M, 4096, 4096):   # different kernels: each against the oracle
+    if _entries_differ(M, 4096, 4096):   # different kernels: each against the oracle
         ref, _, _ = orc.linear_ref(d["x"], wq, ws, 0, d["bias"])
         for yy, nm in ((y, "bf16 entry"), (y2, "pre-quantized entry")):
             ok, rep = tolerance.check(host_bf16_bits(yy), ref, name=nm)

@@ -444,6 +444,91 @@ __global__ __launch_bounds__(64 * (NQ + kRsWaves)) void k_linear_small_m_rs(cons
 constexpr int kSkMaxParts = 8;
 constexpr int kSkMaxM = 64;     // up to four 16-row activation tiles
 
+// The workgroup's sums of its (fragment, activation tile) pairs, pair pr = wave + NW u in s[u],
+// to the output: with P > 1 through the workspace, the P parts of a column group added in
+// part order by the last workgroup of the group to finish; then bias, one bf16 rounding,
+// store.  Every thread of the workgroup calls it (it holds workgroup barriers); `last` is a
+// workgroup-shared int.
+template <int MT, int NW, int PPW>
+__device__ __forceinline__ void sk_parts_to_output(v4f (&s)[PPW], int wave, int lane, int M,
+                                                   int N, int P, int p, int bx, int NG4,
+                                                   uint32_t* __restrict__ cnt,
+                                                   v4f* __restrict__ part,
+                                                   const uint16_t* __restrict__ bias,
+                                                   uint16_t* __restrict__ y, int& last) {
+  constexpr int CT = 4 * MT;
+  const int r = lane & 15, g = lane >> 4;
+  const int ng0 = 4 * bx;
+  if (P > 1) {
+    // The partials go through device-coherent accesses (agent-scope atomic stores and loads,
+    // which bypass the non-coherent caches), so the exchange needs no cache write-back or
+    // invalidation: a workgroup's stores have completed (vmcnt 0) before its thread 0 counts it
+    // in, and the last one reads the others' partials after its count.
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+      const int pr = wave + NW * u;
+      if (pr < CT) {
+        uint64_t* dst = (uint64_t*)(part + ((int64_t)(p * NG4 + bx) * CT + pr) * 64 + lane);
+        uint64_t v[2];
+        __builtin_memcpy(v, &s[u], 16);
+        __hip_atomic_store(dst, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 1, v[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): the stores are done
+    __syncthreads();
+    if (threadIdx.x == 0)
+      last = __hip_atomic_fetch_add(&cnt[bx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (uint32_t)(P - 1);
+    __syncthreads();
+    if (!last) return;
+#pragma unroll
+    for (int u = 0; u < PPW; ++u) {
+      const int pr = wave + NW * u;
+      if (pr < CT) {
+        // all parts' loads in flight together, then the sum in part order, whichever
+        // workgroup finished last
+        uint64_t v[kSkMaxParts][2];
+#pragma unroll
+        for (int q = 0; q < kSkMaxParts; ++q) {
+          if (q < P) {
+            const uint64_t* src = (const uint64_t*)(part + ((int64_t)(q * NG4 + bx) * CT + pr) * 64 + lane);
+            v[q][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            v[q][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kSkMaxParts; ++q) {
+          if (q < P) {
+            v4f t;
+            __builtin_memcpy(&t, v[q], 16);
+            s[u] = q == 0 ? t : s[u] + t;
+          }
+        }
+      }
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(&cnt[bx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+#pragma unroll
+  for (int u = 0; u < PPW; ++u) {
+    const int pr = wave + NW * u;
+    if (pr < CT) {
+      const int c = pr / MT, t = pr % MT;
+      const int m = 16 * t + r, n = 16 * (ng0 + c) + 4 * g;
+      if (m < M) {
+        float bv[4] = {0.f, 0.f, 0.f, 0.f};
+        if (bias) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bv[i] = bf16_to_float(bias[n + i]);
+        }
+        const v2i o = {(int)pack_bf16x2(s[u][0] + bv[0], s[u][1] + bv[1]),
+                       (int)pack_bf16x2(s[u][2] + bv[2], s[u][3] + bv[3])};
+        *(v2i*)(y + (int64_t)m * N + n) = o;
+      }
+    }
+  }
+}
+
 template <int WFMT, int MT>
 __global__ __launch_bounds__(512) void k_linear_decode_sk(const uint16_t* __restrict__ x, int M,
                                                           int K, const uint8_t* __restrict__ packed,
@@ -537,75 +622,162 @@ __global__ __launch_bounds__(512) void k_linear_decode_sk(const uint16_t* __rest
       for (int w = 1; w < kWaves; ++w) s[u] += red[w][pr][lane];
     }
   }
-  if (P > 1) {
-    // The partials go through device-coherent accesses (agent-scope atomic stores and loads,
-    // which bypass the non-coherent caches), so the exchange needs no cache write-back or
-    // invalidation: a workgroup's stores have completed (vmcnt 0) before its thread 0 counts it
-    // in, and the last one reads the others' partials after its count.
+  sk_parts_to_output<MT, kWaves, PPW>(s, wave, lane, M, N, P, p, bx, NG4, cnt, part, bias, y, last);
+}
+
+// The split-K decode kernel with the waves in two roles, for K parts of at most 8 steps: eight
+// waves load the part's activation rows and quantize them row-major (as k_linear_small_m_rs)
+// into an LDS image of codes and scales, while four waves issue the part's weight stream (two
+// steps of the 4 fragments each, in registers); one barrier, then the four run the MFMAs from
+// the image.  Their partials are added in wave order per (fragment, tile) pair, then the parts
+// as in k_linear_decode_sk.  Same codes and scales as k_quantize_act.
+constexpr int kSkRsSteps = 8;                        // K steps per part, at most
+constexpr int kSkRsPitch = 128 * kSkRsSteps + 16;    // code row pitch; +16 B: banks
+constexpr int kSkRsQ = 8;                            // quantizer waves
+constexpr int kSkRsW = 4;                            // weight (MFMA) waves
+
+template <int WFMT, int MT>
+__global__ __launch_bounds__(64 * (kSkRsQ + kSkRsW)) void k_linear_decode_sk_rs(
+    const uint16_t* __restrict__ x, int M, int K, const uint8_t* __restrict__ packed, int N,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, int P, uint32_t* __restrict__ cnt,
+    v4f* __restrict__ part) {
+  constexpr int NW = kSkRsQ + kSkRsW;
+  constexpr int FB = frag_bytes(WFMT);
+  constexpr int CT = 4 * MT;                         // (fragment, activation tile) pairs
+  constexpr int ROWS = 16 * MT;
+  constexpr int CODES = ROWS * kSkRsPitch;
+  constexpr int SCL = ROWS * 4 * kSkRsSteps;         // [ROWS][32 blocks]
+  constexpr int RED = kSkRsW * CT * 64 * 16;         // the weight waves' partials (after the MFMAs)
+  constexpr int LDS = CODES + SCL > RED ? CODES + SCL : RED;
+  constexpr int UMAX = (ROWS * 2 + kSkRsQ - 1) / kSkRsQ;   // (row, 4-step group) units per wave
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS];
+  __shared__ int last;
+  uint8_t* const codes = lds;                        // [ROWS][kSkRsPitch]
+  uint8_t* const scl = lds + CODES;                  // [ROWS][4 kSkRsSteps]
+  v4f* const red = (v4f*)lds;                        // [kSkRsW][CT][64], over the image
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g = lane >> 4;
+  const int NG = N >> 4, KT = K >> 7;
+  const int bx = blockIdx.x, p = blockIdx.y, NG4 = gridDim.x;
+  const int ng0 = 4 * bx;
+  const int kt_lo = (int)((int64_t)p * KT / P), kt_hi = (int)((int64_t)(p + 1) * KT / P);
+  const int KS = kt_hi - kt_lo, GP = (KS + 3) >> 2;  // steps, 4-step groups of the part
+
+  v8i a[2][4];
+  uint32_t sw[2][4];
+  if (wave < kSkRsQ) {
+    // quantizer waves: units u = wave + 8 i, row u / GP, group u % GP; lane l takes the row's
+    // elements 512 group + 8 l .. + 7 of the part.  All loads first; units past the last row
+    // and columns past the part re-read valid elements, whose codes are not stored.
+    typedef const __attribute__((address_space(1))) v4i* gv4i_t;
+    const __attribute__((address_space(1))) uint8_t* xg = (const __attribute__((address_space(1))) uint8_t*)x;
+    const uint32_t kbase = (uint32_t)kt_lo * 128;
+    v4i xr[UMAX];
 #pragma unroll
-    for (int u = 0; u < PPW; ++u) {
-      const int pr = wave + kWaves * u;
-      if (pr < CT) {
-        uint64_t* dst = (uint64_t*)(part + ((int64_t)(p * NG4 + bx) * CT + pr) * 64 + lane);
-        uint64_t v[2];
-        __builtin_memcpy(v, &s[u], 16);
-        __hip_atomic_store(dst, v[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(dst + 1, v[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int i = 0; i < UMAX; ++i) {
+      const int u = wave + kSkRsQ * i;
+      const int row = min(u / GP, M - 1);
+      const int colc = min(512 * (u % GP) + 8 * lane, 128 * KS - 8);
+      xr[i] = *(gv4i_t)(xg + 2 * ((uint32_t)row * (uint32_t)K + kbase + (uint32_t)colc));
+    }
+#pragma unroll
+    for (int i = 0; i < UMAX; ++i) {
+      const int u = wave + kSkRsQ * i;
+      const int row = u / GP, col = 512 * (u % GP) + 8 * lane;
+      const v4i v = xr[i];
+      const uint32_t e = scale_byte_from_amax<0>(quad_max_u32(amax8_bf16_pk(v)));
+      v2i q = cvt8_e4m3(v, e8m0_to_float_ldexp(e));
+      if (e == 0xFFu) q = (v2i){0x7F7F7F7F, 0x7F7F7F7F};   // Inf/NaN block: NaN codes
+      if (row < M && col < 128 * KS) {
+        *(v2i*)(codes + row * kSkRsPitch + col) = q;
+        scl[row * (4 * kSkRsSteps) + (col >> 5)] = (uint8_t)e;   // the quad's lanes, one byte
       }
     }
-    __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0): the stores are done
-    __syncthreads();
-    if (threadIdx.x == 0)
-      last = __hip_atomic_fetch_add(&cnt[bx], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             (uint32_t)(P - 1);
-    __syncthreads();
-    if (!last) return;
+  } else {
+    // weight waves: steps kt_lo + w and kt_lo + w + 4 of the part, the 4 fragments of each and
+    // their scale words (non-temporal: read once per call)
+    const int w = wave - kSkRsQ;
+    const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * FB) + (int64_t)ng0 * 64 + lane;
 #pragma unroll
-    for (int u = 0; u < PPW; ++u) {
-      const int pr = wave + kWaves * u;
-      if (pr < CT) {
-        // all parts' loads in flight together, then the sum in part order, whichever
-        // workgroup finished last
-        uint64_t v[kSkMaxParts][2];
+    for (int h = 0; h < 2; ++h) {
+      const int kt = kt_lo + w + 4 * h;
+      if (kt < kt_hi) {                              // wave-uniform
 #pragma unroll
-        for (int q = 0; q < kSkMaxParts; ++q) {
-          if (q < P) {
-            const uint64_t* src = (const uint64_t*)(part + ((int64_t)(q * NG4 + bx) * CT + pr) * 64 + lane);
-            v[q][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            v[q][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-        }
+        for (int c = 0; c < 4; ++c) sw[h][c] = wsc[(int64_t)(kt >> 2) * NG * 64 + c * 64];
 #pragma unroll
-        for (int q = 0; q < kSkMaxParts; ++q) {
-          if (q < P) {
-            v4f t;
-            __builtin_memcpy(&t, v[q], 16);
-            s[u] = q == 0 ? t : s[u] + t;
+        for (int c = 0; c < 4; ++c) {
+          const uint8_t* f = packed + ((int64_t)kt * NG + ng0 + c) * FB;
+          const v4i lo = __builtin_nontemporal_load((const v4i*)(f + lane * 16));
+          if (WFMT == 0) {
+            const v4i hi = __builtin_nontemporal_load((const v4i*)(f + 1024 + lane * 16));
+            a[h][c] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          } else {
+            const v2i hi = __builtin_nontemporal_load((const v2i*)(f + 1024 + lane * 8));
+            a[h][c] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
           }
         }
       }
     }
-    if (threadIdx.x == 0) __hip_atomic_store(&cnt[bx], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  rs_lds_barrier();   // the code image is complete
+
+  v4f acc[4][MT];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[c][t] = (v4f){0.f, 0.f, 0.f, 0.f};
+  if (wave >= kSkRsQ) {
+    const int w = wave - kSkRsQ;
+    int mrow[MT];     // rows past M read row M - 1: their outputs are not stored
+#pragma unroll
+    for (int t = 0; t < MT; ++t) mrow[t] = min(16 * t + r, M - 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int kt = kt_lo + w + 4 * h;
+      if (kt < kt_hi) {
+        const int ks = kt - kt_lo;
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const uint8_t* pb = codes + mrow[t] * kSkRsPitch + 128 * ks + 16 * g;
+          const v4i lo = *(const v4i*)pb, hi = *(const v4i*)(pb + 64);
+          const v8i b = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const uint32_t sb = scl[mrow[t] * (4 * kSkRsSteps) + 4 * ks + g];
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            acc[c][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                a[h][c], b, acc[c][t], WFMT, 0, 0, (int)(sw[h][c] >> (8 * (kt & 3))), 0, (int)sb);
+        }
+      }
+    }
+  }
+  rs_lds_barrier();   // every MFMA has read the image: the partials may go over it
+  if (wave >= kSkRsQ) {
+    const int w = wave - kSkRsQ;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) red[(w * CT + c * MT + t) * 64 + lane] = acc[c][t];
+  }
+  rs_lds_barrier();
+  // the four weight waves' partials of pair pr, added in wave order, by wave pr % 12
+  constexpr int PPW = (CT + NW - 1) / NW;
+  v4f s4[PPW];
 #pragma unroll
   for (int u = 0; u < PPW; ++u) {
-    const int pr = wave + kWaves * u;
+    const int pr = wave + NW * u;
+    s4[u] = (v4f){0.f, 0.f, 0.f, 0.f};
     if (pr < CT) {
-      const int c = pr / MT, t = pr % MT;
-      const int m = 16 * t + r, n = 16 * (ng0 + c) + 4 * g;
-      if (m < M) {
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias) {
+      s4[u] = red[pr * 64 + lane];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) bv[i] = bf16_to_float(bias[n + i]);
-        }
-        const v2i o = {(int)pack_bf16x2(s[u][0] + bv[0], s[u][1] + bv[1]),
-                       (int)pack_bf16x2(s[u][2] + bv[2], s[u][3] + bv[3])};
-        *(v2i*)(y + (int64_t)m * N + n) = o;
-      }
+      for (int w = 1; w < kSkRsW; ++w) s4[u] += red[(w * CT + pr) * 64 + lane];
     }
   }
+  sk_parts_to_output<MT, NW, PPW>(s4, wave, lane, M, N, P, p, bx, NG4, cnt, part, bias, y, last);
 }
+
+// the role-split variant holds parts of at most 8 K steps
+static bool decode_sk_rs_ok(int64_t KT, int P) { return (KT + P - 1) / P <= kSkRsSteps; }
 
 // K parts: about 256 workgroups, at least 8 K steps (one per wave) in each part, at most 8
 int decode_sk_parts(int64_t N, int64_t K) {
@@ -635,6 +807,28 @@ hipError_t launch_linear_decode_sk(const uint16_t* x, int64_t M, int64_t K, cons
   v4f* part = (v4f*)((uint8_t*)workspace + kWorkspacePrefix);
   const dim3 grid((unsigned)(N / 64), (unsigned)P), block(512);
   const int m = (int)M, k = (int)K, n = (int)N;
+  if (decode_sk_rs_ok(K / 128, P)) {
+    const dim3 block_rs(64 * (kSkRsQ + kSkRsW));
+#define MX_SKRS(W)                                                                                    \
+  do {                                                                                                \
+    if (M <= 16)                                                                                      \
+      hipLaunchKernelGGL((k_linear_decode_sk_rs<W, 1>), grid, block_rs, 0, s, x, m, k, packed, n, bias, y, P, cnt, part); \
+    else if (M <= 32)                                                                                 \
+      hipLaunchKernelGGL((k_linear_decode_sk_rs<W, 2>), grid, block_rs, 0, s, x, m, k, packed, n, bias, y, P, cnt, part); \
+    else if (M <= 48)                                                                                 \
+      hipLaunchKernelGGL((k_linear_decode_sk_rs<W, 3>), grid, block_rs, 0, s, x, m, k, packed, n, bias, y, P, cnt, part); \
+    else                                                                                              \
+      hipLaunchKernelGGL((k_linear_decode_sk_rs<W, 4>), grid, block_rs, 0, s, x, m, k, packed, n, bias, y, P, cnt, part); \
+  } while (0)
+    switch (fmt) {
+      case 0: MX_SKRS(0); break;
+      case 2: MX_SKRS(2); break;
+      case 3: MX_SKRS(3); break;
+      default: return hipErrorInvalidValue;
+    }
+#undef MX_SKRS
+    return hipGetLastError();
+  }
 #define MX_SK(W)                                                                                      \
   do {                                                                                                \
     if (M <= 16)                                                                                      \

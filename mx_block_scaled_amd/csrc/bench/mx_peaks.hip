@@ -3,7 +3,8 @@
 //
 //  * mxpk_mfma_loop: every wave of the grid issues chains of independent scaled MFMAs
 //    (16x16x128, A / B operand formats as given) with no memory traffic in the loop, so the
-//    time is the matrix units' own rate on the running chip.
+//    time is the matrix units' own rate on the running chip; one variant feeds them
+//    pseudo-random operands that change on every MFMA, the power draw of layer data.
 //  * mxpk_clock_probe: one wave that waits a given time and reports the shader-clock cycles
 //    that passed, i.e. the clock the chip runs at while other work fills it.
 //  * mxpk_stream_read: a read of n bytes (16-byte loads, a few in flight per lane) whose words
@@ -106,6 +107,68 @@ __global__ void __launch_bounds__(256) k_mfma_loop(int iters, float* out, uint64
 #pragma unroll
   for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
   if (s == -1.0f) out[0] = s;    // never true for these operands; keeps the loop alive
+}
+
+// the FP8 x FP8 loop with operands like a real GEMM's: four A and four B register images of
+// pseudo-random codes (exponent LSB cleared, so no NaN code) and scale bytes around 1.0, a
+// different (A, B, scales) combination on every MFMA, so the matrix unit's datapath switches
+// as it does on layer data (the constant small codes above barely toggle it, which lets the
+// chip hold a higher clock)
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352dU;
+  x ^= x >> 15;
+  x *= 0x846ca68bU;
+  x ^= x >> 16;
+  return x;
+}
+__global__ void __launch_bounds__(256) k_mfma_rand_loop(int iters, float* out, uint64_t* clk) {
+  const uint32_t t = threadIdx.x + 256u * blockIdx.x;
+  const uint64_t c0 = shader_clock();
+  const uint64_t r0 = real_clock();
+  v8i a[4], b[4];
+  int sa[4], sb[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      a[s][i] = (int)(mix32(t * 64u + s * 16u + i) & 0xF7F7F7F7u);
+      b[s][i] = (int)(mix32(t * 64u + s * 16u + 8u + i + 0x9E3779B9u) & 0xF7F7F7F7u);
+    }
+    sa[s] = 120 + (int)(mix32(t + 77u * s) & 7u);
+    sb[s] = 122 + (int)(mix32(t + 91u * s + 5u) & 3u);
+  }
+  v4f acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) acc[c] = (v4f){0.f, 0.f, 0.f, 0.f};
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+#endif
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < kChains; ++c) {
+#if defined(__HIP_DEVICE_COMPILE__)
+      // A image c % 4, B image (c + c / 4) % 4: consecutive MFMAs differ in both operands
+      asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                   : "+v"(acc[c])
+                   : "v"(a[c % 4]), "v"(b[(c + c / 4) % 4]), "v"(sa[c % 4]),
+                     "v"(sb[(c + c / 4) % 4]));
+#endif
+    }
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#endif
+  const uint64_t c1 = shader_clock();
+  const uint64_t r1 = real_clock();
+  if (clk && blockIdx.x == 0 && threadIdx.x == 0) {
+    clk[0] = c1 - c0;
+    clk[1] = r1 - r0;
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) s += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
+  if (s == 1.0e30f) out[0] = s;   // practically never; keeps the loop alive
 }
 
 // the same loop with the 32x32x64 scaled MFMA (FP8 operands), accumulators in AGPRs
@@ -280,6 +343,8 @@ int mxpk_mfma_loop(int afmt, int bfmt, int blocks, int iters, float* out, uint64
     hipLaunchKernelGGL((k_mfma_loop<2, 2>), dim3(blocks), dim3(256), 0, s, iters, out, clk);
   else if (afmt == 100 && bfmt == 100)   // 32x32x64, FP8 x FP8: 4 chains, 2x the flop each
     hipLaunchKernelGGL(k_mfma32_loop, dim3(blocks), dim3(256), 0, s, iters, out, clk);
+  else if (afmt == 200 && bfmt == 200)   // FP8 x FP8, pseudo-random operands (see above)
+    hipLaunchKernelGGL(k_mfma_rand_loop, dim3(blocks), dim3(256), 0, s, iters, out, clk);
   else
     return -1;
   return hipGetLastError() == hipSuccess ? 0 : -6;

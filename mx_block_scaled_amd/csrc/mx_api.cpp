@@ -93,7 +93,7 @@ int64_t quant_ws_bytes(int64_t M, int64_t K, int afmt = MX_FMT_E4M3) {
 constexpr int64_t kSkMinM = 16;
 bool sk_shape(int64_t M, int64_t N, int64_t K) {
   if (M < kSkMinM || !mx::decode_sk_ok(M, N, K)) return false;
-  if (mx::small_m_rs(M, K)) return false;   // the role-split small-M kernel
+  if (mx::small_m_rs(M, N, K)) return false;   // the role-split small-M kernel
   return M <= 32 || M * (K / mx::decode_sk_parts(N, K)) * 2 <= (256 << 10);
 }
 
@@ -115,6 +115,8 @@ int64_t linear_ws_bytes(int64_t M, int64_t N, int64_t K) {
     const int64_t q = quant_ws_bytes(M, K);
     return sk > q ? sk : q;
   }
+  // the small-M kernels need none; batch-invariant mode quantizes first and never splits K
+  if (mx::small_m_fused(M, N, K)) return quant_ws_bytes(M, K);
   return quant_split_ws_bytes(M, N, K);
 }
 
@@ -177,14 +179,14 @@ int linear_launch(const void* x_bf16, int64_t M, int64_t K, const void* packed, 
                                                   (const uint8_t*)packed, N, fmt,
                                                   (const uint16_t*)bias, (uint16_t*)y, workspace, s),
                       "linear (decode, split K) launch");
-  if (!mx::batch_invariant() && mx::small_m_fused(M, K))   // decode: quantizer fused in
+  if (!mx::batch_invariant() && mx::small_m_fused(M, N, K))   // decode: quantizer fused in
     return hip_status(mx::launch_linear_small_m(x_bf16, nullptr, false, M, K,
                                                 (const uint8_t*)packed, N, fmt,
                                                 (const uint16_t*)bias, (uint16_t*)y, s),
                       "linear (small M) launch");
   uint8_t* xq = (uint8_t*)workspace + mx::kWorkspacePrefix;
   uint8_t* xs = xq + ((M * K + 255) / 256) * 256;
-  float* part = !sk_shape(M, N, K) && mx::gemm_split_bytes(M, N, K)
+  float* part = !sk_shape(M, N, K) && !mx::small_m_fused(M, N, K) && mx::gemm_split_bytes(M, N, K)
                     ? (float*)((uint8_t*)workspace + split_offset(M, K)) : nullptr;
   hipError_t e = mx::launch_quantize_act((const uint16_t*)x_bf16, M, K, K, xq, xs, s);
   if (e != hipSuccess) return hip_status(e, "quantize_act launch");
@@ -361,7 +363,7 @@ int mxfp8_linear_batched(const void* x_bf16, int64_t B, int64_t M, int64_t K, co
   bs.w = P;
   bs.y = M * N * 2;
   bs.bias = bias ? N * 2 : 0;
-  if (!mx::batch_invariant() && mx::small_m_fused(M, K)) {
+  if (!mx::batch_invariant() && mx::small_m_fused(M, N, K)) {
     bs.x = M * K * 2;
     return hip_status(mx::launch_linear_small_m(x_bf16, nullptr, false, M, K,
                                                 (const uint8_t*)packed, N, fmt,

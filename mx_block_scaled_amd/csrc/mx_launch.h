@@ -80,9 +80,9 @@ int64_t decode_sk_workspace(int64_t M, int64_t N, int64_t K);
 hipError_t launch_linear_decode_sk(const uint16_t* x, int64_t M, int64_t K, const uint8_t* packed,
                                    int64_t N, int fmt, const uint16_t* bias, uint16_t* y,
                                    void* workspace, hipStream_t s);
-bool small_m_fused(int64_t M, int64_t K);
+bool small_m_fused(int64_t M, int64_t N, int64_t K);
 // shapes of small_m_fused that run on the role-split kernel (quantizer waves beside MFMA waves)
-bool small_m_rs(int64_t M, int64_t K);
+bool small_m_rs(int64_t M, int64_t N, int64_t K);
 bool small_m_quantized(int64_t M, int64_t K);
 hipError_t launch_linear_small_m(const void* x, const uint8_t* xs, bool quantized, int64_t M,
                                  int64_t K, const uint8_t* packed, int64_t N, int fmt,

@@ -14,7 +14,7 @@
 //    keeps it from displacing cached data (about 10 % per call at M = 1, 4096 x 4096).
 // Activations come either as bf16 (quantized inside the kernel, bit-identical to
 // k_quantize_act) or pre-quantized (E4M3 xq + row-major E8M0 xs, M <= 32).  For the bf16 entry
-// k_linear_small_m_rs below (up to 16 rows with K <= 8192, 24 with K <= 4096) puts the
+// k_linear_small_m_rs below (up to 16 rows with K <= 8192, 32 with K <= 4096) puts the
 // quantizer and the weight stream in different waves; this kernel keeps the other bf16 shapes
 // (M <= 16 with a larger K) and the pre-quantized entry.
 //
@@ -242,31 +242,40 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
 }
 
 // ---------------------------------------------------------------------------------------------
-// Small M, bf16 entry, with the waves of a workgroup in two roles (M <= 16 MT, K <= KMAX).
+// Small M, bf16 entry, with the waves of a workgroup in two roles (up to 32 rows, K <= KMAX).
 // A wave that issues a long run of loads stalls once the CU's memory pipeline is full, and a
 // wave issues in order: in k_linear_small_m each wave's quantizer therefore starts only after
 // its last weight load has gone out, 1-3 us into the call at M = 8 (per-wave clock stamps),
 // and the quantizer's VALU time then adds to the call instead of hiding under the weight
 // stream.  Here:
 //  * waves 0-7 load the activation rows and quantize them (row-major, as k_linear_small_m)
-//    into an LDS image of the whole [M, K] block of codes and scales (K groups q, q + 8, ..);
-//  * waves 8-11 issue the weight stream of all their K groups (w, w + 4, ..; up to KMAX / 2048
-//    groups each, all in registers) and wait at one barrier for the image;
-//  * then waves 8-11 run the MFMAs, B operands and scales read from the image;
-//  * their 4 partials are added in wave order, then bias, one bf16 rounding, store.
+//    into an LDS image of the whole [rows, K] block of codes and scales (K groups q, q + 8, ..);
+//  * the next NW = 4 (8 with four fragments per workgroup) waves issue the weight stream of all
+//    their K groups (w, w + NW, ..; up to 16 fragments of 2 KiB each, all in registers) and
+//    wait at one barrier for the image;
+//  * then those waves run the MFMAs, B operands and scales read from the image;
+//  * their NW partials are added in wave order, then bias, one bf16 rounding, store.
+// A workgroup computes F weight fragments (16 F output columns).  With F > 1 the rows are split
+// into tiles of RT rows, one workgroup per (column group, row tile): each workgroup then quantizes
+// only its own rows, so the quantizer's VALU time per workgroup stays that of one tile while
+// the row tiles of a column group read the same weight bytes (placed on one XCD, so the second
+// read comes from its L2).  Every output is the same sum in the same order whatever the tiling.
 // Same codes and scales as k_quantize_act, so the same operands as every other path; the sum
 // over K runs in a different order than k_linear_small_m's (within the tolerance of any split).
-constexpr int kRsWaves = 4;    // weight (MFMA) waves
-
-// NQ quantizer waves (4 or 8), MT 16-row activation tiles, code image for K <= KMAX
-template <int NQ, int MT, int KMAX>
+// NQ quantizer waves (4 or 8), MT 16-row activation tiles, F weight fragments, code image for
+// K <= KMAX
+template <int NQ, int MT, int F, int KMAX>
 struct RsCfg {
+  static constexpr int NW = F >= 4 ? 8 : 4;                // weight (MFMA) waves
   static constexpr int ROWS = 16 * MT;
   static constexpr int PITCH = KMAX + 16;                  // code row pitch (max); +16 B: banks
-  static constexpr int GMAX = KMAX / 512 / kRsWaves;       // weight groups per weight wave
+  static constexpr int GMAX = KMAX / 512 / NW;             // weight groups per weight wave
   static constexpr int QMAX = KMAX / 512 / NQ;             // K groups per quantizer wave
-  static constexpr int LDS = ROWS * PITCH + ROWS * (KMAX / 32) + kRsWaves * MT * 64 * 16;
+  static constexpr int PAIRS = MT * F;                     // (row tile, fragment) outputs
+  static constexpr int LDS = ROWS * PITCH + ROWS * (KMAX / 32) + NW * PAIRS * 64 * 16;
   static_assert(LDS <= 160 * 1024, "must fit the 160 KiB LDS");
+  static_assert(GMAX >= 1 && GMAX * 4 * F <= 16, "weight fragments held in registers per wave");
+  static_assert(PAIRS <= NW, "one weight wave finishes each output pair");
 };
 
 // s_waitcnt lgkmcnt(0), then the workgroup barrier; the empty assembly statements keep the
@@ -278,14 +287,34 @@ __device__ __forceinline__ void rs_lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// QR: rows quantized, a power of two >= M (rows past M repeat row M - 1; they are never read),
-// so that the row loops have no branches
-template <int WFMT, int NQ, int MT, int KMAX, int QR>
-__global__ __launch_bounds__(64 * (NQ + kRsWaves)) void k_linear_small_m_rs(const uint16_t* __restrict__ x, int M,
+// Workgroup blockIdx.x -> (column group c, row tile t) for R row tiles of G column groups.
+// Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i mod 8), so with G a
+// multiple of 8 the R tiles of a column group are given indices of one residue mod 8, and
+// their shared weight bytes meet in one L2.  Any order computes the same outputs.
+__device__ __forceinline__ void rs_tile_of(int i, int G, int R, int& c, int& t) {
+  if (R == 1) {
+    c = i;
+    t = 0;
+  } else if ((G & 7) == 0) {
+    const int j = i >> 3;
+    c = 8 * (j / R) + (i & 7);
+    t = j % R;
+  } else {
+    c = i / R;
+    t = i % R;
+  }
+}
+
+// QR: rows quantized per workgroup, >= the rows of its tile (rows past the tile repeat its
+// last row; they are never read), so that the row loops have no branches.  RT: rows per row
+// tile (used with F > 1; with F == 1 the workgroup takes all M rows).
+template <int WFMT, int NQ, int MT, int F, int KMAX, int QR>
+__global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_linear_small_m_rs(const uint16_t* __restrict__ x, int M,
                                                            int K, const uint8_t* __restrict__ packed,
                                                            int N, const uint16_t* __restrict__ bias,
-                                                           uint16_t* __restrict__ y, BatchStrides bs) {
-  using R = RsCfg<NQ, MT, KMAX>;
+                                                           uint16_t* __restrict__ y, BatchStrides bs,
+                                                           int RT) {
+  using R = RsCfg<NQ, MT, F, KMAX>;
   static_assert(QR >= 1 && QR <= R::ROWS, "quantized rows");
   {  // batch blockIdx.y (byte strides; all zero when unbatched)
     const int64_t b = blockIdx.y;
@@ -303,12 +332,21 @@ __global__ __launch_bounds__(64 * (NQ + kRsWaves)) void k_linear_small_m_rs(cons
   const int P = K + 16;                                   // code row pitch
   uint8_t* const codes = lds;                             // [ROWS][P]
   uint8_t* const scl = lds + R::ROWS * P;                 // [ROWS][KB]
-  v4f* const red = (v4f*)(lds + R::ROWS * R::PITCH + R::ROWS * (KMAX / 32));   // [4][MT][64]
-  const int ng = blockIdx.x;
-  const int n = 16 * ng + 4 * g;                          // first of this lane's 4 columns
+  v4f* const red = (v4f*)(lds + R::ROWS * R::PITCH + R::ROWS * (KMAX / 32));   // [NW][PAIRS][64]
+  int ng = blockIdx.x;                                    // first weight fragment
+  if constexpr (F > 1) {                                  // row tiles (one with F == 1)
+    const int RTn = (M + RT - 1) / RT;
+    int c, t;
+    rs_tile_of(blockIdx.x, gridDim.x / RTn, RTn, c, t);
+    ng = F * c;
+    const int m0 = RT * t;
+    M = min(RT, M - m0);                                  // rows of this tile
+    x += (int64_t)m0 * K;
+    y += (int64_t)m0 * N;
+  }
 
-  v8i a[R::GMAX][4];
-  uint32_t sw[R::GMAX];
+  v8i a[R::GMAX][4][F];
+  uint32_t sw[R::GMAX][F];
   v2i braw = {0, 0};
   const bool bias8 = bias != nullptr && ((uintptr_t)bias & 7) == 0;
   if (wave < NQ) {
@@ -348,39 +386,46 @@ __global__ __launch_bounds__(64 * (NQ + kRsWaves)) void k_linear_small_m_rs(cons
     const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * FB) + (int64_t)ng * 64 + lane;
 #pragma unroll
     for (int i = 0; i < R::GMAX; ++i) {
-      const int kt4 = w + kRsWaves * i;
+      const int kt4 = w + R::NW * i;
       if (kt4 < KT4) {                                    // wave-uniform
-        sw[i] = wsc[(int64_t)kt4 * NG * 64];
+#pragma unroll
+        for (int f = 0; f < F; ++f) sw[i][f] = wsc[(int64_t)kt4 * NG * 64 + 64 * f];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kt = min(4 * kt4 + j, KT - 1);
-          const uint8_t* f = packed + ((int64_t)kt * NG + ng) * FB;
-          const v4i lo = __builtin_nontemporal_load((const v4i*)(f + lane * 16));
-          if (WFMT == 0) {
-            const v4i hi = __builtin_nontemporal_load((const v4i*)(f + 1024 + lane * 16));
-            a[i][j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          } else {
-            const v2i hi = __builtin_nontemporal_load((const v2i*)(f + 1024 + lane * 8));
-            a[i][j] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+#pragma unroll
+          for (int f = 0; f < F; ++f) {
+            const uint8_t* fr = packed + ((int64_t)kt * NG + ng + f) * FB;
+            const v4i lo = __builtin_nontemporal_load((const v4i*)(fr + lane * 16));
+            if (WFMT == 0) {
+              const v4i hi = __builtin_nontemporal_load((const v4i*)(fr + 1024 + lane * 16));
+              a[i][j][f] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+              const v2i hi = __builtin_nontemporal_load((const v2i*)(fr + 1024 + lane * 8));
+              a[i][j][f] = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], 0, 0};
+            }
           }
         }
       }
     }
-    if (w < MT && bias8) braw = *(const v2i*)(bias + n);
+    // weight wave w finishes output pair w = (row tile w / F, fragment w % F): its bias
+    if (w < R::PAIRS && bias8) braw = *(const v2i*)(bias + 16 * (ng + w % F) + 4 * g);
   }
   rs_lds_barrier();   // the code image is complete
 
   if (wave >= NQ) {
     const int w = wave - NQ;
-    int mrow[MT];     // rows past M read row M - 1: their outputs are not stored
+    int mrow[MT];     // rows past the tile read its last row: their outputs are not stored
 #pragma unroll
     for (int t = 0; t < MT; ++t) mrow[t] = min(16 * t + r, M - 1);
-    v4f acc[MT];
+    v4f acc[MT][F];
 #pragma unroll
-    for (int t = 0; t < MT; ++t) acc[t] = (v4f){0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int f = 0; f < F; ++f) acc[t][f] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < R::GMAX; ++i) {
-      const int kt4 = w + kRsWaves * i;
+      const int kt4 = w + R::NW * i;
       if (kt4 < KT4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -392,21 +437,26 @@ __global__ __launch_bounds__(64 * (NQ + kRsWaves)) void k_linear_small_m_rs(cons
               const v4i lo = *(const v4i*)p, hi = *(const v4i*)(p + 64);
               const v8i b = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
               const uint32_t sb = scl[mrow[t] * KB + 4 * kt + g];
-              acc[t] = mfma_wsel<WFMT>(j, a[i][j], b, acc[t], sw[i], sb);
+#pragma unroll
+              for (int f = 0; f < F; ++f)
+                acc[t][f] = mfma_wsel<WFMT>(j, a[i][j][f], b, acc[t][f], sw[i][f], sb);
             }
           }
         }
       }
     }
 #pragma unroll
-    for (int t = 0; t < MT; ++t) red[(w * MT + t) * 64 + lane] = acc[t];
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int f = 0; f < F; ++f) red[((w * MT + t) * F + f) * 64 + lane] = acc[t][f];
   }
   rs_lds_barrier();   // the partials are in
-  if (wave >= NQ && wave - NQ < MT) {
-    const int t = wave - NQ;
-    v4f s4 = red[t * 64 + lane];
+  if (wave >= NQ && wave - NQ < R::PAIRS) {
+    const int pr = wave - NQ, t = pr / F, f = pr % F;
+    v4f s4 = red[pr * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < kRsWaves; ++w) s4 += red[(w * MT + t) * 64 + lane];
+    for (int w = 1; w < R::NW; ++w) s4 += red[(w * R::PAIRS + pr) * 64 + lane];
+    const int n = 16 * (ng + f) + 4 * g;                  // this lane's 4 output columns
     float bv[4] = {0.f, 0.f, 0.f, 0.f};
     if (bias8) {
       bv[0] = bf16_to_float((uint32_t)braw[0] & 0xFFFFu);
@@ -850,46 +900,68 @@ hipError_t launch_linear_decode_sk(const uint16_t* x, int64_t M, int64_t K, cons
   return hipGetLastError();
 }
 
-// Up to 16 rows with K <= 8192, up to 24 with K <= 4096.  Every workgroup quantizes the whole
-// activation block, so from about 24 rows on the quantizer's VALU time, not the weight stream,
-// sets the call (4096 x 4096: 6.2 us at M = 16, 8.6 at 24, 10.3 at 32, where the split-K decode
-// kernel, which quantizes only its K part, takes 7.8 / 9.0 / 9.3 us).
-bool small_m_rs(int64_t M, int64_t K) {
-  return M >= 1 && K % 128 == 0 && ((M <= 16 && K <= 8192) || (M <= 24 && K <= 4096));
+// Up to 16 rows with K <= 8192 in one row tile; with K <= 4096, 17 to 32 rows in two row tiles
+// of at most 16 rows (two weight fragments per workgroup, N % 32 == 0) and 33 to 64 rows in
+// three or four (four fragments per workgroup, N % 64 == 0), or, for other N, up to 24 rows in
+// one tile.  A workgroup quantizes its whole row tile, so the quantizer's VALU time grows with
+// the tile's rows (4096 x 4096 in one tile: 6.2 us at M = 16, 8.6 at 24, 10.3 at 32).
+constexpr int kRsRowSplitMinM = 17;   // from this many rows on: row tiles
+// fragments per workgroup of the row-split form, 0 where it is not used
+static int rs_row_split(int64_t M, int64_t N, int64_t K) {
+  if (K > 4096 || M < kRsRowSplitMinM || M > 64) return 0;
+  if (M <= 32) return N % 32 == 0 ? 2 : 0;
+  return N % 64 == 0 ? 4 : 0;
 }
-bool small_m_fused(int64_t M, int64_t K) {
-  return M >= 1 && K % 128 == 0 && (M <= 16 || small_m_rs(M, K));
+bool small_m_rs(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && K % 128 == 0 &&
+         ((M <= 16 && K <= 8192) || (M <= 24 && K <= 4096) || rs_row_split(M, N, K) > 0);
+}
+bool small_m_fused(int64_t M, int64_t N, int64_t K) {
+  return M >= 1 && K % 128 == 0 && (M <= 16 || small_m_rs(M, N, K));
 }
 bool small_m_quantized(int64_t M, int64_t K) { return M >= 1 && M <= 32 && K % 128 == 0; }
 
-// the role-split kernel with the smallest code image and row count that hold the call; four
-// quantizer waves for one or two rows (fewer waves in the workgroup), eight from three rows on
-template <int WFMT, int MT, int KMAX>
+// the role-split kernel with the smallest code image and row count that hold a row tile of RT
+// rows; four quantizer waves for one or two rows (fewer waves in the workgroup) and beside the
+// eight weight waves of four fragments per workgroup, eight otherwise
+template <int WFMT, int MT, int F, int KMAX>
 static void launch_rs_k(const uint16_t* x, int M, int K, const uint8_t* packed, int N,
                         const uint16_t* bias, uint16_t* y, hipStream_t s, dim3 grid,
-                        const BatchStrides& bs) {
-#define MX_RS(NQ, QR) hipLaunchKernelGGL((k_linear_small_m_rs<WFMT, NQ, MT, KMAX, QR>), grid, dim3(64 * (NQ + kRsWaves)), 0, s, x, M, K, packed, N, bias, y, bs)
-  if constexpr (MT == 1) {
-    if (M <= 1) MX_RS(4, 1);
-    else if (M <= 2) MX_RS(4, 2);
-    else if (M <= 4) MX_RS(8, 4);
-    else if (M <= 8) MX_RS(8, 8);
-    else if (M <= 12) MX_RS(8, 12);
+                        const BatchStrides& bs, int RT) {
+#define MX_RS(NQ, QR) hipLaunchKernelGGL((k_linear_small_m_rs<WFMT, NQ, MT, F, KMAX, QR>), grid, dim3(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)), 0, s, x, M, K, packed, N, bias, y, bs, RT)
+  if constexpr (F == 4) {
+    if (RT <= 12) MX_RS(4, 12);
+    else MX_RS(4, 16);
+  } else if constexpr (MT == 1) {
+    if (RT <= 1) MX_RS(4, 1);
+    else if (RT <= 2) MX_RS(4, 2);
+    else if (RT <= 4) MX_RS(8, 4);
+    else if (RT <= 8) MX_RS(8, 8);
+    else if (RT <= 12) MX_RS(8, 12);
     else MX_RS(8, 16);
   } else {
     MX_RS(8, 24);
   }
 #undef MX_RS
 }
-template <int WFMT, int MT>
+template <int WFMT>
 static void launch_rs(const uint16_t* x, int M, int K, const uint8_t* packed, int N,
-                      const uint16_t* bias, uint16_t* y, hipStream_t s, dim3 grid,
+                      const uint16_t* bias, uint16_t* y, hipStream_t s, int batch,
                       const BatchStrides& bs) {
-  if constexpr (MT == 2) {
-    launch_rs_k<WFMT, MT, 4096>(x, M, K, packed, N, bias, y, s, grid, bs);
+  const int F = rs_row_split(M, N, K);
+  if (F > 0) {                                  // R row tiles of RT rows, F fragments
+    const int R0 = (M + 15) / 16, RT = (M + R0 - 1) / R0, R = (M + RT - 1) / RT;
+    const dim3 grid((unsigned)(N / (16 * F) * R), (unsigned)batch);
+    if (F == 2) launch_rs_k<WFMT, 1, 2, 4096>(x, M, K, packed, N, bias, y, s, grid, bs, RT);
+    else launch_rs_k<WFMT, 1, 4, 4096>(x, M, K, packed, N, bias, y, s, grid, bs, RT);
+    return;
+  }
+  const dim3 grid((unsigned)(N / 16), (unsigned)batch);
+  if (M <= 16) {
+    if (K <= 4096) launch_rs_k<WFMT, 1, 1, 4096>(x, M, K, packed, N, bias, y, s, grid, bs, M);
+    else launch_rs_k<WFMT, 1, 1, 8192>(x, M, K, packed, N, bias, y, s, grid, bs, M);
   } else {
-    if (K <= 4096) launch_rs_k<WFMT, MT, 4096>(x, M, K, packed, N, bias, y, s, grid, bs);
-    else launch_rs_k<WFMT, MT, 8192>(x, M, K, packed, N, bias, y, s, grid, bs);
+    launch_rs_k<WFMT, 2, 1, 4096>(x, M, K, packed, N, bias, y, s, grid, bs, M);
   }
 }
 
@@ -899,10 +971,8 @@ static void launch_small(const void* x, const uint8_t* xs, bool quantized, int M
                          hipStream_t s, int batch, const BatchStrides& bs) {
   const dim3 grid((unsigned)(N / 16), (unsigned)batch), block(512);
   const bool xs16 = ((uintptr_t)xs & 15) == 0 && K % 512 == 0;   // then K / 32 % 16 == 0 too
-  if (!quantized && M <= 16 && K <= 8192)
-    launch_rs<WFMT, 1>((const uint16_t*)x, M, K, packed, N, bias, y, s, grid, bs);
-  else if (!quantized && M <= 24 && K <= 4096)
-    launch_rs<WFMT, 2>((const uint16_t*)x, M, K, packed, N, bias, y, s, grid, bs);
+  if (!quantized && small_m_rs(M, N, K))
+    launch_rs<WFMT>((const uint16_t*)x, M, K, packed, N, bias, y, s, batch, bs);
   else if (!quantized)
     hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, false, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y, bs);
   else if (M <= 16 && xs16)
@@ -919,7 +989,7 @@ hipError_t launch_linear_small_m(const void* x, const uint8_t* xs, bool quantize
                                  int64_t K, const uint8_t* packed, int64_t N, int fmt,
                                  const uint16_t* bias, uint16_t* y, hipStream_t s, int batch,
                                  BatchStrides bs) {
-  if (quantized ? !small_m_quantized(M, K) : !small_m_fused(M, K)) return hipErrorInvalidValue;
+  if (quantized ? !small_m_quantized(M, K) : !small_m_fused(M, N, K)) return hipErrorInvalidValue;
   const int m = (int)M, k = (int)K, n = (int)N;
   switch (fmt) {
     case 0: launch_small<0>(x, xs, quantized, m, k, packed, n, bias, y, s, batch, bs); break;

@@ -62,20 +62,21 @@ def test_quantize_act_validation(L):
 
 def test_linear_validation(L):
     assert L.mxfp8_workspace_bytes(65, 256, 512, 0) == 65536 + 65 * 512 + 65 * 16  # prefix, xq, xs
-    # 64 rows: the split-K decode kernel in one K part (4 column groups x 16 pairs x 1 KiB),
-    # or, in batch-invariant mode, the quantized activations, which need less
+    # 64 rows, K <= 4096: the role-split small-M kernel (no workspace); the size covers
+    # batch-invariant mode's quantized activations
     ws = L.mxfp8_workspace_bytes(64, 256, 512, 0)
-    assert ws == 65536 + 4 * 16 * 1024
-    # decode shapes with K split across workgroups (16 <= M <= 64, N % 64 == 0): the prefix,
-    # then the partial sums (4 K parts x N/64 column groups x (fragment, tile) pairs x 1 KiB)
-    assert L.mxfp8_workspace_bytes(32, 4096, 4096, 0) == 65536 + 4 * 64 * 8 * 1024
-    # 16 rows (K <= 8192) and 24 (K <= 4096) run on the role-split small-M kernel, which needs
-    # no workspace: the size covers batch-invariant mode's quantized activations (xq, xs)
-    assert L.mxfp8_workspace_bytes(16, 4096, 4096, 0) == 65536 + 16 * 4096 + 16 * 128
-    assert L.mxfp8_workspace_bytes(24, 4096, 4096, 0) == 65536 + 24 * 4096 + 24 * 128
-    assert L.mxfp8_workspace_bytes(25, 4096, 4096, 0) == 65536 + 4 * 64 * 8 * 1024
-    assert L.mxfp8_workspace_bytes(48, 4096, 4096, 0) == 65536 + 4 * 64 * 12 * 1024
-    assert L.mxfp8_workspace_bytes(64, 4096, 4096, 0) == 65536 + 4 * 64 * 16 * 1024
+    assert ws == 65536 + 64 * 512 + 64 * 16
+    # decode shapes with K split across workgroups (N % 64 == 0, 17 <= M <= 64, K > 4096): the
+    # prefix, then the partial sums (K parts x N/64 column groups x (fragment, tile) pairs x
+    # 1 KiB)
+    assert L.mxfp8_workspace_bytes(32, 4096, 8192, 0) == 65536 + 4 * 64 * 8 * 1024
+    assert L.mxfp8_workspace_bytes(17, 2048, 8192, 0) == 65536 + 8 * 32 * 8 * 1024
+    assert L.mxfp8_workspace_bytes(48, 2048, 5120, 0) == 65536 + 5 * 32 * 12 * 1024
+    assert L.mxfp8_workspace_bytes(64, 2048, 8192, 0) == 65536 + 8 * 32 * 16 * 1024
+    # up to 16 rows (K <= 8192) and up to 64 (K <= 4096) run on the role-split small-M kernel,
+    # which needs no workspace: the size covers batch-invariant mode's quantized activations
+    for m in (16, 24, 25, 32, 48, 64):
+        assert L.mxfp8_workspace_bytes(m, 4096, 4096, 0) == 65536 + m * 4096 + m * 128
     # above 64 rows, 32 tiles of 128 x 128: the quantized activations, then 8 K parts of fp32
     # sums of the tiled GEMM
     q = 65536 + 65 * 4096 + 65 * 128

@@ -1,6 +1,6 @@
 """GPU parity of the decode path that splits K across workgroups (mxfp8_linear with bf16
-activations, N % 64 == 0, K % 128 == 0, 25 <= M <= 64; from 17 rows when K > 4096 and from 16
-when K > 8192, where the role-split small-M kernel does not hold the activation block).
+activations, N % 64 == 0, K % 128 == 0, 17 <= M <= 64 with K > 4096, and M = 16 with
+K > 8192: the shapes whose activation rows the role-split small-M kernel does not hold).
 
 That kernel quantizes the activations itself, in the MFMA operand layout, and adds the K parts
 of a column group in a fixed order chosen by the last workgroup to finish (a counter in the
@@ -27,18 +27,17 @@ FMTS = {0: "e4m3", 2: "e2m3", 3: "e3m2"}
 
 # (M, N, K): K parts = min(ceil(256 / (N / 64)), max(1, K / 1024), 8)
 SHAPES = [
-    (25, 64, 128),      # one part, one K step: seven idle waves; two activation tiles
     (16, 1024, 16384),  # one activation tile, eight parts of 16 K steps
-    (28, 4096, 4096),   # four parts of 8 K steps
-    (32, 4096, 4096),   # the decode workload's shape, two activation tiles
+    (28, 2048, 8192),   # two activation tiles, eight parts of 8 K steps
+    (32, 4096, 8192),   # two activation tiles, four parts of 16 K steps
     (17, 4096, 4480),   # 35 K steps in four parts of 8 or 9
     (20, 1024, 8192),   # eight parts
-    (32, 16384, 1024),  # 256 column groups: one part, no cross-workgroup sum
-    (26, 640, 2560),    # ten column groups, two parts of 10 K steps on different XCDs
-    (33, 4096, 4096),   # three activation tiles, the third with one row
-    (48, 2048, 4096),   # three full tiles, eight parts
-    (64, 4096, 4096),   # four tiles: each wave finishes two (fragment, tile) pairs
-    (57, 1024, 1152),   # four tiles, one part of 9 K steps: no cross-workgroup sum
+    (20, 16384, 4224),  # 256 column groups: one part of 33 K steps, no cross-workgroup sum
+    (26, 640, 5120),    # ten column groups, five parts of 8 K steps on different XCDs
+    (33, 4096, 8192),   # three activation tiles, the third with one row
+    (48, 2048, 5120),   # three full tiles, five parts of 8 K steps
+    (64, 2048, 8192),   # four tiles: each wave finishes two (fragment, tile) pairs
+    (57, 2048, 4608),   # four tiles, four parts of 9 K steps
 ]
 
 
@@ -74,7 +73,7 @@ def test_decode_split_k_matches_oracle(M, N, K, fmt):
 
 
 def test_decode_split_k_inf_block():
-    M, N, K = 27, 2048, 4096
+    M, N, K = 27, 2048, 8192
     x, w, b = _inputs(M, N, K, 5)
     x[3, 1000] = 0x7F80                     # +Inf in row 3
     layer, wq, ws = _layer(w, 0, b)
@@ -91,7 +90,7 @@ def test_decode_split_k_inf_block():
 def test_decode_split_k_workspace_reuse():
     """One workspace for a sequence of calls of several shapes and entry points: every call
     repeats its first result bit for bit, so the counters are back at zero after each call."""
-    K = 4096
+    K = 8192
     g = np.random.default_rng(11)
     shapes = [(32, 4096), (16, 1024), (3, 4096), (300, 256), (1, 4096), (20, 640), (64, 4096),
               (100, 4096)]
@@ -120,7 +119,7 @@ def test_decode_split_k_graph_replay():
     """The calls captured in a HIP graph: no memset nodes; every replay, with eager work and
     synchronizations in between, equals the eager results."""
     g = np.random.default_rng(12)
-    N = K = 4096
+    N, K = 4096, 8192
     wb = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
     wq, wsc = orc.quantize(wb, 0)
     pk = mxfp8.prepack_weight(u8_dev(wq), u8_dev(wsc), 0)
@@ -156,16 +155,19 @@ def test_decode_split_k_graph_replay():
 
 
 @pytest.mark.parametrize("bi", [False, True])
-@pytest.mark.parametrize("M", [1, 2, 8, 12, 16, 20, 24, 32, 50, 64, 100])
-def test_fused_quantizers_bit_exact_through_identity_weight(M, bi):
+@pytest.mark.parametrize("M,K", [(1, 2048), (2, 2048), (8, 2048), (12, 2048), (16, 2048),
+                                 (20, 2048), (24, 2048), (32, 2048), (50, 2048), (64, 2048),
+                                 (100, 2048), (32, 4224), (50, 4224)])
+def test_fused_quantizers_bit_exact_through_identity_weight(M, K, bi):
     """With W = I (E4M3 1.0 on the diagonal, scale 2^0) every output is one dequantized
     activation, exact in fp32 and in bf16, so the layer's output equals the oracle's
     dequantize(quantize(x)) bit for bit: a bit-level check of the quantizer each path fuses
-    (role-split small-M kernel at M = 1 .. 24 with each of its row counts, split-K decode kernel
-    at 32, 50 and 64, quantizer launch + tiled GEMM at 100; in batch-invariant mode the quantizer launch + generic or tiled GEMM).  Inputs hold outlier
+    (role-split small-M kernel at M = 1 .. 16 with each of its row counts in one row tile, at
+    20, 24 and 32 in two row tiles, at 50 and 64 in four; split-K decode kernel at 32 and 50
+    with K = 4224; quantizer launch + tiled GEMM at 100; in batch-invariant mode the quantizer launch + generic or tiled GEMM).  Inputs hold outlier
     channels, all-zero blocks, values that saturate at 448 after scaling, bf16 subnormals and
     exact rounding ties."""
-    K = N = 2048
+    N = K
     g = np.random.default_rng(M + 77)
     x = g.standard_normal((M, K)).astype(np.float32)
     x[:, g.choice(K, 20, replace=False)] *= 200.0
@@ -188,6 +190,30 @@ def test_fused_quantizers_bit_exact_through_identity_weight(M, bi):
     # the layer's output is a sum started at +0, so a code of -0 comes out as +0
     expect[expect == 0x8000] = 0
     assert np.array_equal(y, expect), np.argwhere(y != expect)[:8]
+
+
+def test_fused_quantizer_two_activation_tiles_bit_exact_through_identity_weight():
+    """The role-split kernel's one-row-tile form with two 16-row activation tiles (24 rows,
+    N % 32 != 0): W = [I; 0], so the first K outputs of a row are its dequantized activations,
+    bit for bit, and the last 16 are zero."""
+    M, N, K = 24, 2064, 2048
+    g = np.random.default_rng(5)
+    x = g.standard_normal((M, K)).astype(np.float32)
+    x[:, g.choice(K, 20, replace=False)] *= 200.0
+    xb = x.reshape(M, K // 32, 32)
+    xb[g.integers(0, M, 3), g.integers(0, K // 32, 3)] = 0.0
+    xb[:, 5, :] = g.standard_normal((M, 32)).astype(np.float32) * 1e-39
+    xb[:, 7, 0] = 480.0
+    xb[:, 7, 1:5] = [12.5, 13.5, 17.0, 19.0]
+    x_bits = synth.bf16_bits(x)
+    layer, wq, ws = _layer(synth.bf16_bits(np.eye(N, K, dtype=np.float32)), 0, None)
+    banner("identity weight, two activation tiles in one row tile", M, N, K)
+    y = host_bf16_bits(layer(bf16_dev(x_bits)))
+    xq, xs = orc.quantize(x_bits, orc.E4M3)
+    expect = orc.f64_to_bf16(orc.dequantize(xq, xs, orc.E4M3))
+    expect[expect == 0x8000] = 0
+    assert np.array_equal(y[:, :K], expect), np.argwhere(y[:, :K] != expect)[:8]
+    assert not y[:, K:].any()
 
 
 @pytest.mark.parametrize("M", [8, 100])
@@ -219,7 +245,7 @@ def test_concurrent_streams_with_own_workspaces():
     tiled GEMM with K split, small-M kernel): every result equals the same call made alone,
     bit for bit, so workspaces that are not shared never interfere."""
     g = np.random.default_rng(21)
-    N = K = 4096
+    N, K = 4096, 8192
     wb = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
     wq, wsc = orc.quantize(wb, 0)
     pk = mxfp8.prepack_weight(u8_dev(wq), u8_dev(wsc), 0)

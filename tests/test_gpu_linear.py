@@ -290,39 +290,52 @@ def test_small_m_fused(M, N, K, fmt):
         assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
-def _role_split(M, K):
+def _row_split(M, N, K):
+    """shapes on which the role-split kernel splits the rows into tiles: two of up to 16 rows
+    (two weight fragments per workgroup) or three or four (four fragments)"""
+    return K % 128 == 0 and K <= 4096 and ((17 <= M <= 32 and N % 32 == 0)
+                                           or (33 <= M <= 64 and N % 64 == 0))
+
+
+def _role_split(M, N, K):
     """shapes on which mxfp8_linear runs the role-split small-M kernel"""
-    return K % 128 == 0 and ((1 <= M <= 16 and K <= 8192) or (1 <= M <= 24 and K <= 4096))
+    return K % 128 == 0 and ((1 <= M <= 16 and K <= 8192) or (1 <= M <= 24 and K <= 4096)
+                             or _row_split(M, N, K))
 
 
 def _entries_differ(M, N, K):
     """shapes on which mxfp8_linear (bf16 entry) runs another kernel than the pre-quantized
     entry's small-M kernel: the role-split kernel or the split-K decode kernel"""
-    return _role_split(M, K) or (16 <= M <= 64 and N % 64 == 0 and K % 128 == 0)
+    return _role_split(M, N, K) or (16 <= M <= 64 and N % 64 == 0 and K % 128 == 0)
 
 
 # The role-split kernel on each of its row counts (1, 2, 4, 8, 12 and 16 rows with one tile, 24
-# with two), both code-image sizes (K <= 4096, K <= 8192), partial last K groups, quantizer and
-# weight waves with no K group, columns that are not a multiple of 64, and a full decode width.
+# with two 16-row activation tiles, two row tiles of 9 to 16 rows, three or four of 11 to 16),
+# both code-image sizes (K <= 4096, K <= 8192), partial last K groups, quantizer and weight
+# waves with no K group, columns that are not a multiple of 64, and a full decode width.  Row
+# tiles: column-group counts that are a multiple of 8 (row tiles of a group on one XCD) and
+# not (1, 3, 33), row tiles of unequal rows.
 RS = [(1, 64, 128), (2, 80, 8192), (3, 48, 640), (7, 272, 4224), (11, 96, 1152),
-      (12, 64, 3968), (13, 4096, 4096), (16, 160, 8192), (17, 64, 4096), (21, 112, 640),
-      (24, 48, 2048)]
+      (12, 64, 3968), (13, 4096, 4096), (16, 160, 8192), (21, 112, 640), (24, 48, 2048),
+      (17, 64, 4096), (18, 32, 128), (25, 96, 640), (29, 256, 3968), (19, 1056, 1152),
+      (32, 4096, 4096), (23, 512, 4096), (31, 8192, 2048),
+      (33, 64, 4096), (40, 192, 640), (48, 512, 3968), (49, 2112, 1152), (64, 4096, 4096),
+      (57, 1024, 128), (36, 8192, 2048)]
 
 
 @pytest.mark.parametrize("fmt", [0, 2, 3])
 @pytest.mark.parametrize("M,N,K", RS)
 def test_small_m_role_split(M, N, K, fmt):
-    assert _role_split(M, K)
+    assert _role_split(M, N, K)
     x, w, b = _small_inputs(M, N, K, M * 17 + N + K + fmt)
     banner("linear small-M role split", M, N, K, FMTS[fmt])
     _full_check(x, w, fmt, b if (M + K) % 3 else None, name="rs-%d-%d-%d-%d" % (M, N, K, fmt))
 
 
-@pytest.mark.parametrize("M,K", [(9, 1024), (22, 2560)])
-def test_small_m_role_split_inf_block(M, K):
+@pytest.mark.parametrize("M,N,K", [(9, 128, 1024), (22, 128, 2560), (22, 112, 2560)])
+def test_small_m_role_split_inf_block(M, N, K):
     """A block holding Inf: its row of the output is NaN, as in the oracle; the other rows are
-    unaffected."""
-    N = 128
+    unaffected (one row tile; two row tiles; two 16-row activation tiles in one row tile)."""
     x, w, b = _small_inputs(M, N, K, M + K)
     x[3, 100] = 0x7F80                      # +Inf in row 3
     layer, wq, ws = _layer(w, 0, b)
@@ -486,11 +499,12 @@ def test_bias_at_odd_offset(M):
     assert ok, rep
 
 
-# one shape per mxfp8_linear path: small-M fused, split-K decode (2 and 4 row tiles), split-K
-# tiled GEMM with its reduction launch (8 and 2 K parts), tiled GEMM, generic GEMM
-# (K % 128 != 0)
-PATH_SHAPES = [(8, 1024, 2048), (32, 1024, 4096), (64, 2048, 4096), (100, 2048, 4096),
-               (300, 4096, 4096), (300, 8192, 1024), (40, 512, 1120)]
+# one shape per mxfp8_linear path: small-M fused (one, two and four row tiles), split-K decode
+# (2 and 4 activation tiles), split-K tiled GEMM with its reduction launch (8 and 2 K parts), tiled
+# GEMM, generic GEMM (K % 128 != 0)
+PATH_SHAPES = [(8, 1024, 2048), (32, 1024, 4096), (64, 1024, 4096), (32, 1024, 8192),
+               (64, 2048, 8192), (100, 2048, 4096), (300, 4096, 4096), (300, 8192, 1024),
+               (40, 512, 1120)]
 
 
 @pytest.mark.parametrize("M,N,K", PATH_SHAPES)

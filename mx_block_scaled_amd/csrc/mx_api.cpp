@@ -82,14 +82,12 @@ int64_t quant_ws_bytes(int64_t M, int64_t K, int afmt = MX_FMT_E4M3) {
 
 // decode shapes that mxfp8_linear runs on the kernel splitting K across workgroups (outside
 // batch-invariant mode).  Its cross-workgroup sum costs about 2 us of memory round trips at
-// the end (store, count, load), so the role-split small-M kernel takes the shapes it holds
-// (4096 x 4096: 6.2 against 7.8 us at M = 16, 8.6 against 9.0 at M = 24); above 24 rows the
-// small-M kernels' full-K quantizer in every workgroup costs more than the sum (M = 32: 10.3
-// against 9.3 us), and below 16 rows so does the split-K kernel (6.3 against 7.6 us at M = 8
-// before the role split).  From 33 rows on it
-// is kept while one workgroup's share of x (M rows x K / P bf16) stays within 256 KiB; above
-// that the tiled GEMM with K split across workgroups is faster (4096 x 4096: 10.8 against 14.1
-// us at M = 33, 13.1 against 15.2 at M = 64; 8192 x 8192, M = 64: 28.1 against 24.5 us)
+// the end (store, count, load), so the role-split small-M kernel takes every shape it holds:
+// up to 16 rows with K <= 8192, and with K <= 4096 up to 64 rows in row tiles (4096 x 4096:
+// 6.9 against 9.0 us at M = 32, 8.8 against 12.9 at M = 64).  The split-K kernel keeps 17 to
+// 64 rows with a longer K (16 rows from K > 8192) while one workgroup's share of x (M rows x
+// K / P bf16) stays within 256 KiB; above that the tiled GEMM with K split across workgroups
+// is faster (8192 x 8192, M = 64: 28.1 against 24.5 us)
 constexpr int64_t kSkMinM = 16;
 bool sk_shape(int64_t M, int64_t N, int64_t K) {
   if (M < kSkMinM || !mx::decode_sk_ok(M, N, K)) return false;

@@ -177,7 +177,8 @@ int linear_launch(const void* x_bf16, int64_t M, int64_t K, const void* packed, 
                                                   (const uint8_t*)packed, N, fmt,
                                                   (const uint16_t*)bias, (uint16_t*)y, workspace, s),
                       "linear (decode, split K) launch");
-  if (!mx::batch_invariant() && mx::small_m_fused(M, N, K))   // decode: quantizer fused in
+  if (mx::batch_invariant() ? mx::small_m_invariant(M, N, K, false)
+                            : mx::small_m_fused(M, N, K))   // decode: quantizer fused in
     return hip_status(mx::launch_linear_small_m(x_bf16, nullptr, false, M, K,
                                                 (const uint8_t*)packed, N, fmt,
                                                 (const uint16_t*)bias, (uint16_t*)y, s),
@@ -361,7 +362,8 @@ int mxfp8_linear_batched(const void* x_bf16, int64_t B, int64_t M, int64_t K, co
   bs.w = P;
   bs.y = M * N * 2;
   bs.bias = bias ? N * 2 : 0;
-  if (!mx::batch_invariant() && mx::small_m_fused(M, N, K)) {
+  if (mx::batch_invariant() ? mx::small_m_invariant(M, N, K, false)
+                            : mx::small_m_fused(M, N, K)) {
     bs.x = M * K * 2;
     return hip_status(mx::launch_linear_small_m(x_bf16, nullptr, false, M, K,
                                                 (const uint8_t*)packed, N, fmt,

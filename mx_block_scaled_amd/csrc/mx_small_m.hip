@@ -308,7 +308,12 @@ __device__ __forceinline__ void rs_tile_of(int i, int G, int R, int& c, int& t) 
 // QR: rows quantized per workgroup, >= the rows of its tile (rows past the tile repeat its
 // last row; they are never read), so that the row loops have no branches.  RT: rows per row
 // tile (used with F > 1; with F == 1 the workgroup takes all M rows).
-template <int WFMT, int NQ, int MT, int F, int KMAX, int QR>
+// SEQ (batch-invariant mode): weight wave w holds the contiguous K groups [w GPW, w GPW + GPW)
+// instead of w, w + NW, .., and the waves extend one accumulator chain in turn (wave w starts
+// from wave w - 1's sums, passed through LDS) instead of adding partials: every output then
+// takes its K steps in order, one MFMA each, from a zero start, exactly as the tiled and
+// generic GEMM kernels do, so its bits do not depend on M or on the kernel.
+template <int WFMT, int NQ, int MT, int F, int KMAX, int QR, bool SEQ>
 __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_linear_small_m_rs(const uint16_t* __restrict__ x, int M,
                                                            int K, const uint8_t* __restrict__ packed,
                                                            int N, const uint16_t* __restrict__ bias,
@@ -329,6 +334,7 @@ __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_line
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int NG = N >> 4, KT = K >> 7, KT4 = (KT + 3) >> 2, KB = K >> 5;
+  const int GPW = (KT4 + R::NW - 1) / R::NW;              // K groups per weight wave (SEQ)
   const int P = K + 16;                                   // code row pitch
   uint8_t* const codes = lds;                             // [ROWS][P]
   uint8_t* const scl = lds + R::ROWS * P;                 // [ROWS][KB]
@@ -386,8 +392,8 @@ __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_line
     const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * FB) + (int64_t)ng * 64 + lane;
 #pragma unroll
     for (int i = 0; i < R::GMAX; ++i) {
-      const int kt4 = w + R::NW * i;
-      if (kt4 < KT4) {                                    // wave-uniform
+      const int kt4 = SEQ ? w * GPW + i : w + R::NW * i;
+      if (kt4 < KT4 && (!SEQ || i < GPW)) {               // wave-uniform
 #pragma unroll
         for (int f = 0; f < F; ++f) sw[i][f] = wsc[(int64_t)kt4 * NG * 64 + 64 * f];
 #pragma unroll
@@ -413,20 +419,15 @@ __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_line
   }
   rs_lds_barrier();   // the code image is complete
 
-  if (wave >= NQ) {
-    const int w = wave - NQ;
+  // this weight wave's K groups onto the accumulators, in K order
+  auto mfma_groups = [&](v4f (&acc)[MT][F], int w) __attribute__((always_inline)) {
     int mrow[MT];     // rows past the tile read its last row: their outputs are not stored
 #pragma unroll
     for (int t = 0; t < MT; ++t) mrow[t] = min(16 * t + r, M - 1);
-    v4f acc[MT][F];
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int f = 0; f < F; ++f) acc[t][f] = (v4f){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < R::GMAX; ++i) {
-      const int kt4 = w + R::NW * i;
-      if (kt4 < KT4) {
+      const int kt4 = SEQ ? w * GPW + i : w + R::NW * i;
+      if (kt4 < KT4 && (!SEQ || i < GPW)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kt = 4 * kt4 + j;
@@ -445,17 +446,50 @@ __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_line
         }
       }
     }
+  };
+  if constexpr (SEQ) {
+    // one chain per output pair, red[pair][64]: weight wave w extends it in segment w (a
+    // wave with no K group leaves it alone); every wave passes the NW barriers
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+    for (int seg = 0; seg < R::NW; ++seg) {
+      if (wave - NQ == seg && seg * GPW < KT4) {          // wave-uniform
+        v4f acc[MT][F];
 #pragma unroll
-      for (int f = 0; f < F; ++f) red[((w * MT + t) * F + f) * 64 + lane] = acc[t][f];
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int f = 0; f < F; ++f)
+            acc[t][f] = seg == 0 ? (v4f){0.f, 0.f, 0.f, 0.f} : red[(t * F + f) * 64 + lane];
+        mfma_groups(acc, seg);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int f = 0; f < F; ++f) red[(t * F + f) * 64 + lane] = acc[t][f];
+      }
+      rs_lds_barrier();
+    }
+  } else {
+    if (wave >= NQ) {
+      const int w = wave - NQ;
+      v4f acc[MT][F];
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int f = 0; f < F; ++f) acc[t][f] = (v4f){0.f, 0.f, 0.f, 0.f};
+      mfma_groups(acc, w);
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int f = 0; f < F; ++f) red[((w * MT + t) * F + f) * 64 + lane] = acc[t][f];
+    }
+    rs_lds_barrier();   // the partials are in
   }
-  rs_lds_barrier();   // the partials are in
   if (wave >= NQ && wave - NQ < R::PAIRS) {
     const int pr = wave - NQ, t = pr / F, f = pr % F;
     v4f s4 = red[pr * 64 + lane];
+    if constexpr (!SEQ) {
 #pragma unroll
-    for (int w = 1; w < R::NW; ++w) s4 += red[(w * R::PAIRS + pr) * 64 + lane];
+      for (int w = 1; w < R::NW; ++w) s4 += red[(w * R::PAIRS + pr) * 64 + lane];
+    }
     const int n = 16 * (ng + f) + 4 * g;                  // this lane's 4 output columns
     float bv[4] = {0.f, 0.f, 0.f, 0.f};
     if (bias8) {
@@ -920,15 +954,18 @@ bool small_m_fused(int64_t M, int64_t N, int64_t K) {
   return M >= 1 && K % 128 == 0 && (M <= 16 || small_m_rs(M, N, K));
 }
 bool small_m_quantized(int64_t M, int64_t K) { return M >= 1 && M <= 32 && K % 128 == 0; }
+bool small_m_invariant(int64_t M, int64_t N, int64_t K, bool quantized) {
+  return !quantized && M <= 32 && small_m_rs(M, N, K);
+}
 
 // the role-split kernel with the smallest code image and row count that hold a row tile of RT
 // rows; four quantizer waves for one or two rows (fewer waves in the workgroup) and beside the
 // eight weight waves of four fragments per workgroup, eight otherwise
-template <int WFMT, int MT, int F, int KMAX>
+template <int WFMT, int MT, int F, int KMAX, bool SEQ>
 static void launch_rs_k(const uint16_t* x, int M, int K, const uint8_t* packed, int N,
                         const uint16_t* bias, uint16_t* y, hipStream_t s, dim3 grid,
                         const BatchStrides& bs, int RT) {
-#define MX_RS(NQ, QR) hipLaunchKernelGGL((k_linear_small_m_rs<WFMT, NQ, MT, F, KMAX, QR>), grid, dim3(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)), 0, s, x, M, K, packed, N, bias, y, bs, RT)
+#define MX_RS(NQ, QR) hipLaunchKernelGGL((k_linear_small_m_rs<WFMT, NQ, MT, F, KMAX, QR, SEQ>), grid, dim3(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)), 0, s, x, M, K, packed, N, bias, y, bs, RT)
   if constexpr (F == 4) {
     if (RT <= 12) MX_RS(4, 12);
     else MX_RS(4, 16);
@@ -944,7 +981,7 @@ static void launch_rs_k(const uint16_t* x, int M, int K, const uint8_t* packed, 
   }
 #undef MX_RS
 }
-template <int WFMT>
+template <int WFMT, bool SEQ>
 static void launch_rs(const uint16_t* x, int M, int K, const uint8_t* packed, int N,
                       const uint16_t* bias, uint16_t* y, hipStream_t s, int batch,
                       const BatchStrides& bs) {
@@ -952,16 +989,21 @@ static void launch_rs(const uint16_t* x, int M, int K, const uint8_t* packed, in
   if (F > 0) {                                  // R row tiles of RT rows, F fragments
     const int R0 = (M + 15) / 16, RT = (M + R0 - 1) / R0, R = (M + RT - 1) / RT;
     const dim3 grid((unsigned)(N / (16 * F) * R), (unsigned)batch);
-    if (F == 2) launch_rs_k<WFMT, 1, 2, 4096>(x, M, K, packed, N, bias, y, s, grid, bs, RT);
-    else launch_rs_k<WFMT, 1, 4, 4096>(x, M, K, packed, N, bias, y, s, grid, bs, RT);
+    if (F == 2) {
+      launch_rs_k<WFMT, 1, 2, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, RT);
+    } else {
+      // four fragments: not in the accumulator-chain form (small_m_invariant stops at 32 rows),
+      // whose registers would spill
+      if constexpr (!SEQ) launch_rs_k<WFMT, 1, 4, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, RT);
+    }
     return;
   }
   const dim3 grid((unsigned)(N / 16), (unsigned)batch);
   if (M <= 16) {
-    if (K <= 4096) launch_rs_k<WFMT, 1, 1, 4096>(x, M, K, packed, N, bias, y, s, grid, bs, M);
-    else launch_rs_k<WFMT, 1, 1, 8192>(x, M, K, packed, N, bias, y, s, grid, bs, M);
+    if (K <= 4096) launch_rs_k<WFMT, 1, 1, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, M);
+    else launch_rs_k<WFMT, 1, 1, 8192, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, M);
   } else {
-    launch_rs_k<WFMT, 2, 1, 4096>(x, M, K, packed, N, bias, y, s, grid, bs, M);
+    launch_rs_k<WFMT, 2, 1, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, M);
   }
 }
 
@@ -971,8 +1013,10 @@ static void launch_small(const void* x, const uint8_t* xs, bool quantized, int M
                          hipStream_t s, int batch, const BatchStrides& bs) {
   const dim3 grid((unsigned)(N / 16), (unsigned)batch), block(512);
   const bool xs16 = ((uintptr_t)xs & 15) == 0 && K % 512 == 0;   // then K / 32 % 16 == 0 too
-  if (!quantized && small_m_rs(M, N, K))
-    launch_rs<WFMT>((const uint16_t*)x, M, K, packed, N, bias, y, s, batch, bs);
+  if (!quantized && small_m_rs(M, N, K) && batch_invariant())
+    launch_rs<WFMT, true>((const uint16_t*)x, M, K, packed, N, bias, y, s, batch, bs);
+  else if (!quantized && small_m_rs(M, N, K))
+    launch_rs<WFMT, false>((const uint16_t*)x, M, K, packed, N, bias, y, s, batch, bs);
   else if (!quantized)
     hipLaunchKernelGGL((k_linear_small_m<WFMT, 1, false, false>), grid, block, 0, s, x, xs, M, K, packed, N, bias, y, bs);
   else if (M <= 16 && xs16)
@@ -990,6 +1034,7 @@ hipError_t launch_linear_small_m(const void* x, const uint8_t* xs, bool quantize
                                  const uint16_t* bias, uint16_t* y, hipStream_t s, int batch,
                                  BatchStrides bs) {
   if (quantized ? !small_m_quantized(M, K) : !small_m_fused(M, N, K)) return hipErrorInvalidValue;
+  if (batch_invariant() && !small_m_invariant(M, N, K, quantized)) return hipErrorInvalidValue;
   const int m = (int)M, k = (int)K, n = (int)N;
   switch (fmt) {
     case 0: launch_small<0>(x, xs, quantized, m, k, packed, n, bias, y, s, batch, bs); break;

@@ -383,14 +383,18 @@ def test_tiled_kernel_many_tiles(K, fmt):
 
 
 @pytest.mark.parametrize("fmt", [0, 2])
-@pytest.mark.parametrize("K", [512, 4224, 544])
-def test_batch_invariant_mode(K, fmt):
+@pytest.mark.parametrize("K,N", [(512, 272), (4224, 272), (544, 272), (512, 256), (4096, 1024)])
+def test_batch_invariant_mode(K, N, fmt):
     """Batch-invariant mode: the first rows of a 300-row call (tiled kernel; K % 128 != 0:
     generic kernel) are bit-identical to the same rows called alone at M = 1, 8, 16, 17, 31
-    and 32 (generic kernel, one and two activation tiles), on both entries, with E4M3 and E2M3
-    weights; the mode's result is checked against the oracle."""
-    g = np.random.default_rng(K + fmt)
-    M, N = 300, 272
+    and 32, on both entries, with E4M3 and E2M3 weights; the mode's result is checked against
+    the oracle.  The rows called alone run on the role-split kernel with its weight waves
+    extending one accumulator chain in K order (the bf16 entry: one row tile up to 16 rows,
+    K <= 8192; two 16-row activation tiles in one row tile up to 24 rows where N % 32 != 0;
+    two row tiles from 17 rows where N % 32 == 0, K <= 4096) and on the generic kernel
+    elsewhere (the pre-quantized entry, K % 128 != 0, 31 and 32 rows at N = 272)."""
+    g = np.random.default_rng(K + fmt + N)
+    M = 300
     xf = g.standard_normal((M, K)).astype(np.float32)
     xf[:, g.choice(K, 4, replace=False)] *= 50.0                     # outlier channels
     x = synth.bf16_bits(xf)
@@ -413,7 +417,7 @@ def test_batch_invariant_mode(K, fmt):
     finally:
         mxfp8.set_batch_invariant(False)
     ref, _, _ = orc.linear_ref(x, wq, ws, fmt, b)
-    ok, rep = tolerance.check(host_bf16_bits(y_all), ref, name="batch-invariant-%d-%d" % (K, fmt))
+    ok, rep = tolerance.check(host_bf16_bits(y_all), ref, name="batch-invariant-%d-%d-%d" % (K, N, fmt))
     assert ok, rep
 
 
@@ -446,6 +450,32 @@ def test_batched(M, N, K):
     ref, _, _ = orc.linear_ref(xs_[1], layers[1][1], layers[1][2], 0, bs_[1])
     ok, rep = tolerance.check(host_bf16_bits(y[1]), ref, name="batched-%d-%d-%d" % (M, N, K))
     assert ok, rep
+
+
+@pytest.mark.parametrize("M", [8, 24])
+def test_batched_batch_invariant(M):
+    """The batched layer in batch-invariant mode (the role-split kernel's in-order chain, one and
+    two row tiles): every batch equals its rows of a 300-row call of the same layer, bit for
+    bit."""
+    Bn, N, K = 3, 256, 1024
+    g = np.random.default_rng(M + 5)
+    xs_ = [synth.bf16_bits(g.standard_normal((300, K)).astype(np.float32)) for _ in range(Bn)]
+    ws_ = [synth.bf16_bits((g.standard_normal((N, K)) * 0.03).astype(np.float32)) for _ in range(Bn)]
+    bs_ = [synth.bf16_bits((g.standard_normal(N) * 0.1).astype(np.float32)) for _ in range(Bn)]
+    banner("batched, batch-invariant mode", Bn, M, N, K)
+    layers = [_layer(ws_[b], 0, bs_[b]) for b in range(Bn)]
+    packed = torch.cat([l[0].packed for l in layers])
+    bias = torch.stack([bf16_dev(bb) for bb in bs_])
+    x_all = [bf16_dev(xx) for xx in xs_]
+    x = torch.stack([xx[:M] for xx in x_all])
+    mxfp8.set_batch_invariant(True)
+    try:
+        y = mxfp8.linear_batched(x, packed, N, 0, bias)
+        for b in range(Bn):
+            y_all = layers[b][0](x_all[b])
+            assert torch.equal(y[b].view(torch.int16), y_all[:M].view(torch.int16)), b
+    finally:
+        mxfp8.set_batch_invariant(False)
 
 
 @pytest.mark.parametrize("tile", [(7, 36), (6, 36), (7, 4)])

@@ -246,17 +246,23 @@ int mxfp8_linear_prequant_fmt(const void* xq, const void* xs, int64_t M, int64_t
 /* ---------------------------------------------------------------- modes and tuning */
 
 /* Batch-invariant mode (aiter_flydsl page, is_supported: its split-K kernel is not batch
- * invariant).  on != 0: every M runs on kernels that add the K steps of an output in
- * sequence, so a row's result does not depend on how many rows the call has (the small-M
- * kernels, which split K over waves, are not used).  on == 0 (default): fastest kernel per
- * shape.  Returns MX_OK.
- * Thread safety: the mode is one process-wide atomic flag, read by each call while it picks
- * its kernels.  Calls made after this function returns (on any thread) use the new mode.  A
- * call running on another thread while the mode changes may pick some of its kernels under
- * either mode: its result is still correct (within the layer's tolerance) and it still needs
- * only mxfp8_workspace_bytes of workspace, but it is batch invariant only if it started after
- * mxfp8_set_batch_invariant(1) returned.  Already enqueued work is never affected. */
+ * invariant).  on != 0: every M runs on kernels that add the K steps of each output in order,
+ * one MFMA per 128-wide step from a zero start (the tiled and generic GEMMs, and up to 32 rows
+ * on the bf16 entry the role-split small-M kernel with its waves extending one accumulator
+ * chain in turn), so a row's result does not depend on how many rows the call has; the split-K
+ * kernels are not used.  on == 0 (default): fastest kernel per shape.  Returns MX_OK.
+ * Thread safety: the mode is one process-wide atomic flag.  Each call reads the mode that
+ * applies to it once, when it starts, and picks all of its kernels under that mode, so a call
+ * running on another thread while the mode changes runs entirely under the old mode or
+ * entirely under the new one.  Already enqueued work is never affected.  A thread that must
+ * not depend on other threads' settings uses mxfp8_set_batch_invariant_thread. */
 int mxfp8_set_batch_invariant(int on);
+
+/* Batch-invariant mode for the calling thread only (for callers that cannot share a
+ * process-wide mode): mode 1 = on, 0 = off for this thread's calls whatever the process-wide
+ * setting; -1 = follow mxfp8_set_batch_invariant again (the initial state of every thread).
+ * Other threads are not affected.  Returns MX_OK, or MX_EINVAL for any other mode. */
+int mxfp8_set_batch_invariant_thread(int mode);
 
 
 /* Tuning / testing hook: force the tile of the LDS-tiled GEMM used for large M.
@@ -273,8 +279,8 @@ int mxfp8_set_batch_invariant(int on);
  *     rows);
  *   (0,0) restores the automatic choice.  MX_EINVAL for any other pair.
  * A forced tile also turns off the split-K tiled path.  Thread safety as for
- * mxfp8_set_batch_invariant: one process-wide atomic setting, read by each call when it
- * launches; a call concurrent with a change runs with either setting (each correct). */
+ * mxfp8_set_batch_invariant: one process-wide atomic setting, read once by each call when it
+ * starts; a call concurrent with a change runs entirely with the old or the new setting. */
 int mxfp8_set_tile_config(int fn, int fm);
 
 #ifdef __cplusplus

@@ -171,6 +171,7 @@ int linear_check(const void* x_bf16, int64_t M, int64_t K, const void* packed, i
 
 int linear_launch(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N, int fmt,
                   const void* bias, void* y, void* workspace, void* stream) {
+  CallSettings settings;   // the modes of this call, read once
   hipStream_t s = (hipStream_t)stream;
   if (!mx::batch_invariant() && sk_shape(M, N, K))   // decode: K split across workgroups
     return hip_status(mx::launch_linear_decode_sk((const uint16_t*)x_bf16, M, K,
@@ -328,6 +329,7 @@ int mxfp8_linear(const void* x_bf16, int64_t M, int64_t K, const void* packed, i
 
 int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K, const void* packed,
                           int64_t N, int fmt, const void* bias, void* y, void* stream) {
+  mx::CallSettings settings;   // the modes of this call, read once
   int rc = check_linear_common(M, K, packed, N, fmt, y);
   if (rc) return rc;
   if (M == 0) return ok();
@@ -343,6 +345,7 @@ int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K, 
 int mxfp8_linear_batched(const void* x_bf16, int64_t B, int64_t M, int64_t K, const void* packed,
                          int64_t N, int fmt, const void* bias, void* y, void* workspace,
                          int64_t ws_bytes, void* stream) {
+  mx::CallSettings settings;   // the modes of this call, read once
   if (B < 0) return fail(MX_ESHAPE, "B = %lld is negative", (long long)B);
   if (B > 0 && M > 0 && B * M / B != M) return fail(MX_ESHAPE, "B x M overflows");
   int rc = check_linear_common(B * M, K, packed, N, fmt, y);
@@ -384,6 +387,7 @@ int mxfp8_linear_batched(const void* x_bf16, int64_t B, int64_t M, int64_t K, co
 int mxfp8_linear_prequant_batched(const void* xq, const void* xs, int64_t B, int64_t M, int64_t K,
                                   const void* packed, int64_t N, int fmt, const void* bias,
                                   void* y, void* stream) {
+  mx::CallSettings settings;   // the modes of this call, read once
   if (B < 0) return fail(MX_ESHAPE, "B = %lld is negative", (long long)B);
   if (B > 0 && M > 0 && B * M / B != M) return fail(MX_ESHAPE, "B x M overflows");
   int rc = check_linear_common(B * M, K, packed, N, fmt, y);
@@ -433,6 +437,7 @@ int64_t mxfp8_workspace_bytes_fmt(int64_t M, int64_t N, int64_t K, int fmt, int 
 int mxfp8_linear_fmt(const void* x_bf16, int64_t M, int64_t K, const void* packed, int64_t N,
                      int fmt, int afmt, const void* bias, void* y, void* workspace,
                      int64_t ws_bytes, void* stream) {
+  mx::CallSettings settings;   // the modes of this call, read once
   int rc = check_fmt_pair(fmt, afmt);
   if (rc) return rc;
   if (afmt == MX_FMT_E4M3)
@@ -460,6 +465,7 @@ int mxfp8_linear_fmt(const void* x_bf16, int64_t M, int64_t K, const void* packe
 int mxfp8_linear_prequant_fmt(const void* xq, const void* xs, int64_t M, int64_t K, int afmt,
                               const void* packed, int64_t N, int fmt, const void* bias, void* y,
                               void* stream) {
+  mx::CallSettings settings;   // the modes of this call, read once
   int rc = check_fmt_pair(fmt, afmt);
   if (rc) return rc;
   if (afmt == MX_FMT_E4M3)
@@ -496,6 +502,12 @@ int mxfp8_rmsnorm_quantize_act(const void* x_bf16, int64_t M, int64_t K, int64_t
 
 int mxfp8_set_batch_invariant(int on) {
   mx::set_batch_invariant(on != 0);
+  return ok();
+}
+
+int mxfp8_set_batch_invariant_thread(int mode) {
+  if (mode < -1 || mode > 1) return fail(MX_EINVAL, "mode %d is not -1, 0 or 1", mode);
+  mx::set_batch_invariant_thread(mode);
   return ok();
 }
 

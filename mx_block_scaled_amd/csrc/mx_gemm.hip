@@ -1435,13 +1435,38 @@ int64_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
 // counts the tiles of all its layers.
 struct TileChoice { int fn, fm; };
 // compiled tiles (fn, fm) -> workgroup tile 32 fn x 64 fm, two LDS stages
+//
+// The two settings are process-wide atomics; batch-invariant mode can also be set for one
+// thread.  A call reads each setting once, when it starts (CallSettings at every launching
+// entry point), and all its kernel choices use that snapshot.
 static std::atomic<int> g_force_tile{0};   // fn * 256 + fm, 0 = automatic
-void force_tile(int fn, int fm) { g_force_tile.store(fn * 256 + fm); }
 static std::atomic<bool> g_batch_invariant{false};
+static thread_local int tl_batch_invariant = -1;   // this thread's mode; -1: the process-wide one
+static thread_local int tl_call_bi = -1;           // the running call's snapshot, -1: none
+static thread_local int tl_call_tile = -1;
+void force_tile(int fn, int fm) { g_force_tile.store(fn * 256 + fm); }
 void set_batch_invariant(bool on) { g_batch_invariant.store(on); }
-bool batch_invariant() { return g_batch_invariant.load(std::memory_order_relaxed); }
+void set_batch_invariant_thread(int mode) { tl_batch_invariant = mode < 0 ? -1 : (mode != 0); }
+static bool batch_invariant_now() {
+  return tl_batch_invariant >= 0 ? tl_batch_invariant != 0
+                                 : g_batch_invariant.load(std::memory_order_relaxed);
+}
+bool batch_invariant() { return tl_call_bi >= 0 ? tl_call_bi != 0 : batch_invariant_now(); }
+static int forced_tile() {
+  return tl_call_tile >= 0 ? tl_call_tile : g_force_tile.load(std::memory_order_relaxed);
+}
+CallSettings::CallSettings() : bi_(tl_call_bi), tile_(tl_call_tile) {
+  if (tl_call_bi < 0) {   // the outermost scope of a call takes the snapshot
+    tl_call_bi = batch_invariant_now();
+    tl_call_tile = g_force_tile.load(std::memory_order_relaxed);
+  }
+}
+CallSettings::~CallSettings() {
+  tl_call_bi = bi_;
+  tl_call_tile = tile_;
+}
 static TileChoice choose_tile(int M, int N, int batch, bool w4_ok) {
-  const int f = g_force_tile.load(std::memory_order_relaxed);
+  const int f = forced_tile();
   // a forced four-wave tile (fm == 16) applies only where that kernel does
   if (f && ((f % 256 != 16 && f % 256 != 36) || w4_ok)) return TileChoice{f / 256, f % 256};
   static const TileChoice opts[] = {{8, 4}, {7, 4}, {6, 4}, {4, 4}, {4, 2}};
@@ -1463,7 +1488,7 @@ static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int 
                                const uint8_t* packed, int N, const uint16_t* bias, uint16_t* y,
                                hipStream_t s, int batch, const BatchStrides& bs, float* part) {
   const int group_m = 4;
-  const int parts = part && batch == 1 && !batch_invariant() && g_force_tile.load() == 0
+  const int parts = part && batch == 1 && !batch_invariant() && forced_tile() == 0
                         ? gemm_split_parts(M, N, K) : 1;
   if (parts > 1) {
     // too few 128 x 128 tiles for the CUs: K parts on grid z, then the ordered sum
@@ -1479,7 +1504,7 @@ static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int 
     // the ping-pong kernel wherever it applies (E4M3 operands, whole scale groups): chosen
     // tiles 224 x 256, 192 x 256 and 128 x 256, or forced as (fn, 36); a forced (fn, 4) keeps
     // the all-waves-in-step kernel
-    const int f = g_force_tile.load(std::memory_order_relaxed);
+    const int f = forced_tile();
     const bool pp_tile = c.fm == 36 || (f == 0 && c.fm == 4 && (c.fn == 7 || c.fn == 6 || c.fn == 4));
     if (pp_tile && K % 512 == 0) {
       if (c.fn == 6) launch_pp<0, 0, 6, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s, batch, bs);

@@ -47,9 +47,24 @@ hipError_t launch_unpack_shuffled16(const uint8_t* packed, int64_t N, int64_t K,
 
 // Force the tiled GEMM's tile (fragments per wave along n and m); (0, 0) = automatic.
 void force_tile(int fn, int fm);
-// Batch-invariant mode: no small-M (split-K) kernels, so a row's result does not depend on M.
+// Batch-invariant mode: only kernels that add each output's K steps in order, so a row's result
+// does not depend on M.  Process-wide, or for the calling thread (mode 0 / 1; -1 returns the
+// thread to the process-wide setting).
 void set_batch_invariant(bool on);
+void set_batch_invariant_thread(int mode);
+// The mode that applies to the call being launched (its snapshot inside a CallSettings scope).
 bool batch_invariant();
+// Snapshot of the mode and the forced tile for one call: every entry point that launches
+// kernels holds one for its duration, so that all of its kernel choices agree even while
+// another thread changes the settings.
+struct CallSettings {
+  CallSettings();
+  ~CallSettings();
+  CallSettings(const CallSettings&) = delete;
+  CallSettings& operator=(const CallSettings&) = delete;
+ private:
+  int bi_, tile_;
+};
 
 // GEMM from quantized activations xq + xs [M, K/32] (row-major): xq is E4M3 [M, K] (afmt 0)
 // or, with FP6 weights, packed E2M3 / E3M2 [M, 3K/4] (afmt 2 / 3).  With `part` (room for

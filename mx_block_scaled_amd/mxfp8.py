@@ -22,6 +22,7 @@ __all__ = [
     "prepack_weight_shuffled16", "unpack_weight_shuffled16", "linear_batched",
     "linear_prequant_batched", "quantize_act_fmt", "workspace_bytes_fmt", "linear_fmt",
     "linear_prequant_fmt", "rmsnorm_quantize_act", "new_workspace", "linear_noalloc",
+    "set_batch_invariant_thread",
     "NOALLOC_SCRATCH_BYTES",
 ]
 
@@ -61,6 +62,7 @@ def lib():
             "mxfp8_linear_prequant": (I, [P, P, I64, I64, P, I64, I, P, P, P]),
             "mxfp8_set_tile_config": (I, [I, I]),
             "mxfp8_set_batch_invariant": (I, [I]),
+            "mxfp8_set_batch_invariant_thread": (I, [I]),
             "mxfp8_linear_batched": (I, [P, I64, I64, I64, P, I64, I, P, P, P, I64, P]),
             "mxfp8_linear_prequant_batched": (I, [P, P, I64, I64, I64, P, I64, I, P, P, P]),
             "mxfp8_prepack_weight_shuffled16": (I, [P, P, I64, I64, I64, P, P]),
@@ -174,6 +176,12 @@ def set_tile_config(fn=0, fm=0):
 def set_batch_invariant(on=True):
     """Batch-invariant mode: a row's result no longer depends on the number of rows M."""
     _check(lib().mxfp8_set_batch_invariant(1 if on else 0))
+
+
+def set_batch_invariant_thread(mode):
+    """Batch-invariant mode for the calling thread only: True / False, or None to follow the
+    process-wide setting again."""
+    _check(lib().mxfp8_set_batch_invariant_thread(-1 if mode is None else (1 if mode else 0)))
 
 
 def device_supported(device=0):

@@ -148,6 +148,10 @@ def test_shuffled16_and_mode_validation(L):
     assert L.mxfp8_unpack_weight_shuffled16(B + 8, 256, 512, A, A, None) == MX_EALIGN
     assert L.mxfp8_set_batch_invariant(1) == MX_OK
     assert L.mxfp8_set_batch_invariant(0) == MX_OK
+    for mode in (1, 0, -1):
+        assert L.mxfp8_set_batch_invariant_thread(mode) == MX_OK
+    assert L.mxfp8_set_batch_invariant_thread(2) == MX_EINVAL
+    assert L.mxfp8_set_batch_invariant_thread(-2) == MX_EINVAL
 
 
 def test_batched_validation(L):

@@ -452,6 +452,62 @@ def test_batched(M, N, K):
     assert ok, rep
 
 
+def test_batch_invariant_mode_per_thread():
+    """The per-thread mode, seen through the workspace: at M = 8, K = 8320 the normal path
+    (small-M kernel, quantizer fused in) never touches the workspace, while batch-invariant mode
+    quantizes into it first and then runs the generic kernel.  A thread with mode on gets the
+    quantized rows in its workspace and the 300-row call's bits while the process-wide mode is
+    off; a thread with mode off leaves its workspace alone while the process-wide mode is on;
+    a thread back at -1 follows the process-wide mode."""
+    import threading
+    g = np.random.default_rng(3)
+    M, N, K, m = 300, 256, 8320, 8
+    x = bf16_dev(synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32)))
+    w = synth.bf16_bits((g.standard_normal((N, K)) * 0.03).astype(np.float32))
+    layer, _, _ = _layer(w, 0, None)
+    banner("batch-invariant mode per thread", N, K)
+    y_all = layer(x)                                  # tiled: the same bits in either mode
+    xm = x[:m].contiguous()
+    normal = layer(xm)
+    xq, _ = mxfp8.quantize_act(xm)
+    need = mxfp8.workspace_bytes(m, N, K)
+    torch.cuda.synchronize()
+    out, err = {}, []
+
+    def run(name, mode):
+        try:
+            mxfp8.set_batch_invariant_thread(mode)
+            ws = mxfp8.new_workspace(need, DEV)
+            ws[65536:].fill_(0xA5)
+            y = mxfp8.linear(xm, layer.packed, N, 0, None, workspace=ws)
+            torch.cuda.synchronize()
+            out[name] = (y, bool(torch.equal(ws[65536:65536 + m * K], xq.view(-1))),
+                         bool((ws[65536:] == 0xA5).all()))
+        except Exception as e:   # reported by the main thread
+            err.append(e)
+        finally:
+            mxfp8.set_batch_invariant_thread(None)
+
+    try:
+        for proc_mode in (False, True):
+            mxfp8.set_batch_invariant(proc_mode)
+            ts = [threading.Thread(target=run, args=("on", True)),
+                  threading.Thread(target=run, args=("off", False)),
+                  threading.Thread(target=run, args=("follow", None))]
+            for t in ts:
+                t.start()
+            for t in ts:
+                t.join()
+            assert not err, err
+            for name, on in (("on", True), ("off", False), ("follow", proc_mode)):
+                y, quantized_into_ws, untouched = out[name]
+                assert quantized_into_ws == on and untouched == (not on), (proc_mode, name)
+                want = y_all[:m] if on else normal
+                assert torch.equal(y.view(torch.int16), want.view(torch.int16)), (proc_mode, name)
+    finally:
+        mxfp8.set_batch_invariant(False)
+
+
 @pytest.mark.parametrize("M", [8, 24])
 def test_batched_batch_invariant(M):
     """The batched layer in batch-invariant mode (the role-split kernel's in-order chain, one and

@@ -20,9 +20,9 @@ Also measured and printed in the same JSON line:
                 the 5.0 PFLOP/s dense FP8 peak, and against the attainable peak that the MFMA
                 loop of libmxpeaks measures on the same chip; traffic from the committed
                 rocprofv3 counter summary while the kernel source still matches it, else null;
-  clock         the shader clock the chip runs at under back-to-back GEMMs and steps: a one-wave
-                probe on a second stream counts shader-clock cycles against the 100 MHz
-                counter while the calls run;
+  clock         the shader clock the chip runs at under back-to-back GEMMs: a one-wave probe on
+                a second stream counts shader-clock cycles against the 100 MHz counter while
+                the calls run;
   attainable    the MFMA-loop peaks (FP8 x FP8, FP8 x FP6, FP6 x FP6) and the HBM stream-read
                 rate of 1 GiB, measured in this run;
   decode        the decode workload (x [M, 4096], M in {1, 8, 32}, weight [4096, 4096], bias),
@@ -36,7 +36,8 @@ Also measured and printed in the same JSON line:
                 (both MFMA operands FP6), each over enough rotated sets to exceed the Infinity
                 Cache; the fused RMS norm + MXFP8 quantizer on the prefill activations against a
                 torch RMS norm followed by the standalone quantizer; the latency of one tiny
-                call (16 x 256 x 512) from a HIP graph; the batched layer;
+                call (16 x 256 x 512) from a HIP graph; the batched layer.  Each is timed after
+                --settle-ms / 2 of its own calls, as the median of 5 loops (HIP events);
   cpu_baseline  the CPU oracle on bounded samples of the prefill workload (host cores), run in
                 separate processes (oracle/cpu_bench.py): the whole layer (value), and the
                 quantizer (GB/s) and fp64 GEMM (GFLOP/s) apart, on all cores and on one thread.
@@ -132,16 +133,16 @@ def cu_rates(L):
 
 def clock_under(L, fn, calls, probe_ms):
     """Shader clock (MHz) while fn(i) runs ``calls`` times back to back: a one-wave probe on a
-    second stream waits ``probe_ms`` inside that stretch and counts the shader-clock cycles
-    (s_memtime) against the 100 MHz counter (s_memrealtime)."""
+    second stream, launched just before the calls so that it is resident while they run,
+    counts the shader-clock cycles (s_memtime) against the 100 MHz counter (s_memrealtime) for
+    ``probe_ms``.  (Enqueued behind queued calls instead, the probe started only after the
+    quantizer + GEMM steps had drained and read the idle clock.)"""
     import torch
     out = torch.zeros(2, dtype=torch.int64, device="cuda")
     side = torch.cuda.Stream()
-    head = max(1, calls // 5)
-    for i in range(head):
-        fn(i)
+    torch.cuda.synchronize()
     assert L.mxpk_clock_probe(int(probe_ms * 1e5), out.data_ptr(), side.cuda_stream) == 0
-    for i in range(head, calls):
+    for i in range(calls):
         fn(i)
     torch.cuda.synchronize()
     cyc, ticks = out.cpu().tolist()
@@ -450,15 +451,14 @@ def main():
     att_fp8 = (attainable.get("mfma_TFLOPs") or {}).get("fp8xfp8")
     att_fp8_rand = (attainable.get("mfma_TFLOPs") or {}).get("fp8xfp8_random")
     att_hbm = attainable.get("hbm_GBs")
-    # achieved shader clock under the GEMM and under the whole step (a one-wave probe on a
-    # second stream, in a separate stretch of calls after the timed loops)
+    # achieved shader clock under the GEMM (a one-wave probe on a second stream, in a separate
+    # stretch of calls after the timed loops)
     clock = None
     if peaks_lib is not None:
         xq1, xs1 = mxfp8.quantize_act(xs_[0])
         clock = {
             "gemm_MHz": clock_under(peaks_lib, lambda i: mxfp8.linear_prequant(
                 xq1, xs1, ps_[i % R], N, "e4m3", out=ys_[i % R]), 500, 60),
-            "step_MHz": clock_under(peaks_lib, step, 500, 60),
             "mfma_loop_MHz": (attainable.get("mfma_clock_MHz") or {}).get("fp8xfp8"),
             "mfma_loop_random_operands_MHz": (attainable.get("mfma_clock_MHz") or {}).get("fp8xfp8_random"),
             "source": "s_memtime / s_memrealtime of a one-wave probe on a second stream, "
@@ -586,18 +586,34 @@ def main():
             n = max(2, -(-2 * MALL_BYTES // set_bytes))
             return [make_set(j) for j in range(n)]
 
-        def time_calls(fn, n_sets, iters):
-            for j in range(max(2 * n_sets, 100)):   # warm: every set touched, steady clock
+        timing_detail = {}
+
+        def time_calls(fn, n_sets, iters, name=None):
+            """Calls of fn for --settle-ms / 2 of GPU time (every set touched; the chip reaches
+            the steady clock of this workload: 100 calls were measured 15 % slow on the
+            outlier GEMM), then 5 loops of `iters` calls timed with HIP events on the current
+            stream: the median per call (the min goes to timing_detail[name])."""
+            j = 0
+            t_end = time.perf_counter() + args.settle_ms / 2e3
+            while j < 2 * n_sets or time.perf_counter() < t_end:
                 fn(j % n_sets)
+                j += 1
+                if j % 20 == 0:
+                    torch.cuda.synchronize()
             torch.cuda.synchronize()
             stream = torch.cuda.current_stream(dev)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(iters):
-                fn(i % n_sets)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / iters
+            per = []
+            for _ in range(5):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for i in range(iters):
+                    fn(i % n_sets)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) * 1e3 / iters)
+            if name:
+                timing_detail[name] = {"us_min": round(min(per), 2), "warm_calls": j}
+            return statistics.median(per)
 
         # outlier activations on the pre-quantized entry (GEMM only), fused-QKV shape
         do = synth.make("outlier")
@@ -611,7 +627,7 @@ def main():
                        xq_o.numel() + xs_o.numel() + pk_o.numel() + Mo * No * 2)
         us = time_calls(lambda j: mxfp8.linear_prequant(sets[j][0], sets[j][1], sets[j][2], No,
                                                         "e4m3", out=sets[j][3]),
-                        len(sets), max(50, args.steps))
+                        len(sets), max(50, args.steps), "outlier")
         fl = 2.0 * Mo * No * Ko
         others["outlier_prequant_2048x6144x4096"] = {
             "us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
@@ -634,7 +650,7 @@ def main():
             wsf = torch.zeros(mxfp8.workspace_bytes(Mf, Nf, Kf, fname), dtype=torch.uint8, device=dev)
             us = time_calls(lambda j: mxfp8.linear(sets[j][0], sets[j][1], Nf, fname,
                                                    out=sets[j][2], workspace=wsf),
-                            len(sets), max(50, args.steps))
+                            len(sets), max(50, args.steps), "mxfp6_" + fname)
             fl = 2.0 * Mf * Nf * Kf
             others["mxfp6_%s_512x8192x8192" % fname] = {
                 "us": round(us, 2), "TFLOP/s": round(fl / us / 1e6, 1),
@@ -646,7 +662,7 @@ def main():
                                dtype=torch.uint8, device=dev)
             us6 = time_calls(lambda j: mxfp8.linear_fmt(sets[j][0], sets[j][1], Nf, fname, fname,
                                                         out=sets[j][2], workspace=wsf6),
-                             len(sets), max(50, args.steps))
+                             len(sets), max(50, args.steps), "w6a6_" + fname)
             others["w6a6_%s_512x8192x8192" % fname] = {
                 "us": round(us6, 2), "TFLOP/s": round(fl / us6 / 1e6, 1),
                 "mfma_frac_fp6_rate": round(fl / us6 / 1e6 / PEAK_FP6_TFLOPS, 4),
@@ -681,8 +697,8 @@ def main():
             rc = L.mxfp8_quantize_act(yn.data_ptr(), Mp, Kp, Kp, q_.data_ptr(), s_.data_ptr(), st)
             assert rc == 0, L.mxfp8_last_error()
 
-        us_f = time_calls(fused, len(sets), max(50, args.steps))
-        us_s = time_calls(separate, len(sets), max(50, args.steps))
+        us_f = time_calls(fused, len(sets), max(50, args.steps), "producer")
+        us_s = time_calls(separate, len(sets), max(50, args.steps), "producer_torch")
         alg = 3.03125 * Mp * Kp + 2 * Kp
         others["producer_rmsnorm_quant_4096x4096"] = {
             "us": round(us_f, 2), "GB/s": round(alg / us_f / 1e3, 1),
@@ -734,14 +750,17 @@ def main():
                            dtype=torch.uint8, device=dev)   # batched call and single calls
         P = mxfp8.prepacked_bytes(Nb, Kb)
         us_b = time_calls(lambda j: mxfp8.linear_batched(xb, pkb, Nb, "e4m3", out=yb, workspace=wsb2),
-                          1, max(20, args.steps // 4))
+                          1, max(20, args.steps // 4), "batched")
         us_s = time_calls(lambda j: [mxfp8.linear(xb[b], pkb[b * P:(b + 1) * P], Nb, "e4m3",
                                                   out=yb[b], workspace=wsb2) for b in range(Bb)],
-                          1, max(20, args.steps // 4))
+                          1, max(20, args.steps // 4), "batched_separate")
         fl = 2.0 * Bb * Mb * Nb * Kb
         others["batched_8x512x4096x4096"] = {
             "us": round(us_b, 2), "TFLOP/s": round(fl / us_b / 1e6, 1),
             "us_as_8_separate_calls": round(us_s, 2)}
+        others["timing"] = {"protocol": "calls for --settle-ms / 2 of GPU time, then the median "
+                                        "of 5 loops timed with HIP events (min below)",
+                            "detail": timing_detail}
         del xb, pkb, yb, wsb2
 
     # ------------------------------------------------------------ CPU oracle baseline

@@ -11,8 +11,9 @@ driver around it.  Format and rule sources are listed in the C file's header: th
 OCP MX v1.0 conversion rule that the pages rely on without stating.
 
 Parity pins: every function here is checked in ``tests/test_oracle_*.py`` against closed forms,
-brute force, library routines or the pages' own printed inverse (none is "parity unpinned"
-except the Inf/NaN-block convention, which no workload exercises).
+brute force, library routines or the pages' own printed inverse; the Inf/NaN-block convention,
+which no workload exercises, against torch's E8M0 and E4M3FN formats (the block dequantizes to
+NaN).
 """
 from .oracle import *  # noqa: F401,F403
 from .oracle import __all__  # noqa: F401

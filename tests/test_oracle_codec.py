@@ -229,11 +229,30 @@ def test_quantize_block_structure(orc):
 
 
 def test_nonfinite_block_convention(orc):
-    """Reading (parity unpinned by the pages): a block with Inf/NaN gets scale 0xFF and NaN
-    codes for E4M3; no workload contains one."""
+    """Reading c-6 (the pages print no case): a block holding Inf or NaN has a NaN shared scale
+    (the OCP MX rule), and every element of it is NaN.  Pinned against torch's own formats, not
+    the oracle's decoder: the scale byte is the NaN of float8_e8m0fnu, the E4M3 codes are NaN
+    under float8_e4m3fn, so the block dequantizes to NaN element by element; FP6 has no NaN
+    code, and its elements are NaN through the scale.  The other block is quantized as usual."""
+    import torch
+    for bad in (0x7F80, 0xFF80, 0x7FC0):   # +Inf, -Inf, NaN
+        x = np.zeros((1, 64), np.uint16)
+        x[0, 3] = bad                      # block 0
+        x[0, 40] = 0x3F80                  # 1.0 in block 1
+        for fmt in (0, 2, 3):
+            q, s = orc.quantize(x, fmt)
+            sv = torch.tensor(s[0].astype(np.uint8)).view(torch.float8_e8m0fnu).float()
+            assert torch.isnan(sv[0]) and not torch.isnan(sv[1])
+            if fmt == 0:
+                qv = torch.tensor(q[0].astype(np.uint8)).view(torch.float8_e4m3fn).float()
+                deq = qv.reshape(2, 32) * sv[:, None]
+                assert torch.isnan(deq[0]).all() and deq[1, 8] == 1.0
+                assert not torch.isnan(deq[1]).any()
+            else:
+                deq0 = np.array([orc.decode(int(c), fmt) for c in q[0, :32]]) * float(sv[0])
+                assert np.isnan(deq0).all()
+    # the codes the oracle writes: E4M3's NaN code, FP6 zero
     x = np.zeros((1, 64), np.uint16)
-    x[0, 3] = 0x7F80                       # +Inf in block 0
-    x[0, 40] = 0x3F80                      # 1.0 in block 1
+    x[0, 3] = 0x7F80
     q, s = orc.quantize(x, 0)
-    assert s[0].tolist() == [0xFF, 119]
-    assert set(q[0, :32].tolist()) == {0x7F} and q[0, 40] == 0x78
+    assert s[0].tolist() == [0xFF, 0] and set(q[0, :32].tolist()) == {0x7F}

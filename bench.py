@@ -30,6 +30,8 @@ Also measured and printed in the same JSON line:
                 time per call, algorithmic bytes / time against 8 TB/s and against a plain
                 read of the same weight bytes replayed the same way (the stream floor); the
                 same for M = 64 and 128 (prefill chunks), and every M in batch-invariant mode;
+                and M = 1, 8, 32 eight layers per call through the batched entry (time per
+                layer);
   other_workloads  outlier activations on the pre-quantized entry (2048 x 6144 x 4096, GEMM
                 only), MXFP6 weights (E2M3 and E3M2, 512 x 8192 x 8192, activation quantization
                 included) with MXFP8 activations and with MXFP6 activations of the same format
@@ -571,7 +573,49 @@ def main():
             finally:
                 mxfp8.set_batch_invariant(False)
             del g
-        del pks, pk
+        # the same decode layers eight at a time through the batched entry (B independent
+        # layers, each with its own activations, weight and bias, in one launch), replayed from a
+        # HIP graph over the same 32 rotated weights: the weight stream of one launch is then
+        # 8 x 17.3 MB instead of 17.3 MB
+        Bd, RB = 8, 64                         # 64 weights, 1.1 GB: no reuse from the caches
+        pkb = [torch.cat([pks[(b * Bd + i) % RD] for i in range(Bd)]) for b in range(RB // Bd)]
+        biasb = bias.unsqueeze(0).repeat(Bd, 1).contiguous()
+        decode["batched8"] = {"layers_per_call": Bd, "rotated_weights": RB}
+        for Md in (1, 8, 32):
+            xb8 = torch.from_numpy(dd["x"][:Md].view(np.int16)).view(torch.bfloat16).to(dev)
+            xb8 = xb8.unsqueeze(0).repeat(Bd, 1, 1).contiguous()
+            yb8 = torch.empty((Bd, Md, Nd), dtype=torch.bfloat16, device=dev)
+            wsd = torch.zeros(max(1, mxfp8.workspace_bytes(Bd * Md, Nd, Kd)), dtype=torch.uint8,
+                              device=dev)
+            s = torch.cuda.Stream(dev)
+            s.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(s):
+                for j in range(RB // Bd):
+                    mxfp8.linear_batched(xb8, pkb[j], Nd, "e4m3", biasb, out=yb8, workspace=wsd)
+            torch.cuda.current_stream(dev).wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                for j in range(RB // Bd):
+                    mxfp8.linear_batched(xb8, pkb[j], Nd, "e4m3", biasb, out=yb8, workspace=wsd)
+            reps = max(4, args.steps // 2)
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                g.replay()
+            torch.cuda.synchronize()
+            us = (time.perf_counter() - t0) * 1e6 / (reps * RB)        # per layer
+            bytes_alg = Md * Kd * 2 + pks[0].numel() + Md * Nd * 2 + Nd * 2
+            gbs = bytes_alg / (us * 1e-6) / 1e9
+            decode["batched8"]["M%d" % Md] = {
+                "us_per_layer": round(us, 3), "GB/s": round(gbs, 1),
+                "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                "hbm_frac_attainable": round(gbs / att_hbm, 4) if att_hbm else None,
+                "x_stream_floor": round(us / floor_us, 3) if floor_us else None}
+            del g, xb8, yb8, wsd
+        del pkb, pks, pk
 
     # ------------------------------------------------------------ the other workloads
     others = None

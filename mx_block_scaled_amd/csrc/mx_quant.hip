@@ -206,18 +206,13 @@ __global__ __launch_bounds__(64 * WPR) void k_rmsnorm_quant(const uint16_t* __re
       y8[i] = (int)pack_bf16x2(__uint_as_float(t << 16) * __uint_as_float(gq << 16),
                                __uint_as_float(t & 0xFFFF0000u) * __uint_as_float(gq & 0xFFFF0000u));
     }
-    const uint32_t m = quad_max_u32(amax8_bf16(y8));
-    const uint32_t byte = scale_byte_from_amax<0>(m);
-    uint32_t q0, q1;
-    if (byte == 0xFFu) {
-      q0 = q1 = 0x7F7F7F7Fu;
-    } else {
-      const float sc = e8m0_to_float(byte);
-      q0 = cvt4_e4m3((uint32_t)y8[0], (uint32_t)y8[1], sc);
-      q1 = cvt4_e4m3((uint32_t)y8[2], (uint32_t)y8[3], sc);
-    }
+    // the MX quantization of y: packed 16-bit amax, the scale as one ldexp, converted whatever
+    // the scale (branch-free), an Inf/NaN block's codes replaced by NaN codes
+    const uint32_t byte = scale_byte_from_amax<0>(quad_max_u32(amax8_bf16_pk(y8)));
+    v2i q = cvt8_e4m3(y8, e8m0_to_float_ldexp(byte));
+    if (byte == 0xFFu) q = (v2i){0x7F7F7F7F, 0x7F7F7F7F};
     if (live) {
-      *(v2i*)(xq + (int64_t)row * K + col) = (v2i){(int)q0, (int)q1};
+      *(v2i*)(xq + (int64_t)row * K + col) = q;
       if ((lane & 3) == 0) xs[(int64_t)row * KB + (col >> 5)] = (uint8_t)byte;
       if (yout) *(v4i*)(yout + (int64_t)row * K + col) = y8;
     }

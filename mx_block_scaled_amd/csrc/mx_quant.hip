@@ -126,15 +126,40 @@ hipError_t launch_quantize_act_fp6(const uint16_t* x, int64_t M, int64_t K, int6
 // The producer of a pre-quantized activation (the Mxfp8LinearKernel page's input_quant_key lets
 // a layer take activations quantized outside it): r = 1 / sqrt(mean(x^2) + eps) in fp64, rounded
 // once to fp32; y = bf16(bf16(fp32(x r)) gamma); then y quantized as k_quantize_act does.
-// Pass 1: sum of squares in fp64 (a fixed order, so every lane ends with the same bits).  Pass 2:
+// Pass 1: sum of squares in fp64 (a fixed order, every lane ending with the same bits).  Pass 2:
 // the two products in fp32 (x r is one rounding; t gamma is exact), each rounded to bf16 by the
 // hardware convert (RNE).
+
+// fp64 sum of a value over the 64 lanes of a wave by DPP moves (each 64-bit step as two 32-bit
+// halves): quad, half-row and row partners, then rows 0 -> 1 and 2 -> 3 and row 1 -> rows 2, 3;
+// lane 63 ends with the total, which every lane reads back.  Rows left out of a step add +0.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_add_f64(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xF, false);
+  return x + __builtin_bit_cast(double, (uint64_t)hi << 32 | lo);
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+  v = dpp_add_f64<0xB1, 0xF>(v);    // quad_perm [1, 0, 3, 2]
+  v = dpp_add_f64<0x4E, 0xF>(v);    // quad_perm [2, 3, 0, 1]
+  v = dpp_add_f64<0x141, 0xF>(v);   // row_half_mirror: the other quad of the half-row
+  v = dpp_add_f64<0x140, 0xF>(v);   // row_mirror: the other half of the row
+  v = dpp_add_f64<0x142, 0xA>(v);   // row_bcast15: row 0's sum into row 1, row 2's into row 3
+  v = dpp_add_f64<0x143, 0xC>(v);   // row_bcast31: rows 0 + 1 into rows 2 and 3
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, 63);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), 63);
+  return __builtin_bit_cast(double, (uint64_t)hi << 32 | lo);
+}
 
 // One row per workgroup of WPR waves; lane L = 64 h + lane of wave h takes columns
 // 512 WPR c + 8 L .. + 7 of pass c.  CH > 0: the row (K <= 512 WPR CH) is loaded once, all
 // chunks in flight together, and kept in registers for the second pass; CH == 0: any K, chunk
 // by chunk, re-read in the second pass.  The sum of squares: four fp64 partial sums per lane,
-// a fixed xor butterfly per wave, then the waves' sums added in wave order.
+// a fixed DPP tree per wave (wave_sum_f64), then the waves' sums added in wave order.  The sum
+// of bf16 squares in fp64 is exact for rows whose squares span under 2^25 of magnitude (16-bit
+// significands, at most 2^12 terms in 53 bits), so there the order gives the oracle's bits.
 template <int CH, int WPR>
 __global__ __launch_bounds__(64 * WPR) void k_rmsnorm_quant(const uint16_t* __restrict__ x, int M,
                                                             int K, int64_t ldx,
@@ -174,8 +199,7 @@ __global__ __launch_bounds__(64 * WPR) void k_rmsnorm_quant(const uint16_t* __re
     }
   }
   double ss = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  ss = wave_sum_f64(ss);
   if constexpr (WPR > 1) {
     if (lane == 0) part[h] = ss;
     __syncthreads();

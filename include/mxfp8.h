@@ -247,9 +247,10 @@ int mxfp8_linear_prequant_fmt(const void* xq, const void* xs, int64_t M, int64_t
 
 /* Batch-invariant mode (aiter_flydsl page, is_supported: its split-K kernel is not batch
  * invariant).  on != 0: every M runs on kernels that add the K steps of each output in order,
- * one MFMA per 128-wide step from a zero start (the tiled and generic GEMMs, and up to 32 rows
- * on the bf16 entry the role-split small-M kernel with its waves extending one accumulator
- * chain in turn), so a row's result does not depend on how many rows the call has; the split-K
+ * one MFMA per 128-wide step from a zero start (the tiled and generic GEMMs, and up to 64 rows
+ * on the bf16 entry (K <= 4096; 16 rows for K <= 8192) the role-split small-M kernel with its
+ * waves extending one accumulator chain in turn), so a row's result does not depend on how many
+ * rows the call has; the split-K
  * kernels are not used.  on == 0 (default): fastest kernel per shape.  Returns MX_OK.
  * Thread safety: the mode is one process-wide atomic flag.  Each call reads the mode that
  * applies to it once, when it starts, and picks all of its kernels under that mode, so a call

@@ -100,8 +100,8 @@ bool small_m_fused(int64_t M, int64_t N, int64_t K);
 bool small_m_rs(int64_t M, int64_t N, int64_t K);
 bool small_m_quantized(int64_t M, int64_t K);
 // shapes on which the small-M path also runs in batch-invariant mode: the role-split kernel
-// (bf16 entry, up to 32 rows) with its weight waves extending one accumulator chain in K order,
-// which gives each output the bits of the tiled GEMM whatever M is
+// (bf16 entry, its shapes: up to 64 rows) with its weight waves extending one accumulator chain
+// in K order, which gives each output the bits of the tiled GEMM whatever M is
 bool small_m_invariant(int64_t M, int64_t N, int64_t K, bool quantized);
 hipError_t launch_linear_small_m(const void* x, const uint8_t* xs, bool quantized, int64_t M,
                                  int64_t K, const uint8_t* packed, int64_t N, int fmt,

@@ -264,17 +264,23 @@ __global__ __launch_bounds__(512) void k_linear_small_m(const void* __restrict__
 // over K runs in a different order than k_linear_small_m's (within the tolerance of any split).
 // NQ quantizer waves (4 or 8), MT 16-row activation tiles, F weight fragments, code image for
 // K <= KMAX
+// The weight waves come in sets of four; set s takes fragments s FPW .. s FPW + FPW - 1, and its
+// wave l the K groups l, l + 4, .. of them, so every output is the same 4-way split of K, added
+// in wave order, whatever F is (one set for F <= 2, two for F = 4).
 template <int NQ, int MT, int F, int KMAX>
 struct RsCfg {
   static constexpr int NW = F >= 4 ? 8 : 4;                // weight (MFMA) waves
+  static constexpr int SETS = NW / 4;                      // sets of four weight waves
+  static constexpr int FPW = F / SETS;                     // fragments per weight wave
   static constexpr int ROWS = 16 * MT;
   static constexpr int PITCH = KMAX + 16;                  // code row pitch (max); +16 B: banks
-  static constexpr int GMAX = KMAX / 512 / NW;             // weight groups per weight wave
+  static constexpr int GMAX = KMAX / 512 / 4;              // weight groups per weight wave
   static constexpr int QMAX = KMAX / 512 / NQ;             // K groups per quantizer wave
   static constexpr int PAIRS = MT * F;                     // (row tile, fragment) outputs
-  static constexpr int LDS = ROWS * PITCH + ROWS * (KMAX / 32) + NW * PAIRS * 64 * 16;
+  static constexpr int LDS = ROWS * PITCH + ROWS * (KMAX / 32) + NW * MT * FPW * 64 * 16;
   static_assert(LDS <= 160 * 1024, "must fit the 160 KiB LDS");
-  static_assert(GMAX >= 1 && GMAX * 4 * F <= 16, "weight fragments held in registers per wave");
+  static_assert(FPW * SETS == F && GMAX >= 1 && GMAX * 4 * FPW <= 16,
+                "weight fragments held in registers per wave");
   static_assert(PAIRS <= NW, "one weight wave finishes each output pair");
 };
 
@@ -334,7 +340,7 @@ __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_line
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g = lane >> 4;
   const int NG = N >> 4, KT = K >> 7, KT4 = (KT + 3) >> 2, KB = K >> 5;
-  const int GPW = (KT4 + R::NW - 1) / R::NW;              // K groups per weight wave (SEQ)
+  const int GPW = (KT4 + 3) / 4;                          // K groups per weight wave (SEQ)
   const int P = K + 16;                                   // code row pitch
   uint8_t* const codes = lds;                             // [ROWS][P]
   uint8_t* const scl = lds + R::ROWS * P;                 // [ROWS][KB]
@@ -351,8 +357,8 @@ __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_line
     y += (int64_t)m0 * N;
   }
 
-  v8i a[R::GMAX][4][F];
-  uint32_t sw[R::GMAX][F];
+  v8i a[R::GMAX][4][R::FPW];
+  uint32_t sw[R::GMAX][R::FPW];
   v2i braw = {0, 0};
   const bool bias8 = bias != nullptr && ((uintptr_t)bias & 7) == 0;
   if (wave < NQ) {
@@ -388,20 +394,21 @@ __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_line
   } else {
     // weight waves: the scale words and fragments of every K group of this wave, non-temporal
     // (read once per call); steps past the end re-read the last one, unused
-    const int w = wave - NQ;
-    const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * FB) + (int64_t)ng * 64 + lane;
+    const int w = wave - NQ, wl = w & 3;
+    const int f0 = ng + (w >> 2) * R::FPW;                // this wave's first fragment
+    const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)KT * NG * FB) + (int64_t)f0 * 64 + lane;
 #pragma unroll
     for (int i = 0; i < R::GMAX; ++i) {
-      const int kt4 = SEQ ? w * GPW + i : w + R::NW * i;
+      const int kt4 = SEQ ? wl * GPW + i : wl + 4 * i;
       if (kt4 < KT4 && (!SEQ || i < GPW)) {               // wave-uniform
 #pragma unroll
-        for (int f = 0; f < F; ++f) sw[i][f] = wsc[(int64_t)kt4 * NG * 64 + 64 * f];
+        for (int f = 0; f < R::FPW; ++f) sw[i][f] = wsc[(int64_t)kt4 * NG * 64 + 64 * f];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int kt = min(4 * kt4 + j, KT - 1);
 #pragma unroll
-          for (int f = 0; f < F; ++f) {
-            const uint8_t* fr = packed + ((int64_t)kt * NG + ng + f) * FB;
+          for (int f = 0; f < R::FPW; ++f) {
+            const uint8_t* fr = packed + ((int64_t)kt * NG + f0 + f) * FB;
             const v4i lo = __builtin_nontemporal_load((const v4i*)(fr + lane * 16));
             if (WFMT == 0) {
               const v4i hi = __builtin_nontemporal_load((const v4i*)(fr + 1024 + lane * 16));
@@ -419,14 +426,14 @@ __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_line
   }
   rs_lds_barrier();   // the code image is complete
 
-  // this weight wave's K groups onto the accumulators, in K order
-  auto mfma_groups = [&](v4f (&acc)[MT][F], int w) __attribute__((always_inline)) {
+  // the K groups of weight wave l of its set onto the accumulators, in K order
+  auto mfma_groups = [&](v4f (&acc)[MT][R::FPW], int wl) __attribute__((always_inline)) {
     int mrow[MT];     // rows past the tile read its last row: their outputs are not stored
 #pragma unroll
     for (int t = 0; t < MT; ++t) mrow[t] = min(16 * t + r, M - 1);
 #pragma unroll
     for (int i = 0; i < R::GMAX; ++i) {
-      const int kt4 = SEQ ? w * GPW + i : w + R::NW * i;
+      const int kt4 = SEQ ? wl * GPW + i : wl + 4 * i;
       if (kt4 < KT4 && (!SEQ || i < GPW)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -439,7 +446,7 @@ __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_line
               const v8i b = (v8i){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
               const uint32_t sb = scl[mrow[t] * KB + 4 * kt + g];
 #pragma unroll
-              for (int f = 0; f < F; ++f)
+              for (int f = 0; f < R::FPW; ++f)
                 acc[t][f] = mfma_wsel<WFMT>(j, a[i][j][f], b, acc[t][f], sw[i][f], sb);
             }
           }
@@ -448,47 +455,53 @@ __global__ __launch_bounds__(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)) void k_line
     }
   };
   if constexpr (SEQ) {
-    // one chain per output pair, red[pair][64]: weight wave w extends it in segment w (a
-    // wave with no K group leaves it alone); every wave passes the NW barriers
+    // one chain per output pair, red[pair][64]: wave l of each set extends its set's chains in
+    // segment l (a wave with no K group leaves them alone); every wave passes the 4 barriers
 #pragma unroll
-    for (int seg = 0; seg < R::NW; ++seg) {
-      if (wave - NQ == seg && seg * GPW < KT4) {          // wave-uniform
-        v4f acc[MT][F];
+    for (int seg = 0; seg < 4; ++seg) {
+      if (wave >= NQ && ((wave - NQ) & 3) == seg && seg * GPW < KT4) {   // wave-uniform
+        const int fs = ((wave - NQ) >> 2) * R::FPW;       // the set's first fragment
+        v4f acc[MT][R::FPW];
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-          for (int f = 0; f < F; ++f)
-            acc[t][f] = seg == 0 ? (v4f){0.f, 0.f, 0.f, 0.f} : red[(t * F + f) * 64 + lane];
+          for (int f = 0; f < R::FPW; ++f)
+            acc[t][f] = seg == 0 ? (v4f){0.f, 0.f, 0.f, 0.f} : red[(t * F + fs + f) * 64 + lane];
         mfma_groups(acc, seg);
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-          for (int f = 0; f < F; ++f) red[(t * F + f) * 64 + lane] = acc[t][f];
+          for (int f = 0; f < R::FPW; ++f) red[(t * F + fs + f) * 64 + lane] = acc[t][f];
       }
       rs_lds_barrier();
     }
   } else {
     if (wave >= NQ) {
       const int w = wave - NQ;
-      v4f acc[MT][F];
+      v4f acc[MT][R::FPW];
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int f = 0; f < F; ++f) acc[t][f] = (v4f){0.f, 0.f, 0.f, 0.f};
-      mfma_groups(acc, w);
+        for (int f = 0; f < R::FPW; ++f) acc[t][f] = (v4f){0.f, 0.f, 0.f, 0.f};
+      mfma_groups(acc, w & 3);
 #pragma unroll
       for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int f = 0; f < F; ++f) red[((w * MT + t) * F + f) * 64 + lane] = acc[t][f];
+        for (int f = 0; f < R::FPW; ++f) red[((w * MT + t) * R::FPW + f) * 64 + lane] = acc[t][f];
     }
     rs_lds_barrier();   // the partials are in
   }
   if (wave >= NQ && wave - NQ < R::PAIRS) {
     const int pr = wave - NQ, t = pr / F, f = pr % F;
-    v4f s4 = red[pr * 64 + lane];
-    if constexpr (!SEQ) {
+    v4f s4;
+    if constexpr (SEQ) {
+      s4 = red[pr * 64 + lane];
+    } else {
+      // the four partials of the fragment's set, in wave order
+      const int w0 = 4 * (f / R::FPW), fl = f % R::FPW;
+      s4 = red[((w0 * MT + t) * R::FPW + fl) * 64 + lane];
 #pragma unroll
-      for (int w = 1; w < R::NW; ++w) s4 += red[(w * R::PAIRS + pr) * 64 + lane];
+      for (int l = 1; l < 4; ++l) s4 += red[(((w0 + l) * MT + t) * R::FPW + fl) * 64 + lane];
     }
     const int n = 16 * (ng + f) + 4 * g;                  // this lane's 4 output columns
     float bv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -955,7 +968,7 @@ bool small_m_fused(int64_t M, int64_t N, int64_t K) {
 }
 bool small_m_quantized(int64_t M, int64_t K) { return M >= 1 && M <= 32 && K % 128 == 0; }
 bool small_m_invariant(int64_t M, int64_t N, int64_t K, bool quantized) {
-  return !quantized && M <= 32 && small_m_rs(M, N, K);
+  return !quantized && small_m_rs(M, N, K);
 }
 
 // the role-split kernel with the smallest code image and row count that hold a row tile of RT
@@ -967,7 +980,11 @@ static void launch_rs_k(const uint16_t* x, int M, int K, const uint8_t* packed, 
                         const BatchStrides& bs, int RT) {
 #define MX_RS(NQ, QR) hipLaunchKernelGGL((k_linear_small_m_rs<WFMT, NQ, MT, F, KMAX, QR, SEQ>), grid, dim3(64 * (NQ + RsCfg<NQ, MT, F, KMAX>::NW)), 0, s, x, M, K, packed, N, bias, y, bs, RT)
   if constexpr (F == 4) {
-    if (RT <= 12) MX_RS(4, 12);
+    if (RT <= 1) MX_RS(4, 1);
+    else if (RT <= 2) MX_RS(4, 2);
+    else if (RT <= 4) MX_RS(4, 4);
+    else if (RT <= 8) MX_RS(4, 8);
+    else if (RT <= 12) MX_RS(4, 12);
     else MX_RS(4, 16);
   } else if constexpr (MT == 1) {
     if (RT <= 1) MX_RS(4, 1);
@@ -981,29 +998,44 @@ static void launch_rs_k(const uint16_t* x, int M, int K, const uint8_t* packed, 
   }
 #undef MX_RS
 }
+// Weight fragments per workgroup, widened (from 4 rows on) while the grid still holds at least
+// 256 workgroups: a workgroup then loads and quantizes its activation rows once for more output
+// columns, so each CU pulls fewer bytes per output (calls of several layers, wide N).  Eight
+// 4096 x 4096 layers per call: M = 8 3.94 -> 3.22 us per layer, M = 32 5.79 -> 4.81 us; at
+// M = 1 the activation rows are too few to pay (2.96 against 3.08 us with four fragments).
+// Every tiling adds each output's K steps in the same order, so the choice never changes bits.
+constexpr int kRsWidenMax = 4, kRsWidenMinM = 4;
 template <int WFMT, bool SEQ>
 static void launch_rs(const uint16_t* x, int M, int K, const uint8_t* packed, int N,
                       const uint16_t* bias, uint16_t* y, hipStream_t s, int batch,
                       const BatchStrides& bs) {
-  const int F = rs_row_split(M, N, K);
-  if (F > 0) {                                  // R row tiles of RT rows, F fragments
-    const int R0 = (M + 15) / 16, RT = (M + R0 - 1) / R0, R = (M + RT - 1) / RT;
-    const dim3 grid((unsigned)(N / (16 * F) * R), (unsigned)batch);
-    if (F == 2) {
-      launch_rs_k<WFMT, 1, 2, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, RT);
-    } else {
-      // four fragments: not in the accumulator-chain form (small_m_invariant stops at 32 rows),
-      // whose registers would spill
-      if constexpr (!SEQ) launch_rs_k<WFMT, 1, 4, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, RT);
-    }
+  int F = rs_row_split(M, N, K), R = 1;                 // row tiles from 17 rows (K <= 4096)
+  if (F > 0) R = (M + 15) / 16;
+  else if (M > 16) {                                    // up to 24 rows in one tile, N % 32 != 0
+    launch_rs_k<WFMT, 2, 1, 4096, SEQ>(x, M, K, packed, N, bias, y, s,
+                                       dim3((unsigned)(N / 16), (unsigned)batch), bs, M);
     return;
-  }
-  const dim3 grid((unsigned)(N / 16), (unsigned)batch);
-  if (M <= 16) {
-    if (K <= 4096) launch_rs_k<WFMT, 1, 1, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, M);
-    else launch_rs_k<WFMT, 1, 1, 8192, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, M);
   } else {
-    launch_rs_k<WFMT, 2, 1, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, M);
+    F = 1;
+  }
+  if (K <= 4096 && M >= kRsWidenMinM) {
+    for (int f = kRsWidenMax; f > F; f >>= 1)
+      if (N % (16 * f) == 0 && (int64_t)batch * (N / (16 * f)) * R >= 256) {
+        F = f;
+        break;
+      }
+  }
+  const int RT = (M + R - 1) / R;                       // rows per tile
+  R = (M + RT - 1) / RT;
+  const dim3 grid((unsigned)(N / (16 * F) * R), (unsigned)batch);
+  if (F == 4) {
+    launch_rs_k<WFMT, 1, 4, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, RT);
+  } else if (F == 2) {
+    launch_rs_k<WFMT, 1, 2, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, RT);
+  } else if (K <= 4096) {
+    launch_rs_k<WFMT, 1, 1, 4096, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, M);
+  } else {
+    launch_rs_k<WFMT, 1, 1, 8192, SEQ>(x, M, K, packed, N, bias, y, s, grid, bs, M);
   }
 }
 

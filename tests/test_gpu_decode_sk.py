@@ -165,7 +165,7 @@ def test_fused_quantizers_bit_exact_through_identity_weight(M, K, bi):
     (role-split small-M kernel at M = 1 .. 16 with each of its row counts in one row tile, at
     20, 24 and 32 in two row tiles, at 50 and 64 in four; split-K decode kernel at 32 and 50
     with K = 4224; quantizer launch + tiled GEMM at 100; in batch-invariant mode the
-    role-split kernel's in-order form up to 32 rows with K = 2048, and the quantizer launch +
+    role-split kernel's in-order form up to 64 rows with K = 2048, and the quantizer launch +
     generic or tiled GEMM otherwise).  Inputs hold outlier channels, all-zero blocks, values
     that saturate at 448 after scaling, bf16 subnormals and exact rounding ties."""
     N = K

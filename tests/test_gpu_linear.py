@@ -314,13 +314,16 @@ def _entries_differ(M, N, K):
 # both code-image sizes (K <= 4096, K <= 8192), partial last K groups, quantizer and weight
 # waves with no K group, columns that are not a multiple of 64, and a full decode width.  Row
 # tiles: column-group counts that are a multiple of 8 (row tiles of a group on one XCD) and
-# not (1, 3, 33), row tiles of unequal rows.
+# not (1, 3, 33), row tiles of unequal rows.  From 4 rows, grids of at least 512 workgroups take
+# two or four fragments per workgroup (N = 8192: two; N = 16384, and 31 rows in two tiles at
+# N = 8192: four); 1 and 3 rows at N = 16384 keep one.
 RS = [(1, 64, 128), (2, 80, 8192), (3, 48, 640), (7, 272, 4224), (11, 96, 1152),
       (12, 64, 3968), (13, 4096, 4096), (16, 160, 8192), (21, 112, 640), (24, 48, 2048),
       (17, 64, 4096), (18, 32, 128), (25, 96, 640), (29, 256, 3968), (19, 1056, 1152),
       (32, 4096, 4096), (23, 512, 4096), (31, 8192, 2048),
       (33, 64, 4096), (40, 192, 640), (48, 512, 3968), (49, 2112, 1152), (64, 4096, 4096),
-      (57, 1024, 128), (36, 8192, 2048)]
+      (57, 1024, 128), (36, 8192, 2048),
+      (8, 8192, 1024), (4, 16384, 512), (16, 16384, 4096), (1, 16384, 128), (3, 16384, 256)]
 
 
 @pytest.mark.parametrize("fmt", [0, 2, 3])
@@ -386,13 +389,14 @@ def test_tiled_kernel_many_tiles(K, fmt):
 @pytest.mark.parametrize("K,N", [(512, 272), (4224, 272), (544, 272), (512, 256), (4096, 1024)])
 def test_batch_invariant_mode(K, N, fmt):
     """Batch-invariant mode: the first rows of a 300-row call (tiled kernel; K % 128 != 0:
-    generic kernel) are bit-identical to the same rows called alone at M = 1, 8, 16, 17, 31
-    and 32, on both entries, with E4M3 and E2M3 weights; the mode's result is checked against
-    the oracle.  The rows called alone run on the role-split kernel with its weight waves
-    extending one accumulator chain in K order (the bf16 entry: one row tile up to 16 rows,
-    K <= 8192; two 16-row activation tiles in one row tile up to 24 rows where N % 32 != 0;
-    two row tiles from 17 rows where N % 32 == 0, K <= 4096) and on the generic kernel
-    elsewhere (the pre-quantized entry, K % 128 != 0, 31 and 32 rows at N = 272)."""
+    generic kernel) are bit-identical to the same rows called alone at M = 1, 8, 16, 17, 31,
+    32, 33, 48 and 64, on both entries, with E4M3 and E2M3 weights; the mode's result is
+    checked against the oracle.  The rows called alone run on the role-split kernel with its
+    weight waves extending one accumulator chain in K order (the bf16 entry: one row tile up to
+    16 rows, K <= 8192; two 16-row activation tiles in one row tile up to 24 rows where
+    N % 32 != 0; row tiles from 17 rows where N % 32 == 0 (up to 32 rows) or N % 64 == 0,
+    K <= 4096, with two or four weight fragments per workgroup) and on the generic or tiled
+    kernel elsewhere (the pre-quantized entry, K % 128 != 0, 31 rows and more at N = 272)."""
     g = np.random.default_rng(K + fmt + N)
     M = 300
     xf = g.standard_normal((M, K)).astype(np.float32)
@@ -409,7 +413,7 @@ def test_batch_invariant_mode(K, N, fmt):
         y_all = layer(xd)
         yq_all = layer.apply_quantized(xq, xs)
         assert torch.equal(y_all.view(torch.int16), yq_all.view(torch.int16))
-        for m in (1, 8, 16, 17, 31, 32):
+        for m in (1, 8, 16, 17, 31, 32, 33, 48, 64):
             y = layer(xd[:m].contiguous())
             yq = layer.apply_quantized(xq[:m].contiguous(), xs[:m].contiguous())
             assert torch.equal(y.view(torch.int16), y_all[:m].view(torch.int16)), m
@@ -421,7 +425,8 @@ def test_batch_invariant_mode(K, N, fmt):
     assert ok, rep
 
 
-@pytest.mark.parametrize("M,N,K", [(5, 48, 512), (24, 64, 1024), (100, 272, 512),
+@pytest.mark.parametrize("M,N,K", [(5, 48, 512), (24, 64, 1024), (9, 8192, 512), (20, 4096, 1024),
+                                   (100, 272, 512),
                                    (300, 592, 640), (40, 160, 544)])
 def test_batched(M, N, K):
     """Batched layer (bmm_batch_size): every batch equals a separate call bit for bit (same
@@ -508,11 +513,11 @@ def test_batch_invariant_mode_per_thread():
         mxfp8.set_batch_invariant(False)
 
 
-@pytest.mark.parametrize("M", [8, 24])
+@pytest.mark.parametrize("M", [8, 24, 40])
 def test_batched_batch_invariant(M):
-    """The batched layer in batch-invariant mode (the role-split kernel's in-order chain, one and
-    two row tiles): every batch equals its rows of a 300-row call of the same layer, bit for
-    bit."""
+    """The batched layer in batch-invariant mode (the role-split kernel's in-order chain, one,
+    two and three row tiles; the batch's grid takes four fragments per workgroup from 24 rows):
+    every batch equals its rows of a 300-row call of the same layer, bit for bit."""
     Bn, N, K = 3, 256, 1024
     g = np.random.default_rng(M + 5)
     xs_ = [synth.bf16_bits(g.standard_normal((300, K)).astype(np.float32)) for _ in range(Bn)]

@@ -628,3 +628,65 @@ def test_workspace_and_output_bounds_every_path(M, N, K):
     ref, _, _ = orc.linear_ref(host_bf16_bits(x), wq, wsc, 0, host_bf16_bits(b))
     ok, rep = tolerance.check(host_bf16_bits(y), ref, name="bounds-%d-%d-%d" % (M, N, K))
     assert ok, rep
+
+
+def test_role_split_forms_graph_replay():
+    """The role-split kernel's forms captured in one HIP graph (one row tile; two row tiles with
+    two fragments; four row tiles with four; a batched call that widens to four fragments;
+    batch-invariant mode's in-order chain): every replay, with eager work between replays,
+    equals the eager results bit for bit."""
+    g = np.random.default_rng(31)
+    N, K = 4096, 2048
+    wb = synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    wq, wsc = orc.quantize(wb, 0)
+    pk = mxfp8.prepack_weight(u8_dev(wq), u8_dev(wsc), 0)
+    bias = bf16_dev(synth.bf16_bits((g.standard_normal(N) * 0.1).astype(np.float32)))
+    Ms = (8, 32, 64)
+    xs = [bf16_dev(synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32))) for M in Ms]
+    Bn = 4
+    pkb = torch.cat([pk] * Bn)
+    xb = bf16_dev(synth.bf16_bits(g.standard_normal((Bn, 12, K)).astype(np.float32)))
+    biasb = bias.unsqueeze(0).repeat(Bn, 1).contiguous()
+    ys = [torch.empty((x.shape[0], N), dtype=torch.bfloat16, device=DEV) for x in xs]
+    yb = torch.empty((Bn, 12, N), dtype=torch.bfloat16, device=DEV)
+    ybi = torch.empty((24, N), dtype=torch.bfloat16, device=DEV)
+    # explicit workspaces (none of these kernels uses one; the sizes cover every entry)
+    ws = mxfp8.new_workspace(max(mxfp8.workspace_bytes(M, N, K) for M in Ms), DEV)
+    wsb = mxfp8.new_workspace(mxfp8.workspace_bytes(Bn * 12, N, K), DEV)
+    banner("role-split forms, graph replay")
+
+    def calls():
+        for x, y in zip(xs, ys):
+            mxfp8.linear(x, pk, N, 0, bias, out=y, workspace=ws)
+        mxfp8.linear_batched(xb, pkb, N, 0, biasb, out=yb, workspace=wsb)
+        mxfp8.set_batch_invariant_thread(True)
+        try:
+            mxfp8.linear(xs[2][:24].contiguous(), pk, N, 0, bias, out=ybi, workspace=ws)
+        finally:
+            mxfp8.set_batch_invariant_thread(None)
+
+    calls()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys] + [yb.clone(), ybi.clone()]
+    s = torch.cuda.Stream(DEV)
+    s.wait_stream(torch.cuda.current_stream(DEV))
+    x24 = xs[2][:24].contiguous()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=s):
+        for x, y in zip(xs, ys):
+            mxfp8.linear(x, pk, N, 0, bias, out=y, workspace=ws)
+        mxfp8.linear_batched(xb, pkb, N, 0, biasb, out=yb, workspace=wsb)
+        mxfp8.set_batch_invariant_thread(True)
+        try:
+            mxfp8.linear(x24, pk, N, 0, bias, out=ybi, workspace=ws)
+        finally:
+            mxfp8.set_batch_invariant_thread(None)
+    for rep in range(3):
+        for y in ys + [yb, ybi]:
+            y.zero_()
+        gr.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys + [yb, ybi], eager):
+            assert torch.equal(y.view(torch.int16), e.view(torch.int16)), rep
+        calls()                                    # eager work between replays
+        torch.cuda.synchronize()

@@ -192,7 +192,10 @@ int mxfp8_linear_prequant(const void* xq, const void* xs, int64_t M, int64_t K,
 /* Batched layer (Mxfp8LinearKernel page, Mxfp8LinearLayerConfig.bmm_batch_size; the
  * aiter_flydsl page's can_implement turns such layers away): for every b < B,
  *     y[b] = dequant(quantize(x[b])) . dequant(W[b])^T (+ bias[b])
- * with the same kernels, hence the same results, as B separate mxfp8_linear calls.
+ * with the same kernels, hence the same results, as B separate mxfp8_linear calls, with one
+ * exception: a layer that mxfp8_linear would split along K (M > 32 with at most 96 output tiles
+ * of 128 x 128; see mxfp8_workspace_bytes) runs unsplit here, as in mxfp8_linear_prequant, so its
+ * fp32 sums add in another order than the separate call's.
  *   x_bf16    [16]  bf16 [B, M, K], contiguous
  *   packed    [16]  B prepacked weights back to back, mxfp8_prepacked_bytes(N, K, fmt) each
  *   bias            bf16 [B, N] or NULL

@@ -425,13 +425,22 @@ def test_batch_invariant_mode(K, N, fmt):
     assert ok, rep
 
 
+def _tiled_split_k(M, N, K):
+    """Whether a single mxfp8_linear call of this layer splits K across workgroups in the tiled
+    GEMM (M > 32, at most 96 output tiles of 128 x 128, at least two groups of four K steps)."""
+    tiles = -(-N // 128) * -(-M // 128)
+    return M > 32 and K % 128 == 0 and N >= 128 and tiles <= 96 and (K // 128 + 3) // 4 >= 2
+
+
 @pytest.mark.parametrize("M,N,K", [(5, 48, 512), (24, 64, 1024), (9, 8192, 512), (20, 4096, 1024),
                                    (100, 272, 512),
                                    (300, 592, 640), (40, 160, 544)])
 def test_batched(M, N, K):
     """Batched layer (bmm_batch_size): every batch equals a separate call bit for bit (same
     kernels: fused small-M, quantizer + small-M, tiled, generic), and batch 1 matches the
-    oracle; per-batch bias and the pre-quantized batched entry included."""
+    oracle; per-batch bias and the pre-quantized batched entry included.  A layer that a
+    separate call splits along K (300 x 592 x 640) runs unsplit in the batched call, as in the
+    pre-quantized entry, and is compared with that."""
     Bn = 3
     g = np.random.default_rng(M + N + K)
     xs_ = [synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32)) for _ in range(Bn)]
@@ -446,15 +455,19 @@ def test_batched(M, N, K):
     xq, xsc = mxfp8.quantize_act(x.reshape(Bn * M, K))
     yq = mxfp8.linear_prequant_batched(xq.view(Bn, M, K), xsc.view(Bn, M, K // 32), packed, N, 0,
                                        bias)
+    split = _tiled_split_k(M, N, K)
     for b in range(Bn):
         y1 = layers[b][0](x[b])
-        assert torch.equal(y[b].view(torch.int16), y1.view(torch.int16)), b
         y1q = layers[b][0].apply_quantized(xq.view(Bn, M, K)[b].contiguous(),
                                            xsc.view(Bn, M, K // 32)[b].contiguous())
+        assert torch.equal(y[b].view(torch.int16), (y1q if split else y1).view(torch.int16)), b
         assert torch.equal(yq[b].view(torch.int16), y1q.view(torch.int16)), b
     ref, _, _ = orc.linear_ref(xs_[1], layers[1][1], layers[1][2], 0, bs_[1])
     ok, rep = tolerance.check(host_bf16_bits(y[1]), ref, name="batched-%d-%d-%d" % (M, N, K))
     assert ok, rep
+    if split:   # the separate call's split sum meets the same bar
+        ok, rep = tolerance.check(host_bf16_bits(layers[1][0](x[1])), ref, name="split-%d" % M)
+        assert ok, rep
 
 
 def test_batch_invariant_mode_per_thread():
@@ -690,3 +703,29 @@ def test_role_split_forms_graph_replay():
             assert torch.equal(y.view(torch.int16), e.view(torch.int16)), rep
         calls()                                    # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M", [1, 8, 32])
+def test_batched_decode_bench_config(M):
+    """The bench's batched decode configuration: eight 4096 x 4096 layers (own activations,
+    weights, bias) in one call, M = 1 (one fragment per workgroup), 8 (four fragments) and 32
+    (four fragments, two row tiles).  Every batch equals a separate call of its layer bit for
+    bit; batches 0 and 7 are checked against the oracle in full."""
+    Bn, N, K = 8, 4096, 4096
+    g = np.random.default_rng(M + 808)
+    xs_ = [synth.bf16_bits(g.standard_normal((M, K)).astype(np.float32)) for _ in range(Bn)]
+    ws_ = [synth.bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in range(Bn)]
+    bs_ = [synth.bf16_bits((g.standard_normal(N) * 0.01).astype(np.float32)) for _ in range(Bn)]
+    banner("batched decode, bench configuration", Bn, M, N, K)
+    layers = [_layer(ws_[b], 0, bs_[b]) for b in range(Bn)]
+    packed = torch.cat([l[0].packed for l in layers])
+    bias = torch.stack([bf16_dev(bb) for bb in bs_])
+    x = torch.stack([bf16_dev(xx) for xx in xs_])
+    y = mxfp8.linear_batched(x, packed, N, 0, bias)
+    for b in range(Bn):
+        y1 = layers[b][0](x[b])
+        assert torch.equal(y[b].view(torch.int16), y1.view(torch.int16)), b
+    for b in (0, Bn - 1):
+        ref, _, _ = orc.linear_ref(xs_[b], layers[b][1], layers[b][2], 0, bs_[b])
+        ok, rep = tolerance.check(host_bf16_bits(y[b]), ref, name="batched-decode-%d-%d" % (M, b))
+        assert ok, rep

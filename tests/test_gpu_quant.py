@@ -109,3 +109,26 @@ def test_quantize_weight_sweep(fmt):
         rq = orc.fp6_pack(rq)
     assert np.array_equal(host_u8(ws), rs)
     assert np.array_equal(host_u8(wq), rq)
+
+
+def test_quantize_act_large_ragged_and_strided():
+    """A prefill-sized input one row past 4096 (the grid-stride loop's last pass partly past
+    the end) and a row stride of 4160 elements through the C ABI (every row start moved);
+    non-finite blocks at both ends."""
+    g = np.random.default_rng(41)
+    M, K, LD = 4097, 4096, 4160
+    big = synth.bf16_bits(g.standard_normal((M, LD)).astype(np.float32))
+    big[0, 3] = 0x7F80          # +Inf in the first block
+    big[M - 1, K - 1] = 0xFFC1  # NaN in the last block
+    banner("quantize_act large", M, K, LD)
+    x = np.ascontiguousarray(big[:, :K])
+    rq, rs = orc.quantize(x, orc.E4M3)
+    xq, xs = mxfp8.quantize_act(bf16_dev(x))
+    assert np.array_equal(host_u8(xs), rs) and np.array_equal(host_u8(xq), rq)
+    t = bf16_dev(big)
+    q = torch.empty((M, K), dtype=torch.uint8, device=t.device)
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device=t.device)
+    rc = mxfp8.lib().mxfp8_quantize_act(t.data_ptr(), M, K, LD, q.data_ptr(), s.data_ptr(), None)
+    assert rc == 0
+    assert np.array_equal(host_u8(q), rq) and np.array_equal(host_u8(s), rs)
+    assert rs[0, 0] == 0xFF and rs[M - 1, K // 32 - 1] == 0xFF

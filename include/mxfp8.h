@@ -231,7 +231,10 @@ int mxfp8_linear_prequant_batched(const void* xq, const void* xs, int64_t B, int
 int mxfp8_quantize_act_fmt(const void* x_bf16, int64_t M, int64_t K, int64_t ldx, int afmt,
                            void* xq, void* xs, void* stream);
 
-/* Workspace bytes mxfp8_linear_fmt needs (0 for invalid arguments or M == 0). */
+/* Workspace bytes mxfp8_linear_fmt needs (0 for invalid arguments or M == 0).  With FP6
+ * activations the workspace holds their codes in the layout the GEMM reads fastest: where
+ * K % 128 == 0, each 128-wide K step's 96 bytes at the start of a 128-byte slice (K bytes a row),
+ * else packed [M, 3K/4]; then the scales and, where the GEMM splits K, its partial sums. */
 int64_t mxfp8_workspace_bytes_fmt(int64_t M, int64_t N, int64_t K, int fmt, int afmt);
 
 /* mxfp8_linear with activations quantized to afmt (fmt = the weight's format; FP6 afmt needs

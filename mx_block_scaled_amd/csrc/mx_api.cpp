@@ -73,10 +73,16 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// bytes per K step of an FP6 activation row as the library quantizes it for its own GEMM: every
+// step's 96 bytes at the start of a 128-byte slice where K % 128 == 0 (a packed 96-byte slice
+// spans two 128-byte lines for every other step, and the GEMM's copies then fetch 1.5 lines per
+// row and step: W6A6 512 x 8192 x 8192 41.0-41.5 us packed, 36.6-37.1 us in 128-byte slices)
+int fp6_act_step(int64_t K) { return K % 128 == 0 ? 128 : 96; }
+
 int64_t quant_ws_bytes(int64_t M, int64_t K, int afmt = MX_FMT_E4M3) {
-  // the counter prefix, xq [M, K] (E4M3) or [M, 3K/4] (FP6), then xs [M, K/32] at a 256-byte
-  // boundary
-  const int64_t row = afmt == MX_FMT_E4M3 ? K : K / 4 * 3;
+  // the counter prefix, xq [M, K] (E4M3) or FP6 rows of K / 128 slices (fp6_act_step), then
+  // xs [M, K/32] at a 256-byte boundary
+  const int64_t row = afmt == MX_FMT_E4M3 ? K : (fp6_act_step(K) == 128 ? K : K / 4 * 3);
   return mx::kWorkspacePrefix + ((M * row + 255) / 256) * 256 + M * (K / 32);
 }
 
@@ -452,13 +458,17 @@ int mxfp8_linear_fmt(const void* x_bf16, int64_t M, int64_t K, const void* packe
   if (!aligned16(workspace)) return fail(MX_EALIGN, "workspace must be 16-byte aligned");
   if ((rc = check_arch())) return rc;
   hipStream_t s = (hipStream_t)stream;
+  const int xstep = fp6_act_step(K);
   uint8_t* xq = (uint8_t*)workspace + mx::kWorkspacePrefix;
-  uint8_t* xs = xq + ((M * (K / 4 * 3) + 255) / 256) * 256;
+  const int64_t xrow = xstep == 128 ? K : K / 4 * 3;     // code bytes per row (as quant_ws_bytes)
+  uint8_t* xs = xq + ((M * xrow + 255) / 256) * 256;
   float* part = mx::gemm_split_bytes(M, N, K) ? (float*)((uint8_t*)workspace + split_offset(M, K, afmt)) : nullptr;
-  hipError_t e = mx::launch_quantize_act_fp6((const uint16_t*)x_bf16, M, K, K, afmt, xq, xs, s);
+  hipError_t e = mx::launch_quantize_act_fp6((const uint16_t*)x_bf16, M, K, K, afmt, xq, xs, s, xstep);
   if (e != hipSuccess) return hip_status(e, "quantize_act (FP6) launch");
+  mx::BatchStrides bs;
+  bs.xstep = xstep == 128 ? 128 : 0;
   return hip_status(mx::launch_gemm(xq, xs, M, K, (const uint8_t*)packed, N, fmt,
-                                    (const uint16_t*)bias, (uint16_t*)y, s, 1, {}, afmt, part),
+                                    (const uint16_t*)bias, (uint16_t*)y, s, 1, bs, afmt, part),
                     "gemm launch");
 }
 

@@ -46,7 +46,9 @@ __global__ __launch_bounds__(64) void k_gemm_generic(const uint8_t* __restrict__
   const int lane = threadIdx.x;
   const int r = lane & 15, g = lane >> 4;
   const int NG = N >> 4, KT = (K + 127) >> 7, KB = K >> 5;
-  const int LDX = XFMT == 0 ? K : K / 4 * 3;   // activation row bytes
+  // activation row bytes; an FP6 block kb's 24 bytes at XS (kb / 4) + 24 (kb % 4) of its row
+  const int XS = XFMT == 0 ? 128 : (bs.xstep ? bs.xstep : 96);
+  const int LDX = XFMT == 0 ? K : (bs.xstep ? K / 128 * bs.xstep : K / 4 * 3);
   const int ng = blockIdx.x;
   const int m0 = blockIdx.y * 16 * MT;
   const uint8_t* wfr = packed + (int64_t)ng * FB;
@@ -93,10 +95,10 @@ __global__ __launch_bounds__(64) void k_gemm_generic(const uint8_t* __restrict__
           if (mok[t] && k1 < K) b1 = *(const v4i*)(xr + k1);
           b[u][t] = (v8i){b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
         } else {
-          // FP6 operand: block kb's 24 packed bytes (8-byte aligned: rows are 24 K/32 bytes)
+          // FP6 operand: block kb's 24 bytes (8-byte aligned: rows are 24 K/32 or XS K/128 bytes)
           v2i d0 = {0, 0}, d1 = {0, 0}, d2 = {0, 0};
           if (mok[t] && kb < KB) {
-            const uint8_t* p = xr + 24 * kb;
+            const uint8_t* p = xr + XS * (kb >> 2) + 24 * (kb & 3);
             d0 = *(const v2i*)p;
             d1 = *(const v2i*)(p + 8);
             d2 = *(const v2i*)(p + 16);
@@ -360,7 +362,9 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   const int n0 = tn * C::BN, m0 = tm * C::BM;
 
   const int NG = N >> 4, KB = K >> 5;
-  const int LDX = K / 128 * C::XB;   // activation row bytes
+  // bytes per K step of an activation row in global memory (FP6: packed 96, or 128-byte slices)
+  const int XS = XFMT != 0 && bs.xstep ? bs.xstep : C::XB;
+  const int LDX = K / 128 * XS;      // activation row bytes
   const uint32_t* wsc = (const uint32_t*)(packed + (int64_t)(K >> 7) * NG * C::FB);
   // K part of this workgroup (split K: grid z, whole groups of four K steps; one part unless
   // `part` is given): the operand and scale bases move to the part's first step
@@ -372,7 +376,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
   const int KBr = KB - 4 * kt_lo;                 // scale bytes of a row from this part on
   packed += (int64_t)kt_lo * NG * C::FB;
   wsc += (int64_t)g_lo * NG * 64;
-  xq += (int64_t)kt_lo * C::XB;
+  xq += (int64_t)kt_lo * XS;
   xs += 4 * kt_lo;
 
   // ---- per-lane DMA sources, as 32-bit offsets from uniform bases (every operand < 2^31 B):
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     } else {
       const int i = p - C::A_PER_WAVE;
       if (XFMT == 0 || b_on[i])
-        dma16(xq + (uint32_t)(kt * C::XB + b_off[i]), base + C::A_BYTES + (wave + C::NDW * i) * 1024);
+        dma16(xq + (uint32_t)(kt * XS + b_off[i]), base + C::A_BYTES + (wave + C::NDW * i) * 1024);
     }
   };
   auto issue = [&](int kt, int stage) __attribute__((always_inline)) {

@@ -20,13 +20,19 @@ PackGeom pack_geom(int64_t N, int64_t K, int fmt);
 // unbatched call.
 struct BatchStrides {
   int64_t x = 0, xs = 0, w = 0, y = 0, bias = 0;
+  // FP6 activations: bytes per 128-wide K step of an activation row; 0 = packed (96 bytes), 128 =
+  // each step's 96 bytes at the start of a 128-byte slice (K % 128 == 0), the layout the
+  // library's own FP6 quantization writes for its GEMM
+  int xstep = 0;
 };
 
 hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
                                uint8_t* xs, hipStream_t s);
-// MXFP6 activations (fmt E2M3 = 2 or E3M2 = 3): xq [M, 3K/4] packed codes, xs [M, K/32].
+// MXFP6 activations (fmt E2M3 = 2 or E3M2 = 3): xq [M, 3K/4] packed codes (xstep 96) or rows of
+// K / 128 slices of 128 bytes, each holding one K step's 96 bytes first (xstep 128, K % 128 == 0);
+// xs [M, K/32].
 hipError_t launch_quantize_act_fp6(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt,
-                                   uint8_t* xq, uint8_t* xs, hipStream_t s);
+                                   uint8_t* xq, uint8_t* xs, hipStream_t s, int xstep = 96);
 // RMS norm (bf16 weight gamma [K], eps) fused with the E4M3 activation quantization; y
 // (optional) receives the normalized bf16 rows [M, K].
 hipError_t launch_rmsnorm_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,

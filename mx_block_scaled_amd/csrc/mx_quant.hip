@@ -71,14 +71,16 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t 
 // RNE(x / scale) saturated at the format maximum, sign kept, packed little-endian in 6-bit
 // fields: the same bits as the exact per-element encode for every finite bf16 and every scale
 // byte.  A block holding Inf/NaN gets scale 0xFF and zero codes (FP6 has no NaN).
+// xstep 96: rows of packed codes; 128: block kb's 24 bytes at 128 (kb / 4) + 24 (kb % 4) of its row
+// (K % 128 == 0), so that every K step's 96 bytes start a 128-byte line for the GEMM's copies.
 template <int FMT>
 __global__ __launch_bounds__(256) void k_quantize_act_fp6(const uint16_t* __restrict__ x, int64_t K,
                                                           int64_t ldx, int64_t blocks,
                                                           uint8_t* __restrict__ xq,
-                                                          uint8_t* __restrict__ xs) {
+                                                          uint8_t* __restrict__ xs, int xstep) {
   typedef __bf16 v32bf __attribute__((ext_vector_type(32)));
   const int64_t KB = K >> 5;
-  const int64_t ldq = KB * 24;
+  const int64_t ldq = xstep == 96 ? KB * 24 : (KB >> 2) * xstep;
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < blocks;
        b += (int64_t)gridDim.x * blockDim.x) {
     const int64_t row = b / KB, kb = b - row * KB;
@@ -101,7 +103,7 @@ __global__ __launch_bounds__(256) void k_quantize_act_fp6(const uint16_t* __rest
       if constexpr (FMT == 2) q = __builtin_amdgcn_cvt_scalef32_pk32_fp6_bf16(xv, sc);
       else q = __builtin_amdgcn_cvt_scalef32_pk32_bf6_bf16(xv, sc);
     }
-    uint8_t* dst = xq + row * ldq + kb * 24;   // 8-byte aligned
+    uint8_t* dst = xq + row * ldq + (xstep == 96 ? kb * 24 : (kb >> 2) * xstep + (kb & 3) * 24);
     *(v2i*)dst = (v2i){q[0], q[1]};
     *(v2i*)(dst + 8) = (v2i){q[2], q[3]};
     *(v2i*)(dst + 16) = (v2i){q[4], q[5]};
@@ -110,13 +112,14 @@ __global__ __launch_bounds__(256) void k_quantize_act_fp6(const uint16_t* __rest
 }
 
 hipError_t launch_quantize_act_fp6(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int fmt,
-                                   uint8_t* xq, uint8_t* xs, hipStream_t s) {
+                                   uint8_t* xq, uint8_t* xs, hipStream_t s, int xstep) {
+  if (xstep != 96 && (xstep != 128 || K % 128 != 0)) return hipErrorInvalidValue;
   const int64_t blocks = M * (K >> 5);
   int64_t grid = (blocks + 255) / 256;
   if (grid > 256 * 16) grid = 256 * 16;
   switch (fmt) {
-    case 2: hipLaunchKernelGGL(k_quantize_act_fp6<2>, dim3((unsigned)grid), dim3(256), 0, s, x, K, ldx, blocks, xq, xs); break;
-    case 3: hipLaunchKernelGGL(k_quantize_act_fp6<3>, dim3((unsigned)grid), dim3(256), 0, s, x, K, ldx, blocks, xq, xs); break;
+    case 2: hipLaunchKernelGGL(k_quantize_act_fp6<2>, dim3((unsigned)grid), dim3(256), 0, s, x, K, ldx, blocks, xq, xs, xstep); break;
+    case 3: hipLaunchKernelGGL(k_quantize_act_fp6<3>, dim3((unsigned)grid), dim3(256), 0, s, x, K, ldx, blocks, xq, xs, xstep); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -85,8 +85,9 @@ def test_linear_validation(L):
     # one byte short of the split-K parts: rejected before any launch
     assert L.mxfp8_linear(A, 65, 4096, B, 4096, 0, None, B, B, need65 - 1, None) == MX_EWORKSPACE
     assert b"needed" in L.mxfp8_last_error()
-    # FP6 activations: the same split from 33 rows (no split-K decode kernel on that entry)
-    q6 = 65536 + 40 * 3072 + 40 * 128
+    # FP6 activations: the same split from 33 rows (no split-K decode kernel on that entry);
+    # codes in 128-byte slices per K step (K % 128 == 0), so K bytes a row
+    q6 = 65536 + 40 * 4096 + 40 * 128
     assert L.mxfp8_workspace_bytes_fmt(40, 4096, 4096, 2, 2) == (q6 + 255) // 256 * 256 + 8 * 40 * 4096 * 4
     assert L.mxfp8_workspace_bytes(8, 4096, 4096, 0) == 65536 + 8 * 4096 + 8 * 128
     assert L.mxfp8_workspace_bytes(1, 4096, 4096, 0) == 65536 + 4096 + 128
@@ -180,9 +181,10 @@ def test_fp6_activation_validation(L):
     assert q(A + 2, 4, 64, 64, 3, B, B, None) == MX_EALIGN
     assert q(None, 4, 64, 64, 2, B, B, None) == MX_EINVAL
     assert q(None, 0, 64, 64, 2, None, None, None) == MX_OK      # M == 0: no-op
-    # workspace: the 64 KiB counter prefix, packed FP6 codes [M, 3K/4], then the scales at a
+    # workspace: the 64 KiB counter prefix, the FP6 codes (K % 128 == 0: every K step's 96 bytes
+    # in a 128-byte slice, K bytes a row; else packed, 3K/4 bytes a row), then the scales at a
     # 256-byte boundary
-    assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 2, 2) == 65536 + 64 * 384 + 64 * 16
+    assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 2, 2) == 65536 + 64 * 512 + 64 * 16
     assert L.mxfp8_workspace_bytes_fmt(3, 256, 160, 3, 2) == 65536 + 512 + 3 * 5
     assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 0, 2) == 0   # FP6 activations: FP6 weights
     assert L.mxfp8_workspace_bytes_fmt(64, 256, 512, 2, 0) == L.mxfp8_workspace_bytes(64, 256, 512, 2)

@@ -255,6 +255,8 @@ template <int W>
 __global__ void __launch_bounds__(1024) k_lds_read(int iters, int* out, uint64_t* clk) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[65536];
   const int t = threadIdx.x, wv = t >> 6, l = t & 63;
+  (void)wv;   // read by the device code only
+  (void)l;
   for (int i = t; i < 65536 / 4; i += blockDim.x) ((int*)lds)[i] = i * 2654435761u;
   __syncthreads();
   const uint64_t c0 = shader_clock();

@@ -1414,20 +1414,33 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
   }
 }
 
-// K parts for a single-layer tiled GEMM (M > 32) that would occupy at most 96 of the 256 CUs
-// with 128 x 128 tiles: about 256 workgroups, each at least one group of four K steps, at most
-// kMaxSplit parts; 1 = no split.  (At 128 tiles, two parts measured slower than none: the parts'
-// fp32 traffic then costs more than the idle half of the CUs; at 96 tiles, faster.)
-int gemm_split_parts(int64_t M, int64_t N, int64_t K) {
-  if (M <= 32 || K % 128 != 0 || N < 128) return 1;   // up to 32 rows: the decode kernels
+// K parts for a single-layer tiled GEMM (M > 32) whose 128 x 128 tiles would occupy at most 96
+// of the 256 CUs: about 256 workgroups, each at least one group of four K steps, at most
+// kMaxSplit parts; 1 = no split.  From 65 rows the parts run on 64 x 128 tiles (64 weight rows)
+// where those still give two parts or more, else on 128 x 128 tiles: half the parts for the
+// same workgroup count, so half the fp32 bytes written and read back (4096 x 4096 with the
+// quantizer and the sum: 18.5 -> 16.4 us at M = 128, 21.0 -> 18.4 at M = 192, 21.4 -> 19.5 at
+// M = 256; 8192 x 8192 at M = 128 unchanged; at M <= 64 half of each narrow tile's activation
+// rows would be empty, and 8192 x 8192 at M = 64 measured no faster).  Narrow tiles serve E4M3
+// operands only: their FP6 builds returned wrong sums in testing, and their assembly has the
+// compiler's register copies within two wait states of the assembly MFMAs that read them at
+// 15 sites (against 5 in the wide tile).  A call's workspace is sized for the wide plan, whose
+// part count is never the smaller.  (At 128 wide tiles, two parts measured slower than none: the
+// parts' fp32 traffic then costs more than the idle half of the CUs; at 96 tiles, faster.)
+struct SplitPlan { int parts; bool narrow; };
+static SplitPlan split_plan(int64_t M, int64_t N, int64_t K, bool narrow_ok) {
+  if (M <= 32 || K % 128 != 0 || N < 128) return {1, false};   // up to 32 rows: the decode kernels
   const int64_t t = ((N + 127) / 128) * ((M + 127) / 128);
+  if (t > 96) return {1, false};
+  const int64_t tn = ((N + 63) / 64) * ((M + 127) / 128);      // 64 x 128 tiles
+  const bool narrow = narrow_ok && M > 64 && 256 / tn >= 2;
   const int64_t G = (K / 128 + 3) / 4;
-  if (t > 96) return 1;
-  int64_t p = 256 / t;
+  int64_t p = 256 / (narrow ? tn : t);
   if (p > kMaxSplit) p = kMaxSplit;
   if (p > G) p = G;
-  return p < 2 ? 1 : (int)p;
+  return p < 2 ? SplitPlan{1, false} : SplitPlan{(int)p, narrow};
 }
+int gemm_split_parts(int64_t M, int64_t N, int64_t K) { return split_plan(M, N, K, false).parts; }
 
 int64_t gemm_split_bytes(int64_t M, int64_t N, int64_t K) {
   const int p = gemm_split_parts(M, N, K);
@@ -1492,11 +1505,20 @@ static hipError_t launch_tiled(const uint8_t* xq, const uint8_t* xs, int M, int 
                                const uint8_t* packed, int N, const uint16_t* bias, uint16_t* y,
                                hipStream_t s, int batch, const BatchStrides& bs, float* part) {
   const int group_m = 4;
-  const int parts = part && batch == 1 && !batch_invariant() && forced_tile() == 0
-                        ? gemm_split_parts(M, N, K) : 1;
+  const SplitPlan sp = part && batch == 1 && !batch_invariant() && forced_tile() == 0
+                          ? split_plan(M, N, K, WFMT == 0 && XFMT == 0) : SplitPlan{1, false};
+  const int parts = sp.parts;
   if (parts > 1) {
     // too few 128 x 128 tiles for the CUs: K parts on grid z, then the ordered sum
-    launch_tile<WFMT, XFMT, 4, 2, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s, 1, bs, parts, part);
+    if constexpr (WFMT == 0 && XFMT == 0) {
+      if (sp.narrow) {
+        launch_tile<WFMT, XFMT, 2, 2, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s, 1, bs, parts, part);
+      } else {
+        launch_tile<WFMT, XFMT, 4, 2, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s, 1, bs, parts, part);
+      }
+    } else {
+      launch_tile<WFMT, XFMT, 4, 2, 4>(xq, xs, M, K, packed, N, bias, y, group_m, s, 1, bs, parts, part);
+    }
     const int64_t MN = (int64_t)M * N;
     int64_t blocks = (MN / 4 + 255) / 256;
     if (blocks > 4096) blocks = 4096;

@@ -77,8 +77,9 @@ def test_linear_validation(L):
     # which needs no workspace: the size covers batch-invariant mode's quantized activations
     for m in (16, 24, 25, 32, 48, 64):
         assert L.mxfp8_workspace_bytes(m, 4096, 4096, 0) == 65536 + m * 4096 + m * 128
-    # above 64 rows, 32 tiles of 128 x 128: the quantized activations, then 8 K parts of fp32
-    # sums of the tiled GEMM
+    # above 64 rows, 32 tiles of 128 x 128: the quantized activations, then room for 8 K parts
+    # of fp32 sums of the tiled GEMM (E4M3 operands run 4 parts on 64 x 128 tiles; the size
+    # covers the 128 x 128 plan)
     q = 65536 + 65 * 4096 + 65 * 128
     need65 = (q + 255) // 256 * 256 + 8 * 65 * 4096 * 4
     assert L.mxfp8_workspace_bytes(65, 4096, 4096, 0) == need65

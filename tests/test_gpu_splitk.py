@@ -1,7 +1,8 @@
 """GPU parity of the tiled GEMM with K split across workgroups (single layers whose 128 x 128
-tiles would fill at most 96 of the 256 CUs, through an entry point with a workspace: with bf16
-activations from 33 rows on where the split-K decode kernel is not taken (M > 64, or a
-workgroup's share of x above 256 KiB there), with MXFP6 activations from 33 rows on).
+tiles would fill at most 96 of the 256 CUs; the parts on 64 x 128 or 128 x 128 tiles), through
+an entry point with a workspace: with bf16 activations from 33 rows on where the split-K decode
+kernel is not taken (M > 64, or a workgroup's share of x above 256 KiB there), with MXFP6
+activations from 33 rows on).
 
 Each workgroup computes one tile over one K part (whole groups of four K steps) and writes
 fp32 sums; a second kernel adds the parts in part order, adds the bias and rounds once.
@@ -23,16 +24,19 @@ pytestmark = pytest.mark.gpu
 
 FMTS = {0: "e4m3", 2: "e2m3", 3: "e3m2"}
 
-# (M, N, K): parts = min(8, 256 // tiles, groups of four K steps)
+# (M, N, K): parts = min(8, 256 // tiles, groups of four K steps).  E4M3 weights from 65 rows:
+# 64 x 128 ("narrow") tiles while they give two parts or more; else, and for FP6 weights,
+# 128 x 128 ("wide") tiles.  Comments: E4M3 / FP6.
 SHAPES = [
-    (65, 4096, 4096),    # 32 tiles, 8 parts of one group
-    (80, 2048, 4096),    # 16 tiles, 8 parts
-    (100, 4096, 4480),   # 32 tiles, 35 K steps in 9 groups: 8 parts, the last of 4 + 3 steps
-    (128, 4096, 4096),   # 32 tiles, 8 parts
-    (256, 1040, 8192),   # 18 tiles (ragged N), 8 parts of 2 groups
-    (300, 4096, 2048),   # 96 tiles, 2 parts of 2 groups (ragged M)
-    (48, 8192, 8192),    # 64 tiles, 4 parts: a workgroup's share of x would exceed 256 KiB in
-                         # the split-K decode kernel, so 48 rows take this path
+    (65, 4096, 4096),    # 64 narrow tiles, 4 parts of two groups / 32 wide, 8 parts of one
+    (80, 2048, 4096),    # 32 narrow tiles, 8 parts / 16 wide, 8 parts
+    (100, 4096, 4480),   # 35 K steps in 9 groups: 64 narrow tiles, 4 parts, the last of 8 + 3
+                         # steps / 32 wide, 8 parts, the last of 4 + 3
+    (128, 4096, 4096),   # 64 narrow tiles, 4 parts / 32 wide, 8 parts
+    (256, 1040, 8192),   # 34 narrow tiles (ragged N), 7 parts / 18 wide, 8 parts of 2 groups
+    (300, 4096, 2048),   # 96 wide tiles (192 narrow: one part), 2 parts of 2 groups (ragged M)
+    (48, 8192, 8192),    # 64 wide tiles, 4 parts: a workgroup's share of x would exceed 256 KiB
+                         # in the split-K decode kernel, so 48 rows take this path
 ]
 
 

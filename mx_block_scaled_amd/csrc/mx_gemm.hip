@@ -179,23 +179,39 @@ __device__ __forceinline__ v4f mfma_opsel(int q, const v8i& a, const v8i& b, v4f
 #define MX_MFMA_OPSEL_1 "op_sel:[1,1,0] op_sel_hi:[0,0,0]"
 #define MX_MFMA_OPSEL_2 "op_sel_hi:[1,1,0]"
 #define MX_MFMA_OPSEL_3 "op_sel:[1,1,0] op_sel_hi:[1,1,0]"
-#define MX_MFMA_ASM(OPSEL, FMT)                                                                 \
-  asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 " OPSEL FMT           \
+// PRE: instructions in the same statement ahead of the MFMA (the guard's wait states)
+#define MX_MFMA_ASM(PRE, OPSEL, FMT)                                                            \
+  asm volatile(PRE "v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 " OPSEL FMT       \
                : "+v"(acc) : "v"(a), "v"(b), "v"(sa), "v"(sb))
-#define MX_MFMA_Q(FMT)                                            \
-  do {                                                            \
-    if constexpr (Q == 0) MX_MFMA_ASM(MX_MFMA_OPSEL_0, FMT);      \
-    else if constexpr (Q == 1) MX_MFMA_ASM(MX_MFMA_OPSEL_1, FMT); \
-    else if constexpr (Q == 2) MX_MFMA_ASM(MX_MFMA_OPSEL_2, FMT); \
-    else MX_MFMA_ASM(MX_MFMA_OPSEL_3, FMT);                       \
+#define MX_MFMA_Q(PRE, FMT)                                            \
+  do {                                                                 \
+    if constexpr (Q == 0) MX_MFMA_ASM(PRE, MX_MFMA_OPSEL_0, FMT);      \
+    else if constexpr (Q == 1) MX_MFMA_ASM(PRE, MX_MFMA_OPSEL_1, FMT); \
+    else if constexpr (Q == 2) MX_MFMA_ASM(PRE, MX_MFMA_OPSEL_2, FMT); \
+    else MX_MFMA_ASM(PRE, MX_MFMA_OPSEL_3, FMT);                       \
+  } while (0)
+#define MX_MFMA_FMT(PRE)                                                      \
+  do {                                                                        \
+    if constexpr (WFMT == 0) MX_MFMA_Q(PRE, "");                              \
+    else if constexpr (WFMT == 2 && XFMT == 0) MX_MFMA_Q(PRE, " cbsz:2");     \
+    else if constexpr (WFMT == 3 && XFMT == 0) MX_MFMA_Q(PRE, " cbsz:3");     \
+    else if constexpr (WFMT == 2 && XFMT == 2) MX_MFMA_Q(PRE, " cbsz:2 blgp:2"); \
+    else if constexpr (WFMT == 2 && XFMT == 3) MX_MFMA_Q(PRE, " cbsz:2 blgp:3"); \
+    else if constexpr (WFMT == 3 && XFMT == 2) MX_MFMA_Q(PRE, " cbsz:3 blgp:2"); \
+    else MX_MFMA_Q(PRE, " cbsz:3 blgp:3");                                    \
   } while (0)
 // operand register image of one 16-row x 128-K fragment: 32 bytes for E4M3, 24 for FP6
 template <int F> struct AReg { typedef v8i type; };
 template <> struct AReg<2> { typedef v6i type; };
 template <> struct AReg<3> { typedef v6i type; };
 
-// WFMT = A (weight) format, XFMT = B (activation) format: the cbsz / blgp fields
-template <int WFMT, int XFMT, int Q, class TA, class TB>
+// WFMT = A (weight) format, XFMT = B (activation) format: the cbsz / blgp fields.
+// GUARD: three wait states inside the statement, ahead of the MFMA.  The compiler takes the
+// statement for opaque code, so it inserts no wait after its own vector writes of the operand
+// registers (copies into the registers the statement asks for, shifted scale words); a VALU
+// write needs two wait states before an MFMA reads the register.  Kernels whose assembly has
+// such writes within two instructions of the MFMA take the guard.
+template <int WFMT, int XFMT, int Q, bool GUARD = false, class TA, class TB>
 __device__ __forceinline__ void mfma_inplace(v4f& acc, const TA& a, const TB& b, uint32_t sa,
                                              uint32_t sb) {
   static_assert(Q >= 0 && Q < 4, "op-select byte");
@@ -204,13 +220,8 @@ __device__ __forceinline__ void mfma_inplace(v4f& acc, const TA& a, const TB& b,
                 "operand register images: 8 registers for E4M3, 6 for FP6");
   static_assert(XFMT == 0 || WFMT != 0, "FP6 activations go with FP6 weights");
 #if defined(__HIP_DEVICE_COMPILE__)   // the VGPR operand constraints exist for gfx950 only
-  if constexpr (WFMT == 0) MX_MFMA_Q("");
-  else if constexpr (WFMT == 2 && XFMT == 0) MX_MFMA_Q(" cbsz:2");
-  else if constexpr (WFMT == 3 && XFMT == 0) MX_MFMA_Q(" cbsz:3");
-  else if constexpr (WFMT == 2 && XFMT == 2) MX_MFMA_Q(" cbsz:2 blgp:2");
-  else if constexpr (WFMT == 2 && XFMT == 3) MX_MFMA_Q(" cbsz:2 blgp:3");
-  else if constexpr (WFMT == 3 && XFMT == 2) MX_MFMA_Q(" cbsz:3 blgp:2");
-  else MX_MFMA_Q(" cbsz:3 blgp:3");
+  if constexpr (GUARD) MX_MFMA_FMT("s_nop 2\n\t");
+  else MX_MFMA_FMT("");
 #endif
 }
 
@@ -536,7 +547,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
     if (TN > 0 && have) {
       asm volatile("s_nop 2" ::: "memory");   // the tail scale words are VALU-written
 #pragma unroll
-      for (int j = 0; j < TN; ++j) mfma_inplace<WFMT, XFMT, 0>(acc[FN - 1][FM - TN + j], a_tail, b_tail[j], sa_tail, sb_tail[j]);
+      for (int j = 0; j < TN; ++j) mfma_inplace<WFMT, XFMT, 0, true>(acc[FN - 1][FM - TN + j], a_tail, b_tail[j], sa_tail, sb_tail[j]);
     }
   };
   auto compute = [&](int stage, auto qc, const uint32_t* sa_in, const uint32_t* sb_in, int sh, bool have_tail, auto&& mid) __attribute__((always_inline)) {
@@ -574,7 +585,7 @@ __global__ __launch_bounds__(512, 2) void k_gemm_tile(const uint8_t* __restrict_
       }
 #pragma unroll
       for (int j = 0; j < (i == FN - 1 ? FM - TN : FM); ++j) {
-        mfma_inplace<WFMT, XFMT, (Q >= 0 ? Q : 0)>(acc[i][j], a, b[j], sa[i], sb[j]);
+        mfma_inplace<WFMT, XFMT, (Q >= 0 ? Q : 0), true>(acc[i][j], a, b[j], sa[i], sb[j]);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (i < FN - 1) {
